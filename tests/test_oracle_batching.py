@@ -1,0 +1,163 @@
+"""Oracle pins: clamps, batch intake, split_simple, split_equal, output_ids.
+
+Expected values come from tests/golden/page_numbers.json (numbers the pages
+print, with citations) or from closed forms stated in each test.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import batching as B
+from oracle import OracleEngine, SplitError
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_numbers.json")))
+
+
+def chunk_calls(n, n_batch):
+    return [min(n_batch, n - a) for a in range(0, n, n_batch)]
+
+
+def test_caller_chunking_and_split_simple_5000():
+    g = GOLD["caller_chunking"]
+    nb, nub = B.clamp_params(1 << 20, g["n_batch"], g["n_ubatch"])
+    calls = chunk_calls(g["n_tokens"], nb)
+    assert calls == g["calls"]
+    per_call = [len(B.split_batch([{0}] * n, nub, 1)) for n in calls]
+    assert per_call == g["ubatches_per_call"]
+    assert sum(per_call) == g["forward_passes"]
+
+
+def test_split_simple_page_examples():
+    g = GOLD["split_simple_1000"]
+    sizes = [len(s) for (s, _, _) in B.split_batch([{0}] * g["n_tokens"], g["n_ubatch"], 1)]
+    assert sizes == g["sizes"]
+    g = GOLD["split_simple_1500"]
+    parts = B.split_batch([{0}] * g["n_tokens"], g["n_ubatch"], 1)
+    assert [len(s) for (s, _, _) in parts] == g["sizes"]
+    assert [[s[0], s[-1]] for (s, _, _) in parts] == g["ranges"]
+
+
+def test_split_simple_ignores_sequence_ids():
+    # slots of three sequences interleaved are taken purely in submission order
+    sets = [{i % 3} for i in range(10)]
+    parts = B.split_batch(sets, 4, 1)
+    assert [s for (s, _, _) in parts] == [[0, 1, 2, 3], [4, 5, 6, 7], [8, 9]]
+
+
+def test_clamps():
+    g = GOLD["clamp_small_batch"]
+    nb, nub = B.clamp_params(4096, g["n_batch"], g["n_ubatch"])
+    assert nub == g["effective_n_ubatch"]
+    d = GOLD["defaults"]
+    assert B.clamp_params(1 << 20, 0, d["n_ubatch"]) == (d["n_batch"], d["n_ubatch"])
+    # causal: n_batch limited to the cache capacity; non-causal: not
+    assert B.clamp_params(1000, 2048, 512, causal=True) == (1000, 512)
+    assert B.clamp_params(1000, 2048, 512, causal=False) == (2048, 512)
+    # n_ubatch == 0 falls back to n_batch
+    assert B.clamp_params(4096, 1024, 0) == (1024, 1024)
+    assert B.clamp_params(100, 2048, 0) == (100, 100)
+
+
+def test_spec_verify_pass_count_and_no_padding():
+    g = GOLD["spec_verify"]
+    assert len(B.split_batch([{0}] * g["rows"], g["n_ubatch"], 1)) == g["passes"]
+    # a one-token decode is a one-row ubatch, not padded to n_ubatch
+    assert [len(s) for (s, _, _) in B.split_batch([{0}], 512, 1)] == [1]
+
+
+def test_split_equal_decode_then_prompts():
+    # 64 single-token sequences plus two long prompts: the first ubatch takes
+    # one slot from each of the 66 sets (floor(512/66) = 7 >= 1, but the
+    # decoders only have one slot each), then only the prompt sets remain.
+    sets = [{k} for k in range(2, 66)] + [{0}] * 300 + [{1}] * 200
+    parts = B.split_batch(sets, 512, 8)
+    slots, nst, ns = parts[0]
+    assert (nst, ns) == (1, 66)
+    # ordered by smallest sequence id
+    assert [min(sets[i]) for i in slots] == list(range(66))
+    # then the two prompts: min(remaining, 512 // 2) each
+    slots, nst, ns = parts[1]
+    assert (nst, ns) == (199, 2)
+    assert [min(sets[i]) for i in slots] == [0] * 199 + [1] * 199
+    total = sum(len(s) for (s, _, _) in parts)
+    assert total == len(sets)
+    flat = sorted(i for (s, _, _) in parts for i in s)
+    assert flat == list(range(len(sets)))
+
+
+def test_split_equal_equal_lengths_and_caps():
+    sets = [{0}] * 10 + [{1}] * 3 + [{2}] * 7
+    parts = B.split_batch(sets, 512, 4)
+    # every ubatch has the same count from each of its sets
+    for slots, nst, ns in parts:
+        assert len(slots) == nst * ns
+        counts = {}
+        for i in slots:
+            counts[min(sets[i])] = counts.get(min(sets[i]), 0) + 1
+        assert set(counts.values()) == {nst}
+    assert [(nst, ns) for (_, nst, ns) in parts] == [(3, 3), (4, 2), (3, 1)]
+    # n_ubatch caps n_seq_tokens * n_seqs
+    parts = B.split_batch([{0}] * 9 + [{1}] * 9, 4, 2)
+    assert [(nst, ns) for (_, nst, ns) in parts] == [(2, 2)] * 4 + [(1, 2)]
+    # more sets than n_ubatch: stop adopting at n_ubatch sets
+    parts = B.split_batch([{k} for k in range(6)], 4, 2)
+    assert [(len(s), nst, ns) for (s, nst, ns) in parts] == [(4, 1, 4), (2, 1, 2)]
+
+
+def test_split_equal_overlapping_sets_wait():
+    # slot 1's set {0,1} overlaps the adopted {0}: it waits; {1} alone is
+    # then blocked by nothing -- but {0,1} must not share a ubatch with {0}
+    sets = [{0}, {0, 1}, {2}, {0}]
+    parts = B.split_batch(sets, 512, 2)
+    for slots, _, _ in parts:
+        members = [frozenset(sets[i]) for i in slots]
+        uniq = set(members)
+        for a in uniq:
+            for b in uniq:
+                assert a == b or not (a & b)
+    first = parts[0][0]
+    assert 1 not in first
+    assert sorted(i for (s, _, _) in parts for i in s) == [0, 1, 2, 3]
+
+
+def test_split_equal_submission_order_within_set():
+    sets = [{1}, {0}, {1}, {0}, {1}]
+    parts = B.split_batch(sets, 512, 2)
+    slots, nst, ns = parts[0]
+    assert slots == [1, 3, 0, 2]            # set {0} first, each in submission order
+    assert parts[1][0] == [4]
+
+
+def test_output_ids():
+    ids = B.output_ids([0, 1, 0, 1, 1], 8)
+    assert ids.tolist() == [-1, 0, -1, 1, 2, -1, -1, -1]
+
+
+def test_fill_batch_autofill_and_errors():
+    p, s, o = B.fill_batch(3, None, None, None, {0: 5}, 1, 1)
+    assert p == [5, 6, 7] and s == [(0,)] * 3 and o == [0, 0, 1]
+    p, s, o = B.fill_batch(4, None, [[1], [0], [1], [0, 2]], [1, 1, 1, 1], {0: 0, 1: 10}, 4, 1)
+    assert p == [10, 0, 11, 1]
+    assert s[3] == (0, 2)
+    # first listed id stays first (the query masks against it)
+    p, s, o = B.fill_batch(1, [0], [[2, 0, 1]], None, {}, 4, 1)
+    assert s == [(2, 0, 1)]
+    with pytest.raises(SplitError):
+        B.fill_batch(1, [0], [[4]], None, {}, 4, 1)        # id out of range
+    with pytest.raises(SplitError):
+        B.fill_batch(1, [-1], [[0]], None, {}, 4, 1)       # negative position
+    with pytest.raises(SplitError):
+        B.fill_batch(1, [0], [[]], None, {}, 4, 1)         # no id
+    with pytest.raises(SplitError):
+        B.fill_batch(1, [0], [[0, 1]], None, {}, 4, 2)     # ids in two streams
+
+
+def test_engine_rejects_batch_larger_than_n_batch():
+    eng = OracleEngine(1, 2, 1, 16, kv_size=64, n_batch=16, n_ubatch=8)
+    with pytest.raises(SplitError):
+        eng.split(17)
+    st, ubs, ids = eng.split(16)
+    assert st == 0 and [u.n_tokens for u in ubs] == [8, 8]
