@@ -1,0 +1,214 @@
+/*
+ * kvattn -- per-ubatch attention over a cell-granular F16 KV cache, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources: "llama.cpp and the ubatch", joelfernandes.org;
+ * "Batch、Ubatch 与解码主循环", jonathanding.github.io; "What does llama.cpp's
+ * KV cache actually look like in memory?", joelfernandes.org):
+ *
+ *   1. a batch of token slots (position, sequence-id set, output flag) is
+ *      validated and split into ubatches -- split_simple for one stream,
+ *      split_equal for several ("Batch、Ubatch 与解码主循环", Part C);
+ *   2. every slot of every ubatch is given a cache cell, all-or-nothing for
+ *      the batch (same page, Part C "strategy choice"; Part F);
+ *   3. each ubatch writes its K/V rows, rounded to F16, into per-layer
+ *      tensors of shape [n_stream][kv_size][n_head_kv * head_dim] ("What
+ *      does llama.cpp's KV cache ...", "The tensor's three dimensions");
+ *   4. the KQ mask hides empty cells, cells of other sequences and future
+ *      positions, the query masking with its first sequence id ("llama.cpp
+ *      and the ubatch", "The mask is doing the work");
+ *   5. masked-softmax grouped-query attention runs over the visible cells.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success, KVATTN_NO_SLOT (1) when the cache has no room for
+ *     a batch (nothing is reserved), a negative KVATTN_E* code otherwise.
+ *     No call aborts; kvattn_last_error() describes the last failure.
+ *   - "device" pointers are HIP device addresses on params->device; "host"
+ *     pointers are ordinary process memory.  The caller owns every buffer
+ *     it passes; the library owns only its context and pinned staging.
+ *   - All GPU work is enqueued on the hip_stream argument (a hipStream_t,
+ *     NULL = the null stream) and nothing synchronises unless stated.  One
+ *     context must be driven from one thread and one stream at a time.
+ *   - Functions marked HOST-ONLY never touch the GPU and work on a machine
+ *     without one (k_layers may then be NULL).
+ */
+#ifndef KVATTN_H
+#define KVATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVATTN_MAX_SEQ 64           /* sequence ids live in [0, 64): one bit each */
+#define KVATTN_MAX_LAYERS_PER_LAUNCH 32
+
+enum {
+  KVATTN_OK = 0,
+  KVATTN_NO_SLOT = 1,     /* no free cells for the whole batch; nothing reserved */
+  KVATTN_EINVAL = -1,     /* an argument is out of range or inconsistent */
+  KVATTN_ESTATE = -2,     /* call out of order (stale ubatch, attend before store, ...) */
+  KVATTN_ENOMEM = -3,     /* workspace too small for this ubatch, or host allocation failed */
+  KVATTN_EHIP = -4,       /* a HIP runtime call failed */
+  KVATTN_ENODEV = -5      /* device work asked of a context created without device buffers */
+};
+
+typedef struct kvattn_ctx kvattn_ctx;
+
+/* Context parameters.  Mirrors llama_context_params (n_batch, n_ubatch) and
+ * the KV-cache constructor (layer count, head geometry, cells per stream,
+ * stream count): "llama.cpp and the ubatch", "Three things called batch";
+ * "What does llama.cpp's KV cache ...", "28 layers, 56 tensors" and
+ * "Unified versus non-unified". */
+typedef struct kvattn_params {
+  int32_t n_layer;        /* layers owning a K and a V tensor */
+  int32_t n_head;         /* query heads; a multiple of n_head_kv */
+  int32_t n_head_kv;      /* KV heads */
+  int32_t head_dim;       /* 16, 32, 64 or 128 */
+  int32_t kv_size;        /* cells PER STREAM (tensor dimension 1) */
+  int32_t n_stream;       /* 1 = unified cache; a slot's stream is seq_id[0] % n_stream */
+  int32_t n_seq_max;      /* sequence ids must lie in [0, n_seq_max); <= KVATTN_MAX_SEQ */
+  int32_t n_batch;        /* <= 0: 2048; clamped to kv_size*n_stream when causal */
+  int32_t n_ubatch;       /* 0: n_batch; then clamped to n_batch */
+  int32_t causal;         /* nonzero: hide cells with a later position */
+  float kq_scale;         /* 0: 1/sqrt(head_dim) */
+  const int32_t *cell_order; /* host, optional [n_stream][kv_size]: for each stream a permutation
+                                of 0..kv_size-1; free cells are handed out in this order
+                                (NULL = ascending).  Copied at create. */
+  void *const *k_layers;  /* host array of n_layer device pointers, each F16
+                             [n_stream][kv_size][n_head_kv*head_dim]; NULL = host-only context */
+  void *const *v_layers;  /* same for V */
+  void *workspace;        /* device, >= kvattn_workspace_bytes(); NULL with k_layers NULL */
+  size_t workspace_bytes;
+  int32_t device;         /* HIP device ordinal of every device pointer */
+} kvattn_params;
+
+/* A batch as submitted: llama_batch without token/embd ("Batch、Ubatch 与解码主循环",
+ * Part A).  pos, seq_id and output may each be NULL and are then filled:
+ * seq_id -> {0}; pos -> continuing each first sequence id from one past its
+ * largest cached position; output -> last slot only. */
+typedef struct kvattn_batch {
+  int32_t n_tokens;                 /* 0 <= n_tokens <= clamped n_batch */
+  const int32_t *pos;               /* host [n_tokens] or NULL */
+  const int32_t *n_seq_id;          /* host [n_tokens]; ignored when seq_id is NULL */
+  const int32_t *const *seq_id;     /* host [n_tokens] lists, first id = the query's sequence */
+  const int8_t *output;             /* host [n_tokens] or NULL */
+} kvattn_batch;
+
+/* One ubatch: llama_ubatch ("Batch、Ubatch 与解码主循环", Part B) plus its
+ * placement.  All arrays are host memory owned by the context and stay
+ * valid until the next kvattn_split or kvattn_destroy. */
+typedef struct kvattn_ubatch {
+  int32_t id;                       /* handle checked by store/attend */
+  int32_t n_tokens;                 /* = n_seq_tokens * n_seqs */
+  int32_t n_seq_tokens;
+  int32_t n_seqs;
+  int32_t n_seqs_unq;               /* distinct sequence ids in the ubatch */
+  int32_t n_outputs;                /* flagged slots */
+  const int32_t *pos;               /* [n_tokens] */
+  const int32_t *n_seq_id;          /* [n_tokens] */
+  const int32_t *const *seq_id;     /* [n_tokens] */
+  const int32_t *seq_id_unq;        /* [n_seqs_unq], ascending */
+  const int8_t *output;             /* [n_tokens] */
+  const int32_t *src_idx;           /* [n_tokens] row of each slot in the submitted batch */
+  const int32_t *stream;            /* [n_tokens] */
+  const int32_t *cells;             /* [n_tokens] reserved cell within the stream */
+} kvattn_ubatch;
+
+/* Device workspace the caller must provide: cell metadata mirror, the
+ * per-ubatch visibility lists and work plan, and split-K partials, sized for
+ * the clamped n_ubatch ("llama.cpp and the ubatch", "Where the memory
+ * actually sits": the workspace is reserved once for the largest pass). */
+size_t kvattn_workspace_bytes(const kvattn_params *p);
+
+/* Total K+V cache bytes over all layers and streams: 2 * n_layer * n_stream
+ * * kv_size * n_head_kv * head_dim * 2 ("What does llama.cpp's KV cache
+ * ...", "One row, one token's keys": 448 MiB for 28 x 8 x 128 at 4096). */
+size_t kvattn_cache_bytes(const kvattn_params *p);
+
+/* HOST-ONLY.  Validates and copies *p.  Device buffers are only recorded;
+ * the first call that needs the GPU initialises it. */
+int kvattn_create(const kvattn_params *p, kvattn_ctx **out);
+void kvattn_destroy(kvattn_ctx *ctx);
+
+/* HOST-ONLY.  Validate + auto-fill the batch, split it into ubatches and
+ * reserve a cell for every slot of every ubatch, all-or-nothing.  Writes up
+ * to cap ubatches to ubs[] and their count to *n_ubs (cap too small ->
+ * KVATTN_EINVAL, nothing reserved).  output_ids, when not NULL, receives
+ * n_batch entries: the rank of each flagged batch row among flagged rows,
+ * -1 elsewhere.  Cells reserved by the previous split and never stored are
+ * released; ubatches of the previous split become stale. */
+int kvattn_split(kvattn_ctx *ctx, const kvattn_batch *b, kvattn_ubatch *ubs, int32_t cap,
+                 int32_t *n_ubs, int32_t *output_ids);
+
+/* Write K/V rows of layers il0 .. il0+n_il-1.  k_cur/v_cur are host arrays
+ * of n_il device pointers, each fp32 [n_tokens][n_head_kv*head_dim] in
+ * ubatch slot order; rows are rounded to F16 (nearest-even) into the
+ * ubatch's cells.  The first call with il0 == 0 commits the ubatch: its
+ * cells become visible and the visibility lists for its attention are built
+ * on the GPU.  Ubatches of one split commit in order.  Storing again is
+ * idempotent.  On a host-only context, n_il == 0 commits the placement
+ * without touching the GPU (any other call returns KVATTN_ENODEV). */
+int kvattn_store(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t n_il,
+                 const void *const *k_cur, const void *const *v_cur, void *hip_stream);
+
+/* Attention of layers il0 .. il0+n_il-1 for the most recently committed
+ * ubatch.  q/out are host arrays of n_il device pointers; q is fp32
+ * [n_tokens][n_head*head_dim], out fp32 [n_tokens][n_head*head_dim] in
+ * ubatch slot order -- or, with only_outputs, [n_outputs][...] holding the
+ * flagged slots in slot order.  A slot with no visible cell yields zeros.
+ * Repeatable. */
+int kvattn_attend(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t n_il,
+                  const void *const *q, void *const *out, int32_t only_outputs, void *hip_stream);
+
+/* ---- diagnostics (tests and benchmarks) ---------------------------------- */
+
+/* HOST-ONLY.  n_kv reported for the current state ("llama.cpp and the
+ * ubatch", "Prefill and decode are not the same shape"). */
+int32_t kvattn_n_kv(const kvattn_ctx *ctx);
+
+/* Dense F16 KQ mask of the most recently committed ubatch, built on the GPU
+ * from the device cell mirror: 0x0000 visible, 0xFC00 (-inf) hidden,
+ * row-major [n_tokens][n_kv].  d_mask is a device buffer of cap_elems F16;
+ * *n_kv receives the row length.  Asynchronous on hip_stream. */
+int kvattn_get_mask(kvattn_ctx *ctx, const kvattn_ubatch *ub, void *d_mask, size_t cap_elems,
+                    int32_t *n_kv, void *hip_stream);
+
+/* Visibility lists of the most recently committed ubatch, copied to host
+ * (synchronises hip_stream).  Cells are grouped in classes of equal
+ * sequence sets; per class: stream, sequence-set bitmask, number of cells,
+ * then the cells in ascending index.  Fills up to cap_classes classes and
+ * cap_cells cells; *n_classes / *n_cells receive the totals. */
+int kvattn_get_classes(kvattn_ctx *ctx, int32_t *n_classes, int32_t *cls_stream,
+                       uint64_t *cls_mask, int32_t *cls_count, int32_t cap_classes,
+                       int32_t *n_cells, int32_t *cells, int32_t cap_cells, void *hip_stream);
+
+/* HOST-ONLY.  Copy of the committed cell table of one stream: pos (-1 =
+ * empty) and the sequence-set bitmask of each of the kv_size cells. */
+int kvattn_get_cells(const kvattn_ctx *ctx, int32_t stream, int32_t *pos, uint64_t *seqmask);
+
+/* HOST-ONLY.  Remove sequence seq_id (every sequence when < 0) from cells
+ * whose position lies in [p0, p1) (p0 < 0: from 0; p1 < 0: no end).  A cell
+ * left without a sequence becomes free.  The device mirror follows at the
+ * next commit. */
+int kvattn_seq_rm(kvattn_ctx *ctx, int32_t seq_id, int32_t p0, int32_t p1);
+
+/* HOST-ONLY.  Largest committed position of seq_id, -1 when none. */
+int32_t kvattn_seq_pos_max(const kvattn_ctx *ctx, int32_t seq_id);
+
+/* HOST-ONLY.  Work plan of the most recently committed ubatch: number of
+ * visibility classes, vector-ALU work items, matrix-core work items (per
+ * KV head), split-K partial rows and reduced slots.  Any pointer may be NULL. */
+int kvattn_plan_stats(const kvattn_ctx *ctx, int32_t only_outputs, int32_t *n_classes,
+                      int32_t *n_items_valu, int32_t *n_items_mfma, int32_t *n_partial_rows,
+                      int32_t *n_reduced);
+
+/* HOST-ONLY.  Text of the last error on this context ("" if none). */
+const char *kvattn_last_error(const kvattn_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVATTN_H */

@@ -92,13 +92,15 @@ class OracleEngine:
         return 0, ubs, output_ids(out, self.n_batch)
 
     # -- per ubatch ------------------------------------------------------
-    def commit(self, ub: OracleUbatch):
+    def commit(self, ub: OracleUbatch, build_mask=True):
         """The ubatch's cells become visible, then its mask is built over
-        the table as it now stands (later ubatches are not yet committed)."""
+        the table as it now stands (later ubatches are not yet committed).
+        ``build_mask=False`` only records placement (for placement checks)."""
         self.cells.commit(ub.streams, ub.cells, ub.pos, ub.seq_ids)
         ub.committed = True
         ub.n_kv = self.cells.n_kv()
-        ub.mask = self.cells.mask(ub.streams, ub.pos, [s[0] for s in ub.seq_ids], self.causal)
+        if build_mask:
+            ub.mask = self.cells.mask(ub.streams, ub.pos, [s[0] for s in ub.seq_ids], self.causal)
         return ub.mask
 
     def store(self, ub: OracleUbatch, layer: int, k_rows, v_rows):

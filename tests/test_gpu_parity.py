@@ -1,0 +1,242 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Cache bytes, the dense mask and the per-class cell lists must match bit for
+bit; attention outputs must satisfy |g - r| <= 2e-3 + 5e-3 |r| elementwise
+(and the tighter per-kernel bounds below, which catch a dropped cell that the
+tolerance alone would let through).  Sizes here span several 64-cell tiles,
+several q-tiles and ragged tails while the oracle stays within seconds.
+"""
+
+import numpy as np
+import pytest
+
+from synthetic import workloads as W
+from tests.helpers import assert_parity, gpu_run, oracle_run, make_ctx
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+K = pytest.importorskip("ubatch_attention_paged_amd")
+
+
+def small(name):
+    if name == "tiny":
+        return W.tiny()
+    if name == "prefill":
+        return W.qwen_prefill(n_prompt=700, n_layer=2, kv_size=1024, n_batch=512, n_ubatch=256)
+    if name == "cb_decode":
+        return W.cb_decode(n_seq=16, lengths=(5, 40, 130, 300), n_layer=2, kv_size=4096)
+    if name == "mixed":
+        return W.mixed(n_prompt_seq=4, n_decoders=12, prompt_range=(30, 200), ctx_range=(20, 300),
+                       n_layer=2, n_stream=4, kv_size=2048, n_batch=256, n_ubatch=64)
+    if name == "prefix":
+        return W.prefix_decode(n_seq=8, prefix=300, private=50, n_layer=2, kv_size=1024)
+    if name == "prefix32":
+        return W.prefix_decode(n_seq=32, prefix=200, private=20, n_layer=1, kv_size=2048)
+    if name == "d64":
+        wl = W.mixed(n_prompt_seq=2, n_decoders=5, prompt_range=(40, 150), ctx_range=(10, 90),
+                     n_layer=1, n_stream=1, kv_size=1024, n_batch=256, n_ubatch=100)
+        wl.n_head, wl.n_head_kv, wl.head_dim = 32, 16, 64      # E = 1024, G = 2, d = 64
+        return wl
+    raise KeyError(name)
+
+
+NAMES = ["tiny", "prefill", "cb_decode", "mixed", "prefix", "prefix32", "d64"]
+
+
+def expected_classes(eng, ub):
+    """Cells per (stream, sequence set) that some query of the ubatch sees,
+    ascending cell index, classes ordered by (stream, set bitmask)."""
+    out = []
+    for s in range(eng.n_stream):
+        qseqs = {ub.seq_ids[i][0] for i in range(ub.n_tokens) if ub.streams[i] == s}
+        if not qseqs:
+            continue
+        pos = eng.cells.pos[s]
+        bits = (eng.cells.member[s].astype(np.uint64) << np.arange(eng.n_seq_max, dtype=np.uint64)).sum(axis=1)
+        occupied = np.nonzero(pos >= 0)[0]
+        masks = sorted({int(bits[j]) for j in occupied if any(int(bits[j]) >> q & 1 for q in qseqs)})
+        for m in masks:
+            out.append((s, m, occupied[bits[occupied] == np.uint64(m)]))
+    return out
+
+
+@pytest.mark.parametrize("name", NAMES)
+def test_end_to_end_parity(name):
+    wl = small(name)
+    layers = list(range(wl.n_layer))
+    print(f"[gpu] end_to_end {name}: {wl.note}", flush=True)
+    eng, ref, masks, meta = oracle_run(wl, layers, keep_masks=True)
+    seen = {"mask": 0, "classes": 0}
+
+    def check(ctx, b, ub):
+        u = ub_index[b]
+        r = meta[(b, u)]
+        assert ub.cells.tolist() == r.cells
+        m = ctx.mask(ub).cpu().numpy().view(np.uint16)
+        assert m.shape == masks[(b, u)].shape
+        assert np.array_equal(m, masks[(b, u)].view(np.uint16)), f"mask differs (batch {b}, ubatch {u})"
+        seen["mask"] += 1
+        ub_index[b] += 1
+
+    ub_index = {b: 0 for b in range(len(wl.batches))}
+    ctx, got = gpu_run(wl, layers, on_ubatch=check)
+    assert seen["mask"] == len(meta)
+    worst = 0.0
+    for key in ref:
+        ma, mr = assert_parity(got[key], ref[key], tag=f"{name} batch {key[0]} layer {key[1]}")
+        worst = max(worst, ma)
+    # every kernel path keeps well inside the tolerance
+    assert worst < 1e-3, worst
+    # cache bytes: every committed cell row equals the oracle's F16 rounding
+    for l in layers:
+        gk = ctx.K[l].cpu().numpy().view(np.uint16)
+        gv = ctx.V[l].cpu().numpy().view(np.uint16)
+        occ = eng.cells.pos >= 0
+        assert np.array_equal(gk[occ], eng.K[l][occ].view(np.uint16))
+        assert np.array_equal(gv[occ], eng.V[l][occ].view(np.uint16))
+    ctx.close()
+
+
+@pytest.mark.parametrize("name", ["prefill", "cb_decode", "mixed", "prefix32"])
+def test_class_lists_bit_exact(name):
+    wl = small(name)
+    print(f"[gpu] class lists {name}", flush=True)
+    eng, _, _, meta = oracle_run(wl, [0], keep_masks=False)
+    # replay the placement on the GPU, checking the lists after every commit
+    eng2, _, _, _ = None, None, None, None
+    from oracle import OracleEngine
+    eng2 = OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
+                        wl.n_seq_max, wl.n_batch, wl.n_ubatch, wl.causal, cell_order=wl.cell_order, layers=[])
+    ctx = make_ctx(wl)
+    dev = torch.device("cuda:0")
+    E = wl.E
+    checked = 0
+    for b, bt in enumerate(wl.batches):
+        st, ubs, _ = ctx.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        _, rubs, _ = eng2.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        zeros = torch.zeros((max(u.n_tokens for u in ubs), E), device=dev)
+        for ub, r in zip(ubs, rubs):
+            ctx.store(ub, 0, [zeros[:ub.n_tokens]], [zeros[:ub.n_tokens]])
+            eng2.commit(r, build_mask=False)
+            got = ctx.classes()
+            exp = expected_classes(eng2, r)
+            assert [(s, m) for s, m, _ in got] == [(s, m) for s, m, _ in exp]
+            for (_, _, cg), (_, _, ce) in zip(got, exp):
+                assert np.array_equal(cg, ce)
+            checked += 1
+    assert checked == len(meta)
+    ctx.close()
+
+
+def test_only_outputs_and_layer_chunks():
+    wl = small("mixed")
+    layers = [0, 1]
+    print("[gpu] only_outputs / layer chunks", flush=True)
+    _, ref, _, _ = oracle_run(wl, layers)
+    _, full = gpu_run(wl, layers, layer_chunk=2)
+    _, per_layer = gpu_run(wl, layers, layer_chunk=1)
+    _, outs = gpu_run(wl, layers, only_outputs=True)
+    for key in ref:
+        assert np.array_equal(full[key], per_layer[key])          # same kernels, same result
+        b = key[0]
+        flagged = np.nonzero(wl.batches[b].output)[0]
+        assert_parity(outs[key], ref[key], rows=flagged, tag=f"only_outputs {key}")
+        np.testing.assert_array_equal(outs[key][flagged], full[key][flagged])
+
+
+@pytest.mark.parametrize("n_ubatch", [512, 64, 7])
+def test_split_invariance(n_ubatch):
+    wl = W.qwen_prefill(n_prompt=300, n_layer=1, kv_size=512, n_batch=256, n_ubatch=512)
+    print(f"[gpu] split invariance n_ubatch={n_ubatch}", flush=True)
+    _, ref, _, _ = oracle_run(wl, [0])
+    _, got = gpu_run(wl, [0], n_ubatch=n_ubatch)
+    for key in ref:
+        assert_parity(got[key], ref[key], tag=f"n_ubatch {n_ubatch}")
+
+
+def test_repeat_store_attend_is_idempotent():
+    wl = small("cb_decode")
+    print("[gpu] idempotent replay", flush=True)
+    ctx = make_ctx(wl)
+    dev = torch.device("cuda:0")
+    from tests.helpers import batch_tensors
+    for b, bt in enumerate(wl.batches):
+        t = batch_tensors(wl, b, [0, 1], bt.measured)
+        Kt = [torch.from_numpy(t[(l, W.KIND_K)]).to(dev) for l in (0, 1)]
+        Vt = [torch.from_numpy(t[(l, W.KIND_V)]).to(dev) for l in (0, 1)]
+        st, ubs, _ = ctx.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        assert len(ubs) == 1
+        ctx.store(ubs[0], 0, Kt, Vt)
+        if bt.measured:
+            Q = [torch.from_numpy(t[(l, W.KIND_Q)]).to(dev) for l in (0, 1)]
+            o1 = [torch.empty_like(q) for q in Q]
+            o2 = [torch.empty_like(q) for q in Q]
+            ctx.attend(ubs[0], 0, Q, o1)
+            for _ in range(3):
+                ctx.store(ubs[0], 0, Kt, Vt)
+                ctx.attend(ubs[0], 0, Q, o2)
+            torch.cuda.synchronize()
+            for a, c in zip(o1, o2):
+                assert torch.equal(a, c)
+    ctx.close()
+
+
+def test_needles_on_gpu():
+    """A dominant key in a visible cell takes over head 0's output; the same
+    key planted in a hidden cell (other sequence, future position, stale row
+    past n_kv) changes nothing."""
+    from ubatch_attention_paged_amd.harness import decode
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(11)
+    H, Hk, D = 16, 8, 128
+    E = Hk * D
+
+    def run(where):
+        ctx = K.Context(1, H, Hk, D, kv_size=1024, n_seq_max=2, device="cuda:0")
+        q = rng.standard_normal((1, H * D)).astype(np.float32)
+        qhat = q[0, :D] / np.linalg.norm(q[0, :D])
+        k0 = (np.random.default_rng(1).standard_normal((300, E)) * 0.1).astype(np.float32)
+        v0 = np.random.default_rng(2).standard_normal((300, E)).astype(np.float32)
+        k1 = (np.random.default_rng(3).standard_normal((40, E)) * 0.1).astype(np.float32)
+        v1 = np.random.default_rng(4).standard_normal((40, E)).astype(np.float32)
+        needle = np.full(D, 7.0, np.float32)
+        if where == "visible":
+            k0[77, :D], v0[77, :D] = 50 * qhat, needle
+        elif where == "future":
+            k0[250, :D], v0[250, :D] = 50 * qhat, needle
+        elif where == "other_seq":
+            k1[13, :D], v1[13, :D] = 50 * qhat, needle
+        T = lambda a: [torch.from_numpy(np.ascontiguousarray(a)).to(dev)]
+        decode(ctx, 300, np.arange(300), [[0]] * 300, None, T(k0), T(v0))
+        decode(ctx, 40, np.arange(40), [[1]] * 40, None, T(k1), T(v1))
+        if where == "beyond_nkv":
+            ctx.K[0][0, 900, :D] = torch.from_numpy(50 * qhat).half().to(dev)
+            ctx.V[0][0, 900, :D] = torch.from_numpy(needle).half().to(dev)
+        kq = (np.random.default_rng(5).standard_normal((1, E)) * 0.1).astype(np.float32)
+        vq = np.random.default_rng(6).standard_normal((1, E)).astype(np.float32)
+        st, ubs, outs = decode(ctx, 1, [200], [[0]], None, T(kq), T(vq), Q=T(q))
+        torch.cuda.synchronize()
+        o = outs[0].cpu().numpy()
+        ctx.close()
+        return o
+
+    base = run("none")
+    hit = run("visible")
+    np.testing.assert_allclose(hit[0, :D], 7.0, rtol=2e-3)
+    for where in ("future", "other_seq", "beyond_nkv"):
+        np.testing.assert_array_equal(run(where), base)
+
+
+def test_cache_full_and_empty_batch_on_gpu():
+    ctx = K.Context(1, 16, 8, 128, kv_size=16, device="cuda:0")
+    st, ubs, _ = ctx.split(0)
+    assert st == 0 and ubs == []
+    st, ubs, _ = ctx.split(16)
+    z = torch.zeros((16, 1024), device="cuda:0")
+    ctx.store(ubs[0], 0, [z], [z])
+    st, ubs, _ = ctx.split(1)
+    assert st == K.KVATTN_NO_SLOT
+    ctx.close()

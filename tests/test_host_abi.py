@@ -1,0 +1,253 @@
+"""The C ABI on the CPU (no GPU needed).
+
+* libkvattn.so loads and exports every function include/kvattn.h declares;
+* the host half -- batch intake, split_simple / split_equal, placement,
+  commit, n_kv, output_ids, seq_rm, error codes -- matches the oracle bit for
+  bit on every workload shape (reduced sizes) and on edge cases.
+"""
+
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from oracle import OracleEngine, SplitError
+from synthetic import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+K = pytest.importorskip("ubatch_attention_paged_amd")
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvattn_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 15
+    lib = K.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (kvattn_\w+)", out))
+    assert set(names) <= exported
+    # nothing else leaks into the C namespace
+    assert exported == set(names)
+
+
+def host_ctx(wl, order="auto", n_ubatch=None):
+    order = wl.cell_order if order == "auto" else order
+    return K.Context(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
+                     wl.n_seq_max, wl.n_batch, wl.n_ubatch if n_ubatch is None else n_ubatch,
+                     wl.causal, cell_order=order)
+
+
+def oracle_for(wl, order="auto", n_ubatch=None):
+    order = wl.cell_order if order == "auto" else order
+    return OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
+                        wl.n_seq_max, wl.n_batch, wl.n_ubatch if n_ubatch is None else n_ubatch,
+                        wl.causal, cell_order=order, layers=[])
+
+
+def compare_split(ctx, eng, n, pos, seqs, out):
+    st, ubs, ids = ctx.split(n, pos, seqs, out, with_ids=True)
+    rst, rubs, rids = eng.split(n, pos, seqs, out)
+    assert st == rst
+    if st:
+        return ubs, rubs
+    assert len(ubs) == len(rubs)
+    for u, r in zip(ubs, rubs):
+        assert u.src.tolist() == r.src
+        assert u.pos.tolist() == r.pos
+        assert u.seq_ids == [tuple(s) for s in r.seq_ids]
+        assert u.output.tolist() == r.output
+        assert (u.n_seq_tokens, u.n_seqs) == (r.n_seq_tokens, r.n_seqs)
+        assert u.stream.tolist() == r.streams
+        assert u.cells.tolist() == r.cells
+        assert u.n_tokens == u.n_seq_tokens * u.n_seqs
+        assert u.seq_id_unq.tolist() == sorted({s for ss in r.seq_ids for s in ss})
+    assert np.array_equal(ids, rids)
+    return ubs, rubs
+
+
+def commit_all(ctx, eng, ubs, rubs):
+    for u, r in zip(ubs, rubs):
+        ctx.store(u, 0, [], [])
+        eng.commit(r, build_mask=False)
+        assert ctx.n_kv() == eng.cells.n_kv() == r.n_kv
+
+
+def compare_tables(ctx, eng):
+    for s in range(eng.n_stream):
+        pos, mask = ctx.cells(s)
+        assert np.array_equal(pos, eng.cells.pos[s])
+        bits = (eng.cells.member[s].astype(np.uint64) << np.arange(eng.n_seq_max, dtype=np.uint64)).sum(axis=1)
+        assert np.array_equal(mask, bits.astype(np.uint64))
+
+
+def shrink(wl, layers=1):
+    wl.n_layer = layers
+    return wl
+
+
+WORKLOADS = [
+    lambda: W.tiny(),
+    lambda: shrink(W.qwen_prefill(n_prompt=1300, n_layer=1, kv_size=2048, n_batch=1024, n_ubatch=256)),
+    lambda: shrink(W.cb_decode(n_seq=16, lengths=(5, 9, 70, 130), n_layer=1, kv_size=2048)),
+    lambda: shrink(W.mixed(n_prompt_seq=4, n_decoders=12, prompt_range=(20, 90), ctx_range=(10, 60),
+                           n_layer=1, n_stream=4, kv_size=512, n_batch=128, n_ubatch=32)),
+    lambda: shrink(W.prefix_decode(n_seq=8, prefix=300, private=40, n_layer=1, kv_size=1024)),
+]
+
+
+@pytest.mark.parametrize("make", WORKLOADS, ids=["tiny", "prefill", "cb_decode", "mixed", "prefix"])
+def test_host_split_placement_matches_oracle(make):
+    wl = make()
+    ctx, eng = host_ctx(wl), oracle_for(wl)
+    for bt in wl.batches:
+        ubs, rubs = compare_split(ctx, eng, bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        commit_all(ctx, eng, ubs, rubs)
+    compare_tables(ctx, eng)
+
+
+def test_full_size_config_splits_match_oracle():
+    # the caller calls and ubatches of the full Qwen3 prefill and the
+    # full-size decode workloads (placement only, no tensors)
+    for wl in (W.qwen_prefill(n_layer=1), W.cb_decode(n_layer=1), W.prefix_decode(n_layer=1)):
+        ctx, eng = host_ctx(wl), oracle_for(wl)
+        for bt in wl.batches:
+            ubs, rubs = compare_split(ctx, eng, bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+            commit_all(ctx, eng, ubs, rubs)
+        compare_tables(ctx, eng)
+    pre = W.qwen_prefill(n_layer=1)
+    assert [b.n_tokens for b in pre.batches] == [2048, 952]
+
+
+def test_mixed_full_size_split_equal_matches_oracle():
+    wl = W.mixed(n_layer=1)
+    ctx, eng = host_ctx(wl), oracle_for(wl)
+    first = True
+    for bt in wl.batches:
+        ubs, rubs = compare_split(ctx, eng, bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        if bt.measured and first:
+            # one decode token per decoder plus the prompts that fit: one
+            # slot from every sequence set in the first ubatch
+            n_sets = len({s for s in bt.seq_ids})
+            assert n_sets > 56
+            assert (ubs[0].n_seqs, ubs[0].n_seq_tokens) == (n_sets, 1)
+            first = False
+        commit_all(ctx, eng, ubs, rubs)
+    compare_tables(ctx, eng)
+
+
+def test_autofill_and_defaults_match_oracle():
+    ctx = K.Context(1, 2, 1, 16, kv_size=64, n_seq_max=4)
+    eng = OracleEngine(1, 2, 1, 16, kv_size=64, n_seq_max=4, layers=[])
+    ubs, rubs = compare_split(ctx, eng, 5, None, None, None)
+    commit_all(ctx, eng, ubs, rubs)
+    ubs, rubs = compare_split(ctx, eng, 4, None, [[1], [0], [1, 3], [0]], [1, 0, 0, 1])
+    commit_all(ctx, eng, ubs, rubs)
+    assert [u.pos.tolist() for u in ubs] == [[0, 5, 1, 6]]
+    compare_tables(ctx, eng)
+    assert K.kvattn_seq_pos_max(ctx.ctx, 0) == eng.cells.seq_pos_max(0) == 6
+    assert K.kvattn_seq_pos_max(ctx.ctx, 2) == -1
+
+
+def test_seq_rm_and_reuse_match_oracle():
+    wl = W.cb_decode(n_seq=6, lengths=(4, 9, 15), n_layer=1, kv_size=64)
+    ctx, eng = host_ctx(wl), oracle_for(wl)
+    for bt in wl.batches:
+        ubs, rubs = compare_split(ctx, eng, bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        commit_all(ctx, eng, ubs, rubs)
+    for args in ((2, -1, -1), (4, 3, 7), (-1, 10, -1)):
+        ctx.seq_rm(*args)
+        eng.seq_rm(*args)
+        compare_tables(ctx, eng)
+    ubs, rubs = compare_split(ctx, eng, 3, [20, 21, 22], [[1], [2], [3]], None)
+    commit_all(ctx, eng, ubs, rubs)
+    compare_tables(ctx, eng)
+
+
+def test_split_invariance_of_placement():
+    for nub in (512, 64, 7, 1):
+        wl = W.qwen_prefill(n_prompt=150, n_layer=1, kv_size=512, n_batch=100, n_ubatch=nub)
+        ctx = host_ctx(wl)
+        for bt in wl.batches:
+            st, ubs, _ = ctx.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+            assert [u.n_tokens for u in ubs] == [min(nub, bt.n_tokens - a) for a in range(0, bt.n_tokens, nub)]
+            for u in ubs:
+                ctx.store(u, 0, [], [])
+        pos, _ = ctx.cells(0)
+        assert pos[:150].tolist() == list(range(150)) and (pos[150:] == -1).all()
+
+
+def test_error_codes():
+    ctx = K.Context(1, 2, 1, 16, kv_size=8, n_seq_max=3, n_batch=6, n_ubatch=4)
+    with pytest.raises(K.KvattnError) as e:
+        ctx.split(7)                                      # more than n_batch
+    assert e.value.code == K.KVATTN_EINVAL
+    for pos, seqs in (([0], [[3]]), ([-1], [[0]]), ([0], [[]])):
+        with pytest.raises(K.KvattnError) as e:
+            ctx.split(1, pos, seqs)
+        assert e.value.code == K.KVATTN_EINVAL
+    st, ubs, _ = ctx.split(6)
+    assert st == 0 and [u.n_tokens for u in ubs] == [4, 2]
+    with pytest.raises(K.KvattnError) as e:
+        ctx.store(ubs[1], 0, [], [])                      # out of order
+    assert e.value.code == K.KVATTN_ESTATE
+    ctx.store(ubs[0], 0, [], [])
+    ctx.store(ubs[1], 0, [], [])
+    before = ctx.cells(0)
+    st, ubs2, _ = ctx.split(3)                            # 2 cells left: nothing reserved
+    assert st == K.KVATTN_NO_SLOT and ubs2 == []
+    after = ctx.cells(0)
+    assert np.array_equal(before[0], after[0]) and np.array_equal(before[1], after[1])
+    st, ubs3, _ = ctx.split(2)
+    assert st == 0 and ubs3[0].cells.tolist() == [6, 7]
+    with pytest.raises(K.KvattnError) as e:
+        ctx.store(ubs[0], 0, [], [])                      # stale handle from an earlier split
+    assert e.value.code == K.KVATTN_ESTATE
+    # a device call on a host-only context
+    with pytest.raises(K.KvattnError) as e:
+        ctx.attend(ubs3[0], 0, [], [])
+    assert e.value.code == K.KVATTN_ENODEV
+    # streams: a slot whose ids live in two streams
+    c2 = K.Context(1, 2, 1, 16, kv_size=8, n_stream=2, n_seq_max=4)
+    with pytest.raises(K.KvattnError):
+        c2.split(1, [0], [[0, 1]])
+    # bad parameters
+    with pytest.raises(K.KvattnError):
+        K.Context(1, 3, 2, 16, kv_size=8)                 # n_head not a multiple
+    with pytest.raises(K.KvattnError):
+        K.Context(1, 2, 1, 24, kv_size=8)                 # unsupported head_dim
+    with pytest.raises(K.KvattnError):
+        K.Context(1, 2, 1, 16, kv_size=8, n_seq_max=65)   # more than 64 sequences
+    with pytest.raises(K.KvattnError):
+        K.Context(1, 2, 1, 16, kv_size=4, cell_order=[0, 1, 1, 2])
+
+
+def test_empty_batch_and_uncommitted_release():
+    ctx = K.Context(1, 2, 1, 16, kv_size=8, n_ubatch=4)
+    st, ubs, _ = ctx.split(0)
+    assert st == 0 and ubs == []
+    st, ubs, _ = ctx.split(8)
+    assert st == 0 and len(ubs) == 2
+    ctx.store(ubs[0], 0, [], [])
+    # a new split releases the never-stored second ubatch's cells
+    st, ubs, _ = ctx.split(4)
+    assert st == 0 and ubs[0].cells.tolist() == [4, 5, 6, 7]
+
+
+def test_workspace_and_cache_bytes():
+    p = K.kvattn_params()
+    p.n_layer, p.n_head, p.n_head_kv, p.head_dim, p.kv_size = 28, 16, 8, 128, 4096
+    p.n_stream, p.n_seq_max, p.n_ubatch = 1, 1, 512
+    assert K.kvattn_cache_bytes(p) == 448 * 2 ** 20
+    ws = K.kvattn_workspace_bytes(p)
+    assert 0 < ws < 512 * 2 ** 20
+    p.head_dim = 24
+    assert K.kvattn_workspace_bytes(p) == 0

@@ -1,0 +1,17 @@
+"""MI355X-native per-ubatch attention over a cell-granular F16 KV cache.
+
+The work runs in ``libkvattn.so`` (hand-written HIP for gfx950 behind the C
+ABI of ``include/kvattn.h``); this package is its ctypes binding.  Importing
+it loads the library and fails loudly when it has not been built -- there is
+no CPU fallback.
+"""
+
+from .kvattn import (  # noqa: F401
+    KVATTN_OK, KVATTN_NO_SLOT, KVATTN_EINVAL, KVATTN_ESTATE, KVATTN_ENOMEM, KVATTN_EHIP, KVATTN_ENODEV,
+    KvattnError, Context, Ubatch, kvattn_params, kvattn_batch, kvattn_ubatch, load, LIB_PATH,
+    kvattn_workspace_bytes, kvattn_cache_bytes, kvattn_create, kvattn_destroy, kvattn_split,
+    kvattn_store, kvattn_attend, kvattn_n_kv, kvattn_get_mask, kvattn_get_classes, kvattn_get_cells,
+    kvattn_seq_rm, kvattn_seq_pos_max, kvattn_plan_stats, kvattn_last_error,
+)
+
+load()

@@ -1,0 +1,526 @@
+// C ABI of the library (include/kvattn.h): context, workspace carve-up,
+// pinned staging of the per-ubatch plan, and the store / attend sequences.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "host_core.hpp"
+#include "kvattn.h"
+#include "launch.hpp"
+
+using namespace kvattn;
+
+namespace {
+
+constexpr int kStages = 4;                 // pinned staging buffers in flight
+constexpr int64_t kPartialRowsCap = 16384; // split-K partial rows x layers per launch
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  size_t cpos, cmask, cellcls, counts, csr_cell, csr_pos, csr_mask, arena, arena_bytes, part_acc, part_ml;
+  size_t total;
+};
+
+WsLayout ws_layout(const Geometry& g) {
+  WsLayout L{};
+  const size_t sc = static_cast<size_t>(g.n_stream) * g.kv_size;
+  const size_t nseg = (g.kv_size + kSegCells - 1) / kSegCells;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+  L.cpos = take(sc * 4);
+  L.cmask = take(sc * 8);
+  L.cellcls = take(sc * 4);
+  L.counts = take(static_cast<size_t>(kMaxClasses) * nseg * 4);
+  L.csr_cell = take(sc * 4);
+  L.csr_pos = take(sc * 4);
+  L.csr_mask = take(sc * 8);
+  L.arena_bytes = (16u << 20) + 48 * sc + 64 * static_cast<size_t>(g.n_ubatch);
+  L.arena = take(L.arena_bytes);
+  const size_t hd = static_cast<size_t>(g.n_head) * g.head_dim;
+  L.part_acc = take(kPartialRowsCap * hd * 4);
+  L.part_ml = take(kPartialRowsCap * g.n_head * 2 * 4);
+  L.total = o;
+  return L;
+}
+
+// Device offsets of one plan inside the arena.
+struct VariantLayout {
+  size_t slots, qlist, items_valu, items_mfma, red_slot, red_off, red_rows;
+};
+struct ArenaLayout {
+  size_t classes, lookup, lookup_off, dst_rows, updates;
+  VariantLayout v[2];
+  size_t total;
+};
+
+}  // namespace
+
+struct kvattn_ctx {
+  HostCore core;
+  std::string err;
+  int32_t device = 0;
+  bool has_dev = false;
+  std::vector<void*> K, V;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  WsLayout wl{};
+  bool dev_ready = false;
+  void* stage[kStages] = {};
+  size_t stage_cap[kStages] = {};
+  hipEvent_t ev[kStages] = {};
+  bool ev_used[kStages] = {};
+  int stage_next = 0;
+  Plan plan[2];
+  ArenaLayout al{};
+  bool plan_ok = false;
+  int plan_ubatch = -1;       // index in the split of the ubatch whose plan is on the device
+  int32_t plan_serial = -1;
+  std::vector<CellUpdate> upd;
+  std::vector<char> blob;
+
+  int fail(int code, const std::string& msg) {
+    err = msg;
+    return code;
+  }
+  int hip_fail(hipError_t e, const char* where) {
+    err = std::string(where) + ": " + hipGetErrorString(e);
+    return KVATTN_EHIP;
+  }
+  template <class T>
+  T* dptr(size_t off) { return reinterpret_cast<T*>(ws + off); }
+};
+
+#define HIP_TRY(ctx, expr)                              \
+  do {                                                  \
+    hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return (ctx)->hip_fail(e_, #expr); \
+  } while (0)
+
+namespace {
+
+int ensure_device(kvattn_ctx* c) {
+  if (!c->has_dev) return c->fail(KVATTN_ENODEV, "context was created without device buffers");
+  HIP_TRY(c, hipSetDevice(c->device));
+  if (c->dev_ready) return KVATTN_OK;
+  for (int i = 0; i < kStages; ++i) HIP_TRY(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
+  // empty device mirror: every cell free
+  const size_t sc = static_cast<size_t>(c->core.geo().n_stream) * c->core.geo().kv_size;
+  HIP_TRY(c, hipMemset(c->ws + c->wl.cpos, 0xFF, sc * 4));
+  HIP_TRY(c, hipMemset(c->ws + c->wl.cmask, 0, sc * 8));
+  HIP_TRY(c, hipDeviceSynchronize());
+  c->dev_ready = true;
+  return KVATTN_OK;
+}
+
+template <class T>
+size_t put(std::vector<char>& blob, size_t at, const std::vector<T>& v) {
+  if (!v.empty()) std::memcpy(blob.data() + at, v.data(), v.size() * sizeof(T));
+  return at;
+}
+
+// Plan of the committed ubatch k -> pinned staging -> device arena, then the
+// mirror update and the cell-list build, all on stream s.
+int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
+  const Geometry& g = c->core.geo();
+  UbatchRec& u = c->core.ubatches()[k];
+  std::string e0, e1;
+  int rc0 = c->core.build_plan(k, false, c->plan[0], e0);
+  int rc1 = rc0 ? rc0 : c->core.build_plan(k, true, c->plan[1], e1);
+  c->plan_ok = rc0 == KVATTN_OK && rc1 == KVATTN_OK;
+  if (!c->plan_ok) {
+    c->plan[0] = Plan();
+    c->plan[1] = Plan();
+  }
+  const Plan& P0 = c->plan[0];
+  std::vector<int32_t> dst(u.cells.size());
+  for (size_t i = 0; i < u.cells.size(); ++i)
+    dst[i] = static_cast<int32_t>(static_cast<int64_t>(u.stream[i]) * g.kv_size + u.cells[i]);
+
+  // arena layout
+  ArenaLayout& A = c->al;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+  A.classes = take(P0.classes.size() * sizeof(ClassInfo));
+  A.lookup = take(P0.lookup.size() * sizeof(LookupEntry));
+  A.lookup_off = take(P0.lookup_off.size() * 4);
+  A.dst_rows = take(dst.size() * 4);
+  for (int v = 0; v < 2; ++v) {
+    const Plan& P = c->plan[v];
+    A.v[v].slots = take(P.slots.size() * sizeof(SlotInfo));
+    A.v[v].qlist = take(P.qlist.size() * 4);
+    A.v[v].items_valu = take(P.items_valu.size() * sizeof(WorkItem));
+    A.v[v].items_mfma = take(P.items_mfma.size() * sizeof(WorkItem));
+    A.v[v].red_slot = take(P.red_slot.size() * 4);
+    A.v[v].red_off = take(P.red_off.size() * 4);
+    A.v[v].red_rows = take(P.red_rows.size() * 4);
+  }
+  A.updates = take(c->upd.size() * sizeof(CellUpdate));
+  A.total = o;
+  if (A.total > c->wl.arena_bytes) {
+    c->plan_ok = false;
+    return c->fail(KVATTN_ENOMEM, "ubatch plan exceeds the workspace plan arena");
+  }
+  // stage
+  const int st = c->stage_next;
+  c->stage_next = (st + 1) % kStages;
+  if (c->ev_used[st]) HIP_TRY(c, hipEventSynchronize(c->ev[st]));
+  if (c->stage_cap[st] < A.total) {
+    if (c->stage[st]) HIP_TRY(c, hipHostFree(c->stage[st]));
+    c->stage[st] = nullptr;
+    const size_t cap = std::max<size_t>(A.total, 1 << 20);
+    HIP_TRY(c, hipHostMalloc(&c->stage[st], cap, hipHostMallocDefault));
+    c->stage_cap[st] = cap;
+  }
+  char* b = static_cast<char*>(c->stage[st]);
+  auto copy = [&](size_t at, const void* src, size_t bytes) { if (bytes) std::memcpy(b + at, src, bytes); };
+  copy(A.classes, P0.classes.data(), P0.classes.size() * sizeof(ClassInfo));
+  copy(A.lookup, P0.lookup.data(), P0.lookup.size() * sizeof(LookupEntry));
+  copy(A.lookup_off, P0.lookup_off.data(), P0.lookup_off.size() * 4);
+  copy(A.dst_rows, dst.data(), dst.size() * 4);
+  for (int v = 0; v < 2; ++v) {
+    const Plan& P = c->plan[v];
+    copy(A.v[v].slots, P.slots.data(), P.slots.size() * sizeof(SlotInfo));
+    copy(A.v[v].qlist, P.qlist.data(), P.qlist.size() * 4);
+    copy(A.v[v].items_valu, P.items_valu.data(), P.items_valu.size() * sizeof(WorkItem));
+    copy(A.v[v].items_mfma, P.items_mfma.data(), P.items_mfma.size() * sizeof(WorkItem));
+    copy(A.v[v].red_slot, P.red_slot.data(), P.red_slot.size() * 4);
+    copy(A.v[v].red_off, P.red_off.data(), P.red_off.size() * 4);
+    copy(A.v[v].red_rows, P.red_rows.data(), P.red_rows.size() * 4);
+  }
+  copy(A.updates, c->upd.data(), c->upd.size() * sizeof(CellUpdate));
+  char* arena = c->ws + c->wl.arena;
+  if (A.total) HIP_TRY(c, hipMemcpyAsync(arena, b, A.total, hipMemcpyHostToDevice, s));
+  HIP_TRY(c, hipEventRecord(c->ev[st], s));
+  c->ev_used[st] = true;
+
+  CsrArgs ca{};
+  ca.cpos = c->dptr<int32_t>(c->wl.cpos);
+  ca.cmask = c->dptr<uint64_t>(c->wl.cmask);
+  ca.cellcls = c->dptr<int32_t>(c->wl.cellcls);
+  ca.counts = c->dptr<int32_t>(c->wl.counts);
+  ca.csr_cell = c->dptr<int32_t>(c->wl.csr_cell);
+  ca.csr_pos = c->dptr<int32_t>(c->wl.csr_pos);
+  ca.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);
+  ca.classes = reinterpret_cast<const ClassInfo*>(arena + A.classes);
+  ca.lookup = reinterpret_cast<const LookupEntry*>(arena + A.lookup);
+  ca.lookup_off = reinterpret_cast<const int32_t*>(arena + A.lookup_off);
+  ca.updates = reinterpret_cast<const CellUpdate*>(arena + A.updates);
+  ca.n_updates = static_cast<int32_t>(c->upd.size());
+  ca.n_classes = c->plan_ok ? static_cast<int32_t>(P0.classes.size()) : 0;
+  ca.n_seg = P0.n_seg;
+  ca.kv_size = g.kv_size;
+  ca.n_kv = P0.n_kv;
+  ca.n_stream = g.n_stream;
+  ca.csr_cap = g.n_stream * g.kv_size;
+  HIP_TRY(c, launch_commit(ca, s));
+  c->plan_ubatch = k;
+  c->plan_serial = c->core.split_serial();
+  if (!c->plan_ok) return c->fail(rc0 ? rc0 : rc1, rc0 ? e0 : e1);
+  return KVATTN_OK;
+}
+
+int check_ubatch(kvattn_ctx* c, const kvattn_ubatch* ub, int* k) {
+  if (!ub) return c->fail(KVATTN_EINVAL, "ubatch is NULL");
+  *k = c->core.find(ub->id);
+  if (*k < 0) return c->fail(KVATTN_ESTATE, "stale ubatch: it belongs to an earlier split");
+  return KVATTN_OK;
+}
+
+int check_layers(kvattn_ctx* c, int32_t il0, int32_t n_il) {
+  if (il0 < 0 || n_il < 0 || il0 + n_il > c->core.geo().n_layer)
+    return c->fail(KVATTN_EINVAL, "layer range outside [0, n_layer)");
+  return KVATTN_OK;
+}
+
+bool plan_current(kvattn_ctx* c, int k) {
+  return c->plan_ubatch == k && c->plan_serial == c->core.split_serial() && c->core.latest_committed() == k;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvattn_workspace_bytes(const kvattn_params* p) {
+  if (!p) return 0;
+  Geometry g;
+  std::string err;
+  if (make_geometry(*p, g, err)) return 0;
+  return ws_layout(g).total;
+}
+
+size_t kvattn_cache_bytes(const kvattn_params* p) {
+  if (!p) return 0;
+  return 2ull * static_cast<size_t>(p->n_layer) * p->n_stream * p->kv_size * p->n_head_kv * p->head_dim * 2ull;
+}
+
+int kvattn_create(const kvattn_params* p, kvattn_ctx** out) {
+  if (!p || !out) return KVATTN_EINVAL;
+  *out = nullptr;
+  kvattn_ctx* c = new (std::nothrow) kvattn_ctx();
+  if (!c) return KVATTN_ENOMEM;
+  int rc = c->core.init(*p, c->err);
+  if (rc) {
+    delete c;
+    return rc;
+  }
+  const Geometry& g = c->core.geo();
+  c->device = p->device;
+  if (p->k_layers) {
+    c->wl = ws_layout(g);
+    if (!p->v_layers || !p->workspace || p->workspace_bytes < c->wl.total) {
+      delete c;
+      return KVATTN_EINVAL;
+    }
+    for (int l = 0; l < g.n_layer; ++l) {
+      if (!p->k_layers[l] || !p->v_layers[l]) {
+        delete c;
+        return KVATTN_EINVAL;
+      }
+      c->K.push_back(p->k_layers[l]);
+      c->V.push_back(p->v_layers[l]);
+    }
+    c->ws = static_cast<char*>(p->workspace);
+    c->ws_bytes = p->workspace_bytes;
+    c->has_dev = true;
+  }
+  c->core.prow_max = static_cast<int32_t>(std::min<int64_t>(4096, kPartialRowsCap));
+  *out = c;
+  return KVATTN_OK;
+}
+
+void kvattn_destroy(kvattn_ctx* c) {
+  if (!c) return;
+  if (c->dev_ready) {
+    (void)hipSetDevice(c->device);
+    for (int i = 0; i < kStages; ++i) {
+      if (c->ev_used[i]) (void)hipEventSynchronize(c->ev[i]);
+      if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
+      if (c->stage[i]) (void)hipHostFree(c->stage[i]);
+    }
+  }
+  delete c;
+}
+
+int kvattn_split(kvattn_ctx* c, const kvattn_batch* b, kvattn_ubatch* ubs, int32_t cap, int32_t* n_ubs,
+                 int32_t* output_ids) {
+  if (!c) return KVATTN_EINVAL;
+  if (!b || !n_ubs || (cap > 0 && !ubs)) return c->fail(KVATTN_EINVAL, "NULL argument");
+  c->err.clear();
+  *n_ubs = 0;
+  // a split cannot be undone, so check the capacity by dry-running the count
+  int rc = c->core.split(*b, output_ids, c->err);
+  if (rc) return rc;
+  auto& v = c->core.ubatches();
+  if (static_cast<int32_t>(v.size()) > cap) {
+    kvattn_batch empty{0, nullptr, nullptr, nullptr, nullptr};
+    std::string e;
+    c->core.split(empty, nullptr, e);   // releases the reservation
+    return c->fail(KVATTN_EINVAL, "ubatch array too small: need " + std::to_string(v.size()));
+  }
+  for (size_t k = 0; k < v.size(); ++k) {
+    const UbatchRec& u = v[k];
+    kvattn_ubatch& o = ubs[k];
+    o.id = u.id;
+    o.n_tokens = static_cast<int32_t>(u.pos.size());
+    o.n_seq_tokens = u.n_seq_tokens;
+    o.n_seqs = u.n_seqs;
+    o.n_seqs_unq = static_cast<int32_t>(u.seq_unq.size());
+    o.n_outputs = u.n_outputs;
+    o.pos = u.pos.data();
+    o.n_seq_id = u.n_seq_id.data();
+    o.seq_id = u.seq_ptr.data();
+    o.seq_id_unq = u.seq_unq.data();
+    o.output = u.output.data();
+    o.src_idx = u.src.data();
+    o.stream = u.stream.data();
+    o.cells = u.cells.data();
+  }
+  *n_ubs = static_cast<int32_t>(v.size());
+  return KVATTN_OK;
+}
+
+int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_il, const void* const* k_cur,
+                 const void* const* v_cur, void* hip_stream) {
+  if (!c) return KVATTN_EINVAL;
+  int k, rc;
+  if ((rc = check_ubatch(c, ub, &k)) || (rc = check_layers(c, il0, n_il))) return rc;
+  if (n_il > 0 && (!k_cur || !v_cur)) return c->fail(KVATTN_EINVAL, "k_cur / v_cur is NULL");
+  UbatchRec& u = c->core.ubatches()[k];
+  if (!c->has_dev && n_il == 0) {
+    // host-only context: a zero-layer store commits the placement and nothing else
+    if (u.committed) return KVATTN_OK;
+    if (il0 != 0) return c->fail(KVATTN_ESTATE, "the first store of a ubatch must start at layer 0");
+    c->upd.clear();
+    return c->core.commit(k, &c->upd, c->err);
+  }
+  if ((rc = ensure_device(c))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (!u.committed) {
+    if (il0 != 0) return c->fail(KVATTN_ESTATE, "the first store of a ubatch must start at layer 0");
+    c->upd.clear();
+    if ((rc = c->core.commit(k, &c->upd, c->err))) return rc;
+    rc = upload_commit(c, k, s);
+    if (rc && rc != KVATTN_ENOMEM) return rc;
+  } else if (c->core.latest_committed() != k || !plan_current(c, k)) {
+    return c->fail(KVATTN_ESTATE, "only the most recently committed ubatch can be stored again");
+  }
+  const Geometry& g = c->core.geo();
+  StoreArgs a{};
+  a.dst_rows = reinterpret_cast<const int32_t*>(c->ws + c->wl.arena + c->al.dst_rows);
+  a.n_rows = static_cast<int32_t>(u.cells.size());
+  a.E = g.E();
+  for (int32_t l0 = 0; l0 < n_il; l0 += kMaxLayersPerLaunch) {
+    const int n = std::min<int32_t>(kMaxLayersPerLaunch, n_il - l0);
+    for (int i = 0; i < n; ++i) {
+      if (!k_cur[l0 + i] || !v_cur[l0 + i]) return c->fail(KVATTN_EINVAL, "NULL k_cur / v_cur entry");
+      a.k_cur[i] = static_cast<const float*>(k_cur[l0 + i]);
+      a.v_cur[i] = static_cast<const float*>(v_cur[l0 + i]);
+      a.k[i] = static_cast<_Float16*>(c->K[il0 + l0 + i]);
+      a.v[i] = static_cast<_Float16*>(c->V[il0 + l0 + i]);
+    }
+    HIP_TRY(c, launch_store(a, n, s));
+  }
+  return rc;
+}
+
+int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_il, const void* const* q,
+                  void* const* out, int32_t only_outputs, void* hip_stream) {
+  if (!c) return KVATTN_EINVAL;
+  int k, rc;
+  if ((rc = check_ubatch(c, ub, &k)) || (rc = check_layers(c, il0, n_il))) return rc;
+  if (n_il > 0 && (!q || !out)) return c->fail(KVATTN_EINVAL, "q / out is NULL");
+  if ((rc = ensure_device(c))) return rc;
+  if (!c->core.ubatches()[k].committed) return c->fail(KVATTN_ESTATE, "attend before the ubatch was stored");
+  if (!plan_current(c, k)) return c->fail(KVATTN_ESTATE, "attend must follow its own ubatch's store");
+  if (!c->plan_ok) return c->fail(KVATTN_ENOMEM, "no work plan for this ubatch (workspace too small)");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const Geometry& g = c->core.geo();
+  const int v = only_outputs ? 1 : 0;
+  const Plan& P = c->plan[v];
+  const VariantLayout& VL = c->al.v[v];
+  char* arena = c->ws + c->wl.arena;
+  AttnArgs a{};
+  a.slots = reinterpret_cast<const SlotInfo*>(arena + VL.slots);
+  a.classes = reinterpret_cast<const ClassInfo*>(arena + c->al.classes);
+  a.qlist = reinterpret_cast<const int32_t*>(arena + VL.qlist);
+  a.csr_cell = c->dptr<int32_t>(c->wl.csr_cell);
+  a.csr_pos = c->dptr<int32_t>(c->wl.csr_pos);
+  a.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);
+  a.part_acc = c->dptr<float>(c->wl.part_acc);
+  a.part_ml = c->dptr<float>(c->wl.part_ml);
+  a.red_slot = reinterpret_cast<const int32_t*>(arena + VL.red_slot);
+  a.red_off = reinterpret_cast<const int32_t*>(arena + VL.red_off);
+  a.red_rows = reinterpret_cast<const int32_t*>(arena + VL.red_rows);
+  a.rows_per_layer = P.n_partial_rows;
+  a.kv_size = g.kv_size;
+  a.n_head = g.n_head;
+  a.n_head_kv = g.n_head_kv;
+  a.causal = g.causal;
+  a.scale_log2e = g.kq_scale * 1.4426950408889634f;
+  const int64_t per = std::max<int64_t>(1, P.n_partial_rows);
+  const int32_t chunk = static_cast<int32_t>(std::min<int64_t>(kMaxLayersPerLaunch, kPartialRowsCap / per));
+  for (int32_t l0 = 0; l0 < n_il; l0 += chunk) {
+    const int n = std::min<int32_t>(chunk, n_il - l0);
+    for (int i = 0; i < n; ++i) {
+      if (!q[l0 + i] || !out[l0 + i]) return c->fail(KVATTN_EINVAL, "NULL q / out entry");
+      a.q[i] = static_cast<const float*>(q[l0 + i]);
+      a.o[i] = static_cast<float*>(out[l0 + i]);
+      a.k[i] = static_cast<const _Float16*>(c->K[il0 + l0 + i]);
+      a.v[i] = static_cast<const _Float16*>(c->V[il0 + l0 + i]);
+    }
+    a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
+    a.n_items = static_cast<int32_t>(P.items_valu.size());
+    HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s));
+    a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_mfma);
+    a.n_items = static_cast<int32_t>(P.items_mfma.size());
+    HIP_TRY(c, launch_attn_mfma(a, n, g.head_dim, g.G(), s));
+    HIP_TRY(c, launch_reduce(a, static_cast<int32_t>(P.red_slot.size()), n, g.head_dim, s));
+  }
+  return KVATTN_OK;
+}
+
+int32_t kvattn_n_kv(const kvattn_ctx* c) { return c ? c->core.n_kv() : 0; }
+
+int kvattn_get_mask(kvattn_ctx* c, const kvattn_ubatch* ub, void* d_mask, size_t cap_elems, int32_t* n_kv,
+                    void* hip_stream) {
+  if (!c) return KVATTN_EINVAL;
+  int k, rc;
+  if ((rc = check_ubatch(c, ub, &k))) return rc;
+  if ((rc = ensure_device(c))) return rc;
+  if (!plan_current(c, k)) return c->fail(KVATTN_ESTATE, "mask is only kept for the latest committed ubatch");
+  const Plan& P = c->plan[0];
+  const int32_t T = static_cast<int32_t>(c->core.ubatches()[k].pos.size());
+  if (n_kv) *n_kv = P.n_kv;
+  if (static_cast<size_t>(T) * P.n_kv > cap_elems || !d_mask) return c->fail(KVATTN_EINVAL, "mask buffer too small");
+  MaskArgs a{};
+  a.cpos = c->dptr<int32_t>(c->wl.cpos);
+  a.cmask = c->dptr<uint64_t>(c->wl.cmask);
+  a.slots = reinterpret_cast<const SlotInfo*>(c->ws + c->wl.arena + c->al.v[0].slots);
+  a.mask = static_cast<uint16_t*>(d_mask);
+  a.n_rows = T;
+  a.n_kv = P.n_kv;
+  a.kv_size = c->core.geo().kv_size;
+  a.causal = c->core.geo().causal;
+  HIP_TRY(c, launch_mask(a, static_cast<hipStream_t>(hip_stream)));
+  return KVATTN_OK;
+}
+
+int kvattn_get_classes(kvattn_ctx* c, int32_t* n_classes, int32_t* cls_stream, uint64_t* cls_mask,
+                       int32_t* cls_count, int32_t cap_classes, int32_t* n_cells, int32_t* cells, int32_t cap_cells,
+                       void* hip_stream) {
+  if (!c) return KVATTN_EINVAL;
+  int rc;
+  if ((rc = ensure_device(c))) return rc;
+  if (c->plan_ubatch < 0 || !plan_current(c, c->plan_ubatch)) return c->fail(KVATTN_ESTATE, "no committed ubatch");
+  const Plan& P = c->plan[0];
+  if (n_classes) *n_classes = static_cast<int32_t>(P.classes.size());
+  if (n_cells) *n_cells = P.total_cells;
+  for (int32_t i = 0; i < std::min<int32_t>(cap_classes, static_cast<int32_t>(P.classes.size())); ++i) {
+    if (cls_stream) cls_stream[i] = P.classes[i].stream;
+    if (cls_mask) cls_mask[i] = P.classes[i].mask;
+    if (cls_count) cls_count[i] = P.classes[i].n_cells;
+  }
+  const int32_t n = std::min(cap_cells, P.total_cells);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (cells && n > 0)
+    HIP_TRY(c, hipMemcpyAsync(cells, c->ws + c->wl.csr_cell, static_cast<size_t>(n) * 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(c, hipStreamSynchronize(s));
+  return KVATTN_OK;
+}
+
+int kvattn_get_cells(const kvattn_ctx* c, int32_t stream, int32_t* pos, uint64_t* seqmask) {
+  if (!c || stream < 0 || stream >= c->core.geo().n_stream) return KVATTN_EINVAL;
+  c->core.get_cells(stream, pos, seqmask);
+  return KVATTN_OK;
+}
+
+int kvattn_seq_rm(kvattn_ctx* c, int32_t seq_id, int32_t p0, int32_t p1) {
+  if (!c) return KVATTN_EINVAL;
+  int rc = c->core.seq_rm(seq_id, p0, p1);
+  if (rc) return c->fail(rc, "sequence id out of range");
+  return KVATTN_OK;
+}
+
+int32_t kvattn_seq_pos_max(const kvattn_ctx* c, int32_t seq_id) { return c ? c->core.seq_pos_max(seq_id) : -1; }
+
+int kvattn_plan_stats(const kvattn_ctx* c, int32_t only_outputs, int32_t* n_classes, int32_t* n_items_valu,
+                      int32_t* n_items_mfma, int32_t* n_partial_rows, int32_t* n_reduced) {
+  if (!c) return KVATTN_EINVAL;
+  const Plan& P = c->plan[only_outputs ? 1 : 0];
+  if (n_classes) *n_classes = static_cast<int32_t>(P.classes.size());
+  if (n_items_valu) *n_items_valu = static_cast<int32_t>(P.items_valu.size());
+  if (n_items_mfma) *n_items_mfma = static_cast<int32_t>(P.items_mfma.size());
+  if (n_partial_rows) *n_partial_rows = P.n_partial_rows;
+  if (n_reduced) *n_reduced = static_cast<int32_t>(P.red_slot.size());
+  return KVATTN_OK;
+}
+
+const char* kvattn_last_error(const kvattn_ctx* c) { return c ? c->err.c_str() : "NULL context"; }
+
+}  // extern "C"

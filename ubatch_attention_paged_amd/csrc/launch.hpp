@@ -1,0 +1,81 @@
+// Launch wrappers for the gfx950 kernels (kernels.hip).  Argument records
+// are plain structs passed by value as kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.hpp"
+
+namespace kvattn {
+
+struct StoreArgs {
+  const float* k_cur[kMaxLayersPerLaunch];
+  const float* v_cur[kMaxLayersPerLaunch];
+  _Float16* k[kMaxLayersPerLaunch];
+  _Float16* v[kMaxLayersPerLaunch];
+  const int32_t* dst_rows;    // [n_rows] stream * kv_size + cell
+  int32_t n_rows;
+  int32_t E;
+};
+
+struct CsrArgs {
+  int32_t* cpos;              // [S * C] device mirror: position, -1 empty
+  uint64_t* cmask;            // [S * C] sequence-set bitmask
+  int32_t* cellcls;           // [S * C] class of each cell (-1 none), scratch
+  int32_t* counts;            // [n_classes * n_seg] per segment counts, then offsets
+  int32_t* csr_cell;          // [total] cells, class-major, ascending within a class
+  int32_t* csr_pos;
+  uint64_t* csr_mask;
+  const ClassInfo* classes;
+  const LookupEntry* lookup;
+  const int32_t* lookup_off;  // [S + 1]
+  const CellUpdate* updates;
+  int32_t n_updates, n_classes, n_seg, kv_size, n_kv, n_stream;
+  int32_t csr_cap;            // entries of csr_*: n_stream * kv_size
+};
+
+struct AttnArgs {
+  const float* q[kMaxLayersPerLaunch];
+  float* o[kMaxLayersPerLaunch];
+  const _Float16* k[kMaxLayersPerLaunch];
+  const _Float16* v[kMaxLayersPerLaunch];
+  const SlotInfo* slots;
+  const ClassInfo* classes;
+  const int32_t* qlist;
+  const WorkItem* items;
+  const int32_t* csr_cell;
+  const int32_t* csr_pos;
+  const uint64_t* csr_mask;
+  float* part_acc;            // [n_il][rows][n_head * head_dim]
+  float* part_ml;             // [n_il][rows][n_head][2]  (max in log2 units, sum)
+  const int32_t* red_slot;
+  const int32_t* red_off;
+  const int32_t* red_rows;
+  int32_t rows_per_layer;
+  int32_t n_items;
+  int32_t kv_size;
+  int32_t n_head;
+  int32_t n_head_kv;
+  int32_t causal;
+  float scale_log2e;          // kq_scale * log2(e)
+};
+
+struct MaskArgs {
+  const int32_t* cpos;
+  const uint64_t* cmask;
+  const SlotInfo* slots;      // ubatch order
+  uint16_t* mask;             // [n_rows][n_kv]
+  int32_t n_rows, n_kv, kv_size, causal;
+};
+
+hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s);
+hipError_t launch_commit(const CsrArgs& a, hipStream_t s);
+hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
+// head_dim / group size are dispatched at run time
+hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s);
+hipError_t launch_reduce(const AttnArgs& a, int n_reduced, int n_il, int head_dim, hipStream_t s);
+
+}  // namespace kvattn

@@ -1,0 +1,70 @@
+// Plain-old-data records shared by the host planner and the gfx950 kernels.
+//
+// A committed ubatch is turned into a "plan": its query slots, the classes of
+// cells its queries may see, and the work items the attention kernels run.
+// A class is a set of committed cells of one stream whose sequence sets are
+// equal (or, past a cap, a merged group of such sets); every query whose
+// first sequence id lies in the class's set attends over the class's cells,
+// subject to the causal test -- the mask of "llama.cpp and the ubatch", "The
+// mask is doing the work", kept in sparse form.  Cells of one class are
+// listed in ascending cell index by the GPU (csr_* kernels).
+#pragma once
+
+#include <cstdint>
+
+namespace kvattn {
+
+constexpr int kMaxSeq = 64;            // sequence ids are bits of a uint64_t
+constexpr int kMaxLayersPerLaunch = 32;
+constexpr int kMaxClasses = 1024;      // per ubatch; extra sequence sets are merged
+constexpr int kSegCells = 64;          // cells per counting segment (one wavefront)
+constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
+
+struct SlotInfo {        // one query slot
+  int32_t stream;
+  int32_t pos;
+  int32_t seq0;          // first sequence id: the one the query masks with
+  int32_t q_row;         // row of q (ubatch order)
+  int32_t out_row;       // row of the output (ubatch row, or rank among outputs)
+  int32_t pad[3];
+};
+
+struct CellUpdate {      // one cell of the device mirror to overwrite
+  int32_t idx;           // stream * kv_size + cell
+  int32_t pos;           // -1 = empty
+  uint64_t mask;         // sequence-set bitmask
+};
+
+struct LookupEntry {     // sorted by (stream, mask); maps a cell's set to its class
+  uint64_t mask;
+  int32_t cls;
+  int32_t pad;
+};
+
+struct ClassInfo {
+  uint64_t mask;         // OR of the member sets
+  int32_t stream;
+  int32_t n_cells;
+  int32_t cell_off;      // first entry in the csr arrays
+  int32_t q_off;         // first entry in qlist
+  int32_t n_q;
+  int32_t pure;          // 1: one sequence set, which every listed query belongs to
+};
+
+struct WorkItem {        // one workgroup (per KV head for the MFMA kernel)
+  int32_t cls;
+  int32_t q_off;         // queries qlist[q_off .. q_off + n_q)
+  int32_t n_q;
+  int32_t c0, c1;        // csr range [c0, c1)
+  int32_t prow;          // first partial row, -1 = write the output directly
+  int32_t qpos_min, qpos_max;
+};
+
+// Byte offsets of each plan array inside the device plan arena.
+struct PlanLayout {
+  int64_t slots, classes, lookup, lookup_off, qlist, items_valu, items_mfma;
+  int64_t red_slot, red_off, red_rows, updates;
+  int64_t total;
+};
+
+}  // namespace kvattn

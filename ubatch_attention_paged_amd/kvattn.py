@@ -1,0 +1,383 @@
+"""ctypes binding of libkvattn.so (include/kvattn.h), same names as the C ABI.
+
+Argument marshalling only: every step of the path runs in the library.  The
+``Context`` class adds torch plumbing -- it allocates the F16 K/V caches and
+the workspace on the GPU and passes their addresses down.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvattn.so")
+
+KVATTN_OK, KVATTN_NO_SLOT = 0, 1
+KVATTN_EINVAL, KVATTN_ESTATE, KVATTN_ENOMEM, KVATTN_EHIP, KVATTN_ENODEV = -1, -2, -3, -4, -5
+MAX_SEQ = 64
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_vpp = ctypes.POINTER(ctypes.c_void_p)
+
+
+class kvattn_params(ctypes.Structure):
+    _fields_ = [("n_layer", ctypes.c_int32), ("n_head", ctypes.c_int32),
+                ("n_head_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_size", ctypes.c_int32), ("n_stream", ctypes.c_int32),
+                ("n_seq_max", ctypes.c_int32), ("n_batch", ctypes.c_int32),
+                ("n_ubatch", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("kq_scale", ctypes.c_float), ("cell_order", _i32p),
+                ("k_layers", _vpp), ("v_layers", _vpp),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("device", ctypes.c_int32)]
+
+
+class kvattn_batch(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int32), ("pos", _i32p), ("n_seq_id", _i32p),
+                ("seq_id", ctypes.POINTER(_i32p)), ("output", ctypes.POINTER(ctypes.c_int8))]
+
+
+class kvattn_ubatch(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int32), ("n_tokens", ctypes.c_int32),
+                ("n_seq_tokens", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("n_seqs_unq", ctypes.c_int32), ("n_outputs", ctypes.c_int32),
+                ("pos", _i32p), ("n_seq_id", _i32p), ("seq_id", ctypes.POINTER(_i32p)),
+                ("seq_id_unq", _i32p), ("output", ctypes.POINTER(ctypes.c_int8)),
+                ("src_idx", _i32p), ("stream", _i32p), ("cells", _i32p)]
+
+
+class KvattnError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"kvattn error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+SIGNATURES = {
+    "kvattn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(kvattn_params)]),
+    "kvattn_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(kvattn_params)]),
+    "kvattn_create": (ctypes.c_int, [ctypes.POINTER(kvattn_params), ctypes.POINTER(ctypes.c_void_p)]),
+    "kvattn_destroy": (None, [ctypes.c_void_p]),
+    "kvattn_split": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_batch),
+                                    ctypes.POINTER(kvattn_ubatch), ctypes.c_int32, _i32p, _i32p]),
+    "kvattn_store": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_int32,
+                                    ctypes.c_int32, _vpp, _vpp, ctypes.c_void_p]),
+    "kvattn_attend": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_int32,
+                                     ctypes.c_int32, _vpp, _vpp, ctypes.c_int32, ctypes.c_void_p]),
+    "kvattn_n_kv": (ctypes.c_int32, [ctypes.c_void_p]),
+    "kvattn_get_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_void_p,
+                                       ctypes.c_size_t, _i32p, ctypes.c_void_p]),
+    "kvattn_get_classes": (ctypes.c_int, [ctypes.c_void_p, _i32p, _i32p, _u64p, _i32p, ctypes.c_int32,
+                                          _i32p, _i32p, ctypes.c_int32, ctypes.c_void_p]),
+    "kvattn_get_cells": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, _i32p, _u64p]),
+    "kvattn_seq_rm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "kvattn_seq_pos_max": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvattn_plan_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p]),
+    "kvattn_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
+}
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library; raises when it has not been built (there is no
+    fallback implementation)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m ubatch_attention_paged_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _arr(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.POINTER(np.ctypeslib.as_ctypes_type(dtype)))
+
+
+# --- thin wrappers with the C names ---------------------------------------
+
+def kvattn_workspace_bytes(p: kvattn_params) -> int:
+    return load().kvattn_workspace_bytes(ctypes.byref(p))
+
+
+def kvattn_cache_bytes(p: kvattn_params) -> int:
+    return load().kvattn_cache_bytes(ctypes.byref(p))
+
+
+def kvattn_create(p: kvattn_params) -> ctypes.c_void_p:
+    ctx = ctypes.c_void_p()
+    rc = load().kvattn_create(ctypes.byref(p), ctypes.byref(ctx))
+    if rc != 0:
+        raise KvattnError(rc, "kvattn_create rejected the parameters")
+    return ctx
+
+
+def kvattn_destroy(ctx):
+    load().kvattn_destroy(ctx)
+
+
+def kvattn_last_error(ctx) -> str:
+    r = load().kvattn_last_error(ctx)
+    return r.decode() if r else ""
+
+
+class Ubatch:
+    """Host-side copy of a kvattn_ubatch plus the raw struct for later calls."""
+
+    def __init__(self, raw: kvattn_ubatch):
+        self.raw = raw
+        n = raw.n_tokens
+        self.id = raw.id
+        self.n_tokens = n
+        self.n_seq_tokens, self.n_seqs = raw.n_seq_tokens, raw.n_seqs
+        self.n_outputs = raw.n_outputs
+        take = lambda p, k, dt: np.ctypeslib.as_array(p, shape=(k,)).astype(dt).copy() if k else np.zeros(0, dt)
+        self.pos = take(raw.pos, n, np.int32)
+        self.src = take(raw.src_idx, n, np.int32)
+        self.stream = take(raw.stream, n, np.int32)
+        self.cells = take(raw.cells, n, np.int32)
+        self.output = take(raw.output, n, np.int8)
+        nsid = take(raw.n_seq_id, n, np.int32)
+        self.seq_ids = [tuple(raw.seq_id[i][t] for t in range(nsid[i])) for i in range(n)]
+        self.seq_id_unq = take(raw.seq_id_unq, raw.n_seqs_unq, np.int32)
+
+
+def kvattn_split(ctx, n_tokens, pos=None, seq_ids=None, output=None, cap=None, n_batch_ids=0):
+    """Returns (status, [Ubatch], output_ids or None).  status is 0 or 1
+    (no room); invalid input raises KvattnError."""
+    lib = load()
+    keep = []
+    b = kvattn_batch()
+    b.n_tokens = n_tokens
+    if pos is not None:
+        a, p = _arr(pos, np.int32)
+        keep.append(a)
+        b.pos = p
+    if seq_ids is not None:
+        rows = []
+        ptrs = (_i32p * max(1, n_tokens))()
+        nsid, pn = _arr([len(s) for s in seq_ids], np.int32)
+        for i, s in enumerate(seq_ids):
+            r = np.ascontiguousarray(s, dtype=np.int32)
+            rows.append(r)
+            ptrs[i] = r.ctypes.data_as(_i32p)
+        keep += rows + [nsid, ptrs]
+        b.seq_id = ctypes.cast(ptrs, ctypes.POINTER(_i32p))
+        b.n_seq_id = pn
+    if output is not None:
+        a, p = _arr(output, np.int8)
+        keep.append(a)
+        b.output = p
+    if cap is None:
+        cap = max(1, n_tokens)
+    ubs = (kvattn_ubatch * cap)()
+    n_ubs = ctypes.c_int32(0)
+    ids = np.zeros(max(1, n_batch_ids), np.int32)
+    rc = lib.kvattn_split(ctx, ctypes.byref(b), ubs, cap, ctypes.byref(n_ubs),
+                          ids.ctypes.data_as(_i32p) if n_batch_ids else None)
+    if rc < 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+    if rc == KVATTN_NO_SLOT:
+        return rc, [], None
+    return rc, [Ubatch(ubs[k]) for k in range(n_ubs.value)], (ids if n_batch_ids else None)
+
+
+def _ptrs(vals):
+    arr = (ctypes.c_void_p * max(1, len(vals)))(*[int(v) for v in vals])
+    return arr
+
+
+def kvattn_store(ctx, ub: Ubatch, il0, k_ptrs: Sequence[int], v_ptrs: Sequence[int], stream=0):
+    rc = load().kvattn_store(ctx, ctypes.byref(ub.raw), il0, len(k_ptrs),
+                             ctypes.cast(_ptrs(k_ptrs), _vpp), ctypes.cast(_ptrs(v_ptrs), _vpp),
+                             ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+
+
+def kvattn_attend(ctx, ub: Ubatch, il0, q_ptrs: Sequence[int], out_ptrs: Sequence[int], only_outputs=0, stream=0):
+    rc = load().kvattn_attend(ctx, ctypes.byref(ub.raw), il0, len(q_ptrs),
+                              ctypes.cast(_ptrs(q_ptrs), _vpp), ctypes.cast(_ptrs(out_ptrs), _vpp),
+                              int(only_outputs), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+
+
+def kvattn_n_kv(ctx) -> int:
+    return load().kvattn_n_kv(ctx)
+
+
+def kvattn_get_mask(ctx, ub: Ubatch, d_mask_ptr: int, cap_elems: int, stream=0) -> int:
+    nkv = ctypes.c_int32(0)
+    rc = load().kvattn_get_mask(ctx, ctypes.byref(ub.raw), ctypes.c_void_p(d_mask_ptr), cap_elems,
+                                ctypes.byref(nkv), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+    return nkv.value
+
+
+def kvattn_get_classes(ctx, stream=0):
+    """Returns list of (stream, mask, cells ndarray) in class order."""
+    lib = load()
+    ncls, ncells = ctypes.c_int32(0), ctypes.c_int32(0)
+    rc = lib.kvattn_get_classes(ctx, ctypes.byref(ncls), None, None, None, 0, ctypes.byref(ncells), None, 0,
+                                ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+    k, n = ncls.value, ncells.value
+    st = np.zeros(max(1, k), np.int32)
+    mk = np.zeros(max(1, k), np.uint64)
+    ct = np.zeros(max(1, k), np.int32)
+    cells = np.zeros(max(1, n), np.int32)
+    rc = lib.kvattn_get_classes(ctx, ctypes.byref(ncls), st.ctypes.data_as(_i32p), mk.ctypes.data_as(_u64p),
+                                ct.ctypes.data_as(_i32p), k, ctypes.byref(ncells), cells.ctypes.data_as(_i32p), n,
+                                ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+    out, off = [], 0
+    for i in range(k):
+        out.append((int(st[i]), int(mk[i]), cells[off:off + ct[i]].copy()))
+        off += ct[i]
+    return out
+
+
+def kvattn_get_cells(ctx, stream: int, kv_size: int):
+    pos = np.zeros(kv_size, np.int32)
+    mask = np.zeros(kv_size, np.uint64)
+    rc = load().kvattn_get_cells(ctx, stream, pos.ctypes.data_as(_i32p), mask.ctypes.data_as(_u64p))
+    if rc != 0:
+        raise KvattnError(rc, "kvattn_get_cells")
+    return pos, mask
+
+
+def kvattn_seq_rm(ctx, seq_id, p0=-1, p1=-1):
+    rc = load().kvattn_seq_rm(ctx, seq_id, p0, p1)
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+
+
+def kvattn_seq_pos_max(ctx, seq_id) -> int:
+    return load().kvattn_seq_pos_max(ctx, seq_id)
+
+
+def kvattn_plan_stats(ctx, only_outputs=0):
+    vals = [ctypes.c_int32(0) for _ in range(5)]
+    load().kvattn_plan_stats(ctx, int(only_outputs), *[ctypes.byref(v) for v in vals])
+    keys = ("n_classes", "n_items_valu", "n_items_mfma", "n_partial_rows", "n_reduced")
+    return dict(zip(keys, [v.value for v in vals]))
+
+
+# --- torch plumbing ----------------------------------------------------------
+
+class Context:
+    """One library context plus its device memory.
+
+    The caches live in one torch allocation holding K0, V0, K1, V1, ... in
+    layer order ("What does llama.cpp's KV cache actually look like in
+    memory?", "28 layers, 56 tensors"); each tensor is [n_stream][kv_size][E]
+    F16.  ``device=None`` makes a host-only context (split / placement only).
+    """
+
+    def __init__(self, n_layer, n_head, n_head_kv, head_dim, kv_size, n_stream=1, n_seq_max=1,
+                 n_batch=0, n_ubatch=512, causal=True, kq_scale=0.0, cell_order=None, device=None):
+        self.n_layer, self.n_head, self.n_head_kv, self.head_dim = n_layer, n_head, n_head_kv, head_dim
+        self.kv_size, self.n_stream, self.n_seq_max = kv_size, n_stream, n_seq_max
+        self.E = n_head_kv * head_dim
+        p = kvattn_params()
+        p.n_layer, p.n_head, p.n_head_kv, p.head_dim = n_layer, n_head, n_head_kv, head_dim
+        p.kv_size, p.n_stream, p.n_seq_max = kv_size, n_stream, n_seq_max
+        p.n_batch, p.n_ubatch, p.causal, p.kq_scale = n_batch, n_ubatch, int(bool(causal)), kq_scale
+        self._order = None
+        if cell_order is not None:
+            self._order, p.cell_order = _arr(np.asarray(cell_order).reshape(-1), np.int32)
+        self.device = device
+        self.cache = None
+        if device is not None:
+            import torch
+            dev = torch.device(device)
+            p.device = dev.index or 0
+            per = n_stream * kv_size * self.E
+            self.cache = torch.zeros(2 * n_layer * per, dtype=torch.float16, device=dev)
+            self.K = [self.cache[(2 * l) * per:(2 * l + 1) * per].view(n_stream, kv_size, self.E) for l in range(n_layer)]
+            self.V = [self.cache[(2 * l + 1) * per:(2 * l + 2) * per].view(n_stream, kv_size, self.E) for l in range(n_layer)]
+            ws = kvattn_workspace_bytes(p)
+            if ws == 0:
+                raise KvattnError(KVATTN_EINVAL, "invalid parameters")
+            self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+            self._kp = _ptrs([t.data_ptr() for t in self.K])
+            self._vp = _ptrs([t.data_ptr() for t in self.V])
+            p.k_layers = ctypes.cast(self._kp, _vpp)
+            p.v_layers = ctypes.cast(self._vp, _vpp)
+            p.workspace = self.workspace.data_ptr()
+            p.workspace_bytes = ws
+        self.params = p
+        self.ctx = kvattn_create(p)
+
+    def close(self):
+        if self.ctx:
+            kvattn_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _stream(self, stream):
+        if stream is not None:
+            return stream
+        if self.device is None:
+            return 0
+        import torch
+        return torch.cuda.current_stream(torch.device(self.device)).cuda_stream
+
+    def split(self, n_tokens, pos=None, seq_ids=None, output=None, with_ids=False):
+        from_ids = self.n_batch_clamped() if with_ids else 0
+        return kvattn_split(self.ctx, n_tokens, pos, seq_ids, output, n_batch_ids=from_ids)
+
+    def n_batch_clamped(self):
+        n_ctx = self.kv_size * self.n_stream
+        nb = self.params.n_batch if self.params.n_batch > 0 else 2048
+        return min(n_ctx, nb) if self.params.causal else nb
+
+    def store(self, ub, il0, k_list, v_list, stream=None):
+        kvattn_store(self.ctx, ub, il0, [t.data_ptr() for t in k_list], [t.data_ptr() for t in v_list],
+                     self._stream(stream))
+
+    def attend(self, ub, il0, q_list, out_list, only_outputs=False, stream=None):
+        kvattn_attend(self.ctx, ub, il0, [t.data_ptr() for t in q_list], [t.data_ptr() for t in out_list],
+                      only_outputs, self._stream(stream))
+
+    def mask(self, ub, stream=None):
+        import torch
+        nkv = kvattn_n_kv(self.ctx)
+        buf = torch.empty(ub.n_tokens * nkv, dtype=torch.int16, device=self.device)
+        got = kvattn_get_mask(self.ctx, ub, buf.data_ptr(), buf.numel(), self._stream(stream))
+        return buf[:ub.n_tokens * got].view(ub.n_tokens, got)
+
+    def classes(self, stream=None):
+        return kvattn_get_classes(self.ctx, self._stream(stream))
+
+    def cells(self, stream=0):
+        return kvattn_get_cells(self.ctx, stream, self.kv_size)
+
+    def seq_rm(self, seq_id, p0=-1, p1=-1):
+        kvattn_seq_rm(self.ctx, seq_id, p0, p1)
+
+    def n_kv(self):
+        return kvattn_n_kv(self.ctx)
+
+    def plan_stats(self, only_outputs=False):
+        return kvattn_plan_stats(self.ctx, only_outputs)
