@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-ubatch attention step on one MI355X.
+
+Default workload: a 3000-token prompt on the Qwen3-0.6B shape (28 layers, 16
+query heads over 8 KV heads of 128, F16 cache of 4096 cells), submitted as
+caller calls of 2048 + 952 slots and split into six 512/440-slot ubatches.
+One step = the whole path for that prompt: split + placement, then for every
+ubatch the F16 K/V store, the visibility-list build and the attention, all
+28 layers.  The cache is cleared before each step (the previous request is
+retired).  Inputs are seeded synthetic tensors already resident in HBM.
+
+Two decode workloads are measured in the same run and reported under
+"decode": 64 continuous-batching sequences with contexts 64..2048 over a
+shuffled 65536-cell cache, and 32 sequences sharing a 2048-cell prefix.  A
+decode step appends one token per sequence (positions advance each step).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense F16 matrix peak, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gen_tensors(wl, b, layers, with_q, dev):
+    import torch
+    from synthetic import workloads as W
+    kinds = [W.KIND_K, W.KIND_V] + ([W.KIND_Q] if with_q else [])
+    jobs = [(l, k) for l in layers for k in kinds]
+    with ThreadPoolExecutor(16) as ex:
+        arrs = list(ex.map(lambda lk: wl.tensor(b, lk[0], lk[1]), jobs))
+    d = {jk: torch.from_numpy(a).to(dev, non_blocking=False) for jk, a in zip(jobs, arrs)}
+    K = [d[(l, W.KIND_K)] for l in layers]
+    V = [d[(l, W.KIND_V)] for l in layers]
+    Q = [d[(l, W.KIND_Q)] for l in layers] if with_q else None
+    return K, V, Q
+
+
+def make_ctx(wl, dev):
+    from ubatch_attention_paged_amd import Context
+    return Context(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
+                   wl.n_seq_max, wl.n_batch, wl.n_ubatch, wl.causal, cell_order=wl.cell_order,
+                   device=dev)
+
+
+class Runner:
+    """Drives measured batches through the library with HIP events around
+    every attend call (on torch's current stream, where the library
+    launches)."""
+
+    def __init__(self, ctx, layer_chunk):
+        self.ctx = ctx
+        self.chunk = layer_chunk
+        self.attend_ms = []
+        self.store_calls = 0
+
+    def run_batch(self, n, pos, seqs, out_flags, K, V, Q, outs, timed):
+        import torch
+        from ubatch_attention_paged_amd.harness import ubatch_rows
+        ctx = self.ctx
+        st, ubs, _ = ctx.split(n, pos, seqs, out_flags)
+        if st != 0:
+            raise RuntimeError("cache full")
+        L = len(K)
+        for ub in ubs:
+            kr = [ubatch_rows(ub, x) for x in K]
+            vr = [ubatch_rows(ub, x) for x in V]
+            qr = [ubatch_rows(ub, x) for x in Q]
+            orow = [o[:ub.n_tokens] for o in outs]
+            for a in range(0, L, self.chunk):
+                b = min(L, a + self.chunk)
+                ctx.store(ub, a, kr[a:b], vr[a:b])
+                if timed:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                ctx.attend(ub, a, qr[a:b], orow[a:b])
+                if timed:
+                    e1.record()
+                    self.attend_ms.append((e0, e1))
+        return ubs
+
+    def attend_avg_ms(self):
+        import torch
+        torch.cuda.synchronize()
+        vals = [a.elapsed_time(b) for a, b in self.attend_ms]
+        return float(np.mean(vals)) if vals else float("nan"), len(vals)
+
+
+# ---------------------------------------------------------------------------
+# prefill (headline)
+
+def prefill_pairs(wl):
+    """Visible (query, cell) pairs of one step: every prompt token sees
+    itself and every earlier token of its sequence."""
+    return sum(int((bt.pos.astype(np.int64) + 1).sum()) for bt in wl.batches)
+
+
+def bench_prefill(wl, dev, steps, warmup, layer_chunk):
+    import torch
+    ctx = make_ctx(wl, dev)
+    layers = list(range(wl.n_layer))
+    log(f"[bench] prefill: generating inputs ({wl.note})")
+    from ubatch_attention_paged_amd import SeqIds
+    data = [gen_tensors(wl, b, layers, True, dev) for b in range(len(wl.batches))]
+    sids = [SeqIds(bt.seq_ids) for bt in wl.batches]
+    HD = wl.n_head * wl.head_dim
+    outs = [torch.empty((wl.n_ubatch, HD), dtype=torch.float32, device=dev) for _ in layers]
+    runner = Runner(ctx, layer_chunk)
+
+    def step(timed):
+        ctx.seq_rm(-1)                          # retire the previous request
+        for b, bt in enumerate(wl.batches):
+            K, V, Q = data[b]
+            runner.run_batch(bt.n_tokens, bt.pos, sids[b], bt.output, K, V, Q, outs, timed)
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms, n_launch = runner.attend_avg_ms()
+    stats = ctx.plan_stats()
+    pairs = prefill_pairs(wl)
+    flops_step = 4.0 * wl.n_head * wl.head_dim * wl.n_layer * pairs
+    n_ub_step = n_launch / steps
+    res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens=wl.measured_tokens(),
+               flops_step=flops_step, attend_launches_per_step=n_ub_step, attend_avg_ms=avg_ms,
+               attend_ms_per_step=avg_ms * n_ub_step, last_plan=stats)
+    ctx.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# decode
+
+def decode_step_cells(wl, t):
+    """Unique cells read by decode step t (the context of every sequence
+    plus the new token; a cell shared by several sequences counts once)."""
+    ctx_cells = set()
+    # cells are identified by (first batch, slot) of the setup batches
+    for b, bt in enumerate(wl.batches):
+        if bt.measured:
+            continue
+        for i in range(bt.n_tokens):
+            ctx_cells.add((b, i))
+    n_seq = wl.batches[-1].n_tokens
+    return len(ctx_cells) + n_seq * (t + 1)
+
+
+def bench_decode(wl, dev, steps, warmup, layer_chunk):
+    import torch
+    from ubatch_attention_paged_amd.harness import decode
+    ctx = make_ctx(wl, dev)
+    layers = list(range(wl.n_layer))
+    log(f"[bench] decode {wl.name}: filling the context ({wl.note})")
+    t0 = time.perf_counter()
+    for b, bt in enumerate(wl.batches):
+        if bt.measured:
+            continue
+        K, V, _ = gen_tensors(wl, b, layers, False, dev)
+        st, _, _ = decode(ctx, bt.n_tokens, bt.pos, bt.seq_ids, bt.output, K, V)
+        assert st == 0
+        del K, V
+    torch.cuda.synchronize()
+    log(f"[bench] decode {wl.name}: context filled in {time.perf_counter() - t0:.1f}s")
+    mb = len(wl.batches) - 1
+    bt = wl.batches[mb]
+    K, V, Q = gen_tensors(wl, mb, layers, True, dev)
+    from ubatch_attention_paged_amd import SeqIds
+    sid = SeqIds(bt.seq_ids)
+    HD = wl.n_head * wl.head_dim
+    outs = [torch.empty((bt.n_tokens, HD), dtype=torch.float32, device=dev) for _ in layers]
+    runner = Runner(ctx, layer_chunk)
+    t = 0
+    for _ in range(warmup):
+        runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, False)
+        t += 1
+    torch.cuda.synchronize()
+    t_first = t
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, True)
+        t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_ms, n_launch = runner.attend_avg_ms()
+    cells = np.mean([decode_step_cells(wl, s) for s in range(t_first, t)])
+    row = 2 * wl.n_head_kv * wl.head_dim * 2                       # K + V bytes per cell per layer
+    kv_bytes = cells * row * wl.n_layer
+    qo_bytes = 2 * bt.n_tokens * HD * 4 * wl.n_layer
+    per_launch = (kv_bytes + qo_bytes) / (n_launch / steps)
+    gbs = per_launch / (avg_ms * 1e-3) / 1e9
+    res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens_per_step=bt.n_tokens,
+               tokens_per_s=bt.n_tokens * steps / wall, unique_cells=float(cells),
+               kv_bytes_step=kv_bytes, attend_avg_ms=avg_ms, attend_launches_per_step=n_launch / steps,
+               kv_read_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, plan=ctx.plan_stats())
+    ctx.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# oracle on the host cores
+
+def cpu_baseline(wl, budget_s=25.0):
+    """The fp64 oracle over the same prompt for as many layers as fit in
+    about budget_s, scaled to the full step."""
+    from oracle import OracleEngine
+    from synthetic import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    done_layers, t_all = 0, 0.0
+    for layer in range(wl.n_layer):
+        eng = OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
+                           wl.n_seq_max, wl.n_batch, wl.n_ubatch, wl.causal, cell_order=wl.cell_order,
+                           layers=[layer])
+        tens = [(wl.tensor(b, layer, W.KIND_K), wl.tensor(b, layer, W.KIND_V), wl.tensor(b, layer, W.KIND_Q))
+                for b in range(len(wl.batches))]
+        t0 = time.perf_counter()
+        for b, bt in enumerate(wl.batches):
+            st, ubs, _ = eng.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+            k, v, q = tens[b]
+            for ub in ubs:
+                eng.commit(ub)
+                eng.store(ub, layer, k[ub.src], v[ub.src])
+                eng.attend(ub, layer, q[ub.src])
+        t_all += time.perf_counter() - t0
+        done_layers += 1
+        if t_all >= budget_s:
+            break
+    per_step = t_all / done_layers * wl.n_layer
+    return dict(value=wl.measured_tokens() / per_step, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"{done_layers} of {wl.n_layer} layers of the full {wl.measured_tokens()}-token prompt "
+                       f"(all {sum(1 for _ in wl.batches)} calls, every ubatch), {t_all:.1f}s, scaled x"
+                       f"{wl.n_layer / done_layers:.1f}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layer-chunk", type=int, default=28,
+                    help="layers per store/attend call (28 = one call per ubatch, 1 = per layer)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--per-layer", action="store_true", help="also time one call per layer")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is not sharded "
+              f"across GPUs in this build", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from synthetic import workloads as W
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = W.qwen_prefill()
+    pre = bench_prefill(wl, dev, args.steps, args.warmup, args.layer_chunk)
+    tok_s = pre["tokens"] * args.steps / pre["wall_s"]
+    mfma_tf = pre["flops_step"] / pre["attend_launches_per_step"] / (pre["attend_avg_ms"] * 1e-3) / 1e12
+    log(f"[bench] prefill: {tok_s:,.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
+        f"attend {pre['attend_avg_ms']:.3f} ms/launch x {pre['attend_launches_per_step']:.0f}, "
+        f"{mfma_tf:.1f} TFLOP/s")
+    line = {
+        "metric": "ubatch attention tokens/s + decode KV-read GB/s (% HBM peak), 1xMI355X",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-0.6B-shape single-sequence prefill: 3000-token prompt, caller calls "
+                               "2048+952, split_simple n_ubatch=512 (6 ubatches), 28 layers, 16 q-heads / "
+                               "8 kv-heads x 128, F16 cache kv_size=4096",
+                   "n_layer": 28, "n_tokens": 3000, "n_batch": 2048, "n_ubatch": 512, "kv_size": 4096,
+                   "layers_per_call": args.layer_chunk, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "k_attn_mfma",
+                     "achieved": round(mfma_tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(mfma_tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "per_launch": f"{pre['flops_step'] / pre['attend_launches_per_step'] / 1e9:.2f} GFLOP "
+                                   f"(4*H*d per visible (query, cell) pair x 28 layers of one ubatch), "
+                                   f"avg {pre['attend_avg_ms']:.3f} ms"},
+    }
+    if args.per_layer:
+        pl = bench_prefill(wl, dev, max(2, args.steps // 2), 1, 1)
+        line["per_layer_calls"] = {"tokens_per_s": round(pl["tokens"] * max(2, args.steps // 2) / pl["wall_s"], 1),
+                                   "ms_per_step": round(pl["ms_per_step"], 3),
+                                   "attend_avg_ms": round(pl["attend_avg_ms"], 4)}
+    if not args.no_decode:
+        dec = {}
+        for name, w in (("cb_decode", W.cb_decode()), ("prefix_decode", W.prefix_decode())):
+            r = bench_decode(w, dev, args.steps, args.warmup, args.layer_chunk)
+            log(f"[bench] {name}: {r['tokens_per_s']:,.0f} tok/s, attend {r['attend_avg_ms']:.3f} ms, "
+                f"{r['kv_read_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% of HBM)")
+            dec[name] = {"workload": w.note, "tokens_per_s": round(r["tokens_per_s"], 1),
+                         "ms_per_step": round(r["ms_per_step"], 4),
+                         "kv_read_gbs": round(r["kv_read_gbs"], 1), "hbm_frac": round(r["hbm_frac"], 4),
+                         "attend_avg_ms": round(r["attend_avg_ms"], 4),
+                         "unique_cells_per_step": r["unique_cells"], "plan": r["plan"]}
+        line["decode"] = dec
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

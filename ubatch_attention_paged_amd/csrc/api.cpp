@@ -403,6 +403,7 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   const Geometry& g = c->core.geo();
   const int v = only_outputs ? 1 : 0;
   const Plan& P = c->plan[v];
+  if (P.slots.empty()) return KVATTN_OK;      // no query rows (e.g. no flagged slot)
   const VariantLayout& VL = c->al.v[v];
   char* arena = c->ws + c->wl.arena;
   AttnArgs a{};

@@ -525,9 +525,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(sacc[kb][i] - m_use);
-        rs += p;
-        pb[kb][i >> 3][i & 7] = static_cast<_Float16>(p);
+        // the row sum uses the same F16-rounded weights the PV product sees
+        const _Float16 ph = static_cast<_Float16>(exp2f(sacc[kb][i] - m_use));
+        rs += static_cast<float>(ph);
+        pb[kb][i >> 3][i & 7] = ph;
       }
     rs += __shfl_xor(rs, 32);
     l_run = l_run * alpha + rs;

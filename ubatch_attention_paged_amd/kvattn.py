@@ -132,6 +132,10 @@ def kvattn_last_error(ctx) -> str:
     return r.decode() if r else ""
 
 
+def _take(p, k, dt):
+    return np.ctypeslib.as_array(p, shape=(k,)).astype(dt) if k else np.zeros(0, dt)
+
+
 class Ubatch:
     """Host-side copy of a kvattn_ubatch plus the raw struct for later calls."""
 
@@ -142,15 +146,43 @@ class Ubatch:
         self.n_tokens = n
         self.n_seq_tokens, self.n_seqs = raw.n_seq_tokens, raw.n_seqs
         self.n_outputs = raw.n_outputs
-        take = lambda p, k, dt: np.ctypeslib.as_array(p, shape=(k,)).astype(dt).copy() if k else np.zeros(0, dt)
-        self.pos = take(raw.pos, n, np.int32)
-        self.src = take(raw.src_idx, n, np.int32)
-        self.stream = take(raw.stream, n, np.int32)
-        self.cells = take(raw.cells, n, np.int32)
-        self.output = take(raw.output, n, np.int8)
-        nsid = take(raw.n_seq_id, n, np.int32)
-        self.seq_ids = [tuple(raw.seq_id[i][t] for t in range(nsid[i])) for i in range(n)]
-        self.seq_id_unq = take(raw.seq_id_unq, raw.n_seqs_unq, np.int32)
+        self.pos = _take(raw.pos, n, np.int32)
+        self.src = _take(raw.src_idx, n, np.int32)
+        self.stream = _take(raw.stream, n, np.int32)
+        self.cells = _take(raw.cells, n, np.int32)
+        self.output = _take(raw.output, n, np.int8)
+        self.seq_id_unq = _take(raw.seq_id_unq, raw.n_seqs_unq, np.int32)
+        self._seq_ids = None
+
+    @property
+    def seq_ids(self):
+        """Sequence ids of every slot (first id first), read on demand."""
+        if self._seq_ids is None:
+            raw, n = self.raw, self.n_tokens
+            nsid = _take(raw.n_seq_id, n, np.int32)
+            self._seq_ids = [tuple(raw.seq_id[i][t] for t in range(nsid[i])) for i in range(n)]
+        return self._seq_ids
+
+
+class SeqIds:
+    """Sequence-id lists marshalled once: a flat int32 array, the count per
+    slot and a matching array of row addresses (what llama_batch.seq_id
+    points at)."""
+
+    def __init__(self, seq_ids):
+        if isinstance(seq_ids, np.ndarray) and seq_ids.ndim == 2:
+            self.flat = np.ascontiguousarray(seq_ids, np.int32).reshape(-1)
+            self.counts = np.full(seq_ids.shape[0], seq_ids.shape[1], np.int32)
+        else:
+            self.counts = np.fromiter((len(s) for s in seq_ids), np.int32, len(seq_ids))
+            self.flat = np.fromiter((x for s in seq_ids for x in s), np.int32, int(self.counts.sum()))
+        offs = np.zeros(len(self.counts), np.int64)
+        if len(self.counts) > 1:
+            offs[1:] = np.cumsum(self.counts[:-1])
+        self.rows = (self.flat.ctypes.data + 4 * offs).astype(np.uint64)
+
+    def __len__(self):
+        return len(self.counts)
 
 
 def kvattn_split(ctx, n_tokens, pos=None, seq_ids=None, output=None, cap=None, n_batch_ids=0):
@@ -165,16 +197,12 @@ def kvattn_split(ctx, n_tokens, pos=None, seq_ids=None, output=None, cap=None, n
         keep.append(a)
         b.pos = p
     if seq_ids is not None:
-        rows = []
-        ptrs = (_i32p * max(1, n_tokens))()
-        nsid, pn = _arr([len(s) for s in seq_ids], np.int32)
-        for i, s in enumerate(seq_ids):
-            r = np.ascontiguousarray(s, dtype=np.int32)
-            rows.append(r)
-            ptrs[i] = r.ctypes.data_as(_i32p)
-        keep += rows + [nsid, ptrs]
-        b.seq_id = ctypes.cast(ptrs, ctypes.POINTER(_i32p))
-        b.n_seq_id = pn
+        sid = seq_ids if isinstance(seq_ids, SeqIds) else SeqIds(seq_ids)
+        if len(sid) < n_tokens:
+            raise KvattnError(KVATTN_EINVAL, "fewer sequence-id lists than tokens")
+        keep.append(sid)
+        b.seq_id = ctypes.cast(ctypes.c_void_p(sid.rows.ctypes.data), ctypes.POINTER(_i32p))
+        b.n_seq_id = sid.counts.ctypes.data_as(_i32p)
     if output is not None:
         a, p = _arr(output, np.int8)
         keep.append(a)
