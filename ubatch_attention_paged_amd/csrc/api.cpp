@@ -23,7 +23,8 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t cpos, cmask, cellcls, counts, csr_cell, csr_pos, csr_mask, arena, arena_bytes, part_acc, part_ml;
+  size_t cpos, cmask, cellcls, counts, csr_cell, csr_pos, csr_mask, tile_min, tile_max, arena, arena_bytes,
+      part_acc, part_ml;
   size_t total;
 };
 
@@ -40,6 +41,9 @@ WsLayout ws_layout(const Geometry& g) {
   L.csr_cell = take(sc * 4);
   L.csr_pos = take(sc * 4);
   L.csr_mask = take(sc * 8);
+  const size_t ntile = sc / kTileCells + kMaxClasses + 1;   // each class adds at most one partial tile
+  L.tile_min = take(ntile * 4);
+  L.tile_max = take(ntile * 4);
   L.arena_bytes = (16u << 20) + 48 * sc + 64 * static_cast<size_t>(g.n_ubatch);
   L.arena = take(L.arena_bytes);
   const size_t hd = static_cast<size_t>(g.n_head) * g.head_dim;
@@ -218,6 +222,9 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
   ca.n_kv = P0.n_kv;
   ca.n_stream = g.n_stream;
   ca.csr_cap = g.n_stream * g.kv_size;
+  ca.tile_min = c->dptr<int32_t>(c->wl.tile_min);
+  ca.tile_max = c->dptr<int32_t>(c->wl.tile_max);
+  ca.max_class_tiles = P0.max_class_tiles;
   HIP_TRY(c, launch_commit(ca, s));
   c->plan_ubatch = k;
   c->plan_serial = c->core.split_serial();
@@ -413,6 +420,8 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   a.csr_cell = c->dptr<int32_t>(c->wl.csr_cell);
   a.csr_pos = c->dptr<int32_t>(c->wl.csr_pos);
   a.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);
+  a.tile_min = c->dptr<int32_t>(c->wl.tile_min);
+  a.tile_max = c->dptr<int32_t>(c->wl.tile_max);
   a.part_acc = c->dptr<float>(c->wl.part_acc);
   a.part_ml = c->dptr<float>(c->wl.part_ml);
   a.red_slot = reinterpret_cast<const int32_t*>(arena + VL.red_slot);

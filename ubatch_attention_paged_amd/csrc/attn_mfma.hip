@@ -1,0 +1,313 @@
+// Prefill-class attention on the gfx950 matrix cores.
+//
+// One workgroup = (work item, KV head): 128 query rows = QT = 128 / G
+// queries x the G query heads that share that KV head, 4 wavefronts of 32
+// rows.  The item's cells are walked in 64-cell tiles:
+//
+//  * K and V rows of a tile (that head's 2*D bytes of each cell row) are
+//    gathered through the cell list with 16 B loads into registers one tile
+//    ahead, then stored row-major into a double-buffered LDS ring; the cell
+//    indices themselves are fetched two tiles ahead.  One barrier per tile.
+//  * Wavefront w computes S^T[64 cells][its 32 rows] = K Q^T with
+//    v_mfma_f32_32x32x16_f16 (A = K rows from LDS, B = its queries, held in
+//    registers as F16 and pre-scaled by scale*log2(e)).
+//  * Each lane owns one query row (column lane % 32 of the accumulators):
+//    mask, online base-2 softmax, then P^T goes straight from the S^T
+//    accumulators into the B operand of O^T = V^T P^T -- a lane's 16 scores
+//    of a 32-cell block are exactly the 8 + 8 k-values it supplies to the two
+//    32x32x16 steps of that block.  The matching A operand (V^T, 8 cells of
+//    one d per lane) comes from the row-major V tile through the LDS
+//    transpose read, in the same cell order.
+//  * Tiles entirely in the future of every query of the item are never
+//    loaded (per-tile position ranges from the commit step); tiles entirely
+//    visible skip the per-element mask.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace kvattn {
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
+  constexpr int QT = 128 / G;                     // queries per item
+  constexpr int KT = kTileCells;                  // cells per tile (64)
+  constexpr int DP = D < 32 ? 32 : D;             // O^T rows, padded to a 32-row block
+  constexpr int KS = D + 16;                      // halfs per LDS row: rows shift by 8 banks
+  constexpr int SEGS = D / 8;                     // 16 B segments per row
+  constexpr int RPP = 256 / SEGS;                 // rows one pass of 256 threads loads
+  constexpr int ROW_STEP = RPP >= KT ? KT : RPP;
+  constexpr int NP = KT / ROW_STEP;               // passes per tile
+  static_assert(KS >= DP, "V rows must hold the padded columns");
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KT * KS];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KT * KS];
+  __shared__ int32_t kpos_s[2][KT];
+  __shared__ uint64_t kmask_s[2][KT];
+
+  const int HK = a.n_head_kv;
+  const int H = a.n_head;
+  const int E = HK * D;
+  const int kvh = blockIdx.x % HK;
+  const WorkItem it = a.items[blockIdx.x / HK];
+  const int il = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int half_id = lane >> 5;
+  const ClassInfo ci = a.classes[it.cls];
+  const bool pure = ci.pure;
+  const _Float16* __restrict__ Kl = a.k[il];
+  const _Float16* __restrict__ Vl = a.v[il];
+  const int64_t sbase = static_cast<int64_t>(ci.stream) * a.kv_size;
+
+  // this lane's query row
+  const int r = 32 * w + (lane & 31);
+  const int hg = r / QT, t = r % QT;
+  const bool qvalid = t < it.n_q;
+  const SlotInfo si = a.slots[a.qlist[it.q_off + (qvalid ? t : 0)]];
+  const int h = kvh * G + hg;
+
+  // B operand of S^T = K Q^T: q[row][16*ks + 8*half + 0..7], scaled, F16
+  half8 qb[D / 16];
+  {
+    const float* qp = a.q[il] + static_cast<int64_t>(si.q_row) * H * D + h * D + 8 * half_id;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const float4 x0 = qvalid ? *reinterpret_cast<const float4*>(qp + 16 * ks) : make_float4(0, 0, 0, 0);
+      const float4 x1 = qvalid ? *reinterpret_cast<const float4*>(qp + 16 * ks + 4) : make_float4(0, 0, 0, 0);
+      qb[ks][0] = static_cast<_Float16>(x0.x * a.scale_log2e);
+      qb[ks][1] = static_cast<_Float16>(x0.y * a.scale_log2e);
+      qb[ks][2] = static_cast<_Float16>(x0.z * a.scale_log2e);
+      qb[ks][3] = static_cast<_Float16>(x0.w * a.scale_log2e);
+      qb[ks][4] = static_cast<_Float16>(x1.x * a.scale_log2e);
+      qb[ks][5] = static_cast<_Float16>(x1.y * a.scale_log2e);
+      qb[ks][6] = static_cast<_Float16>(x1.z * a.scale_log2e);
+      qb[ks][7] = static_cast<_Float16>(x1.w * a.scale_log2e);
+    }
+  }
+  if (D < DP) {   // columns D .. DP-1 of every V row are read as O^T rows >= D: keep them zero
+    for (int i = tid; i < 2 * KT * (DP - D); i += 256) {
+      const int b = i / (KT * (DP - D)), rem = i % (KT * (DP - D));
+      Vs[b][(rem / (DP - D)) * KS + D + rem % (DP - D)] = static_cast<_Float16>(0.f);
+    }
+  }
+
+  // tiles of this item; trailing tiles in the future of every query are dropped
+  const int tb = ci.tile_base + (it.c0 - ci.cell_off) / KT;
+  int ntile = (it.c1 - it.c0 + KT - 1) / KT;
+  if (a.causal) {
+    int last = -1;
+    for (int k = lane; k < ntile; k += 64)
+      if (a.tile_min[tb + k] <= it.qpos_max) last = k;
+    ntile = wave_max_i(last) + 1;
+  }
+
+  floatx16 oacc[DP / 32];
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // loader geometry: thread -> (row0 + p * ROW_STEP, 16 B segment seg)
+  const int seg = tid % SEGS;
+  const int row0 = tid / SEGS;
+  const bool loader = row0 < ROW_STEP;
+  uint4 kreg[NP], vreg[NP];
+  int cnext[NP];
+  int pk = INT32_MAX;
+  uint64_t mk = 0;
+  auto cell_at = [&](int tile, int row) {
+    const int idx = it.c0 + tile * KT + row;
+    return idx < it.c1 ? a.csr_cell[idx] : -1;
+  };
+  auto issue = [&](int tile, const int* cells) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      if (loader && cells[p] >= 0) {
+        const int64_t off = (sbase + cells[p]) * E + kvh * D + seg * 8;
+        kreg[p] = *reinterpret_cast<const uint4*>(Kl + off);
+        vreg[p] = *reinterpret_cast<const uint4*>(Vl + off);
+      } else {
+        kreg[p] = make_uint4(0, 0, 0, 0);
+        vreg[p] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    if (tid < KT) {
+      const int idx = it.c0 + tile * KT + tid;
+      const bool in = idx < it.c1;
+      pk = in ? a.csr_pos[idx] : INT32_MAX;
+      mk = in ? a.csr_mask[idx] : 0ULL;
+    }
+  };
+  if (ntile > 0) {
+    int cfirst[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) cfirst[p] = loader ? cell_at(0, row0 + p * ROW_STEP) : -1;
+    issue(0, cfirst);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) cnext[p] = (loader && ntile > 1) ? cell_at(1, row0 + p * ROW_STEP) : -1;
+  }
+
+  const int s16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1);
+  for (int i = 0; i < ntile; ++i) {
+    const int buf = i & 1;
+    // stage tile i
+    if (loader) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int rr = row0 + p * ROW_STEP;
+        *reinterpret_cast<uint4*>(&Ks[buf][rr * KS + seg * 8]) = kreg[p];
+        *reinterpret_cast<uint4*>(&Vs[buf][rr * KS + seg * 8]) = vreg[p];
+      }
+    }
+    if (tid < KT) {
+      kpos_s[buf][tid] = pk;
+      kmask_s[buf][tid] = mk;
+    }
+    __syncthreads();
+    // tile i+1 loads and tile i+2 cell indices fly while tile i computes
+    if (i + 1 < ntile) {
+      issue(i + 1, cnext);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) cnext[p] = (loader && i + 2 < ntile) ? cell_at(i + 2, row0 + p * ROW_STEP) : -1;
+    }
+
+    const int nk = min(KT, it.c1 - (it.c0 + i * KT));
+    const int pl = kpos_s[buf][lane];
+    const int kmin = wave_min_i(pl);
+    const int kmax = wave_max_i(lane < nk ? pl : INT32_MIN);
+    if (a.causal && kmin > it.qpos_max) continue;
+    const bool full = nk == KT && pure && (!a.causal || kmax <= it.qpos_min);
+
+    floatx16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const half8 ka =
+            *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + (lane & 31)) * KS + 16 * ks + 8 * half_id]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+    if (!full) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * 32 + acc_row(e, lane);
+          bool vis = key < nk && (!a.causal || kpos_s[buf][key] <= si.pos);
+          if (!pure) vis = vis && ((kmask_s[buf][key] >> si.seq0) & 1ULL);
+          if (!vis) sacc[kb][e] = -INFINITY;
+        }
+    }
+    // online softmax over this lane's row (the other half-wave holds the rest)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float rs = 0.f;
+    half8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        // the row sum uses the same F16-rounded weights the PV product sees
+        const _Float16 ph = static_cast<_Float16>(exp2f(sacc[kb][e] - m_use));
+        rs += static_cast<float>(ph);
+        pb[kb][e >> 3][e & 7] = ph;
+      }
+    rs += __shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    // O^T += V^T P^T: source lane s of each 16-lane group points at cell row
+    // key0 + s/4, column dsub + 4*(s%4); lane gets cells key0..key0+3 of column
+    // db*32 + lane%32 (and key0+8.. for the upper four k-values)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int key0 = kb * 32 + 16 * st + 4 * half_id;
+        const _Float16* vb = &Vs[buf][(key0 + (s16 >> 2)) * KS + 4 * (s16 & 3) + dsub];
+#pragma unroll
+        for (int db = 0; db < DP / 32; ++db) {
+          const half4 lo = lds_read_tr16(vb + db * 32);
+          const half4 hi = lds_read_tr16(vb + db * 32 + 8 * KS);
+          half8 va;
+          va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
+          va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kb][st], oacc[db], 0, 0, 0);
+        }
+      }
+  }
+
+  if (!qvalid) return;
+  if (it.prow < 0) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* op = a.o[il] + static_cast<int64_t>(si.out_row) * H * D + h * D;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + acc_row(4 * g4, lane);
+        if (d < D)
+          *reinterpret_cast<float4*>(op + d) =
+              make_float4(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv, oacc[db][4 * g4 + 2] * inv,
+                          oacc[db][4 * g4 + 3] * inv);
+      }
+  } else {
+    const int64_t row = static_cast<int64_t>(il) * a.rows_per_layer + it.prow + t;
+    float* pp = a.part_acc + row * H * D + h * D;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + acc_row(4 * g4, lane);
+        if (d < D)
+          *reinterpret_cast<float4*>(pp + d) =
+              make_float4(oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]);
+      }
+    if (half_id == 0) {
+      a.part_ml[(row * H + h) * 2] = m_run;
+      a.part_ml[(row * H + h) * 2 + 1] = l_run;
+    }
+  }
+}
+
+template <int D, int G>
+static void mfma_launch(const AttnArgs& a, int n_il, hipStream_t s) {
+  hipLaunchKernelGGL((k_attn_mfma<D, G>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256), 0, s, a);
+}
+
+template <int D>
+static hipError_t mfma_by_group(const AttnArgs& a, int n_il, int G, hipStream_t s) {
+  switch (G) {
+    case 1: mfma_launch<D, 1>(a, n_il, s); break;
+    case 2: mfma_launch<D, 2>(a, n_il, s); break;
+    case 4: mfma_launch<D, 4>(a, n_il, s); break;
+    case 8: mfma_launch<D, 8>(a, n_il, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_mfma(const AttnArgs& a, int n_il, int D, int G, hipStream_t s) {
+  if (a.n_items == 0 || n_il == 0) return hipSuccess;
+  switch (D) {
+    case 16: return mfma_by_group<16>(a, n_il, G, s);
+    case 32: return mfma_by_group<32>(a, n_il, G, s);
+    case 64: return mfma_by_group<64>(a, n_il, G, s);
+    case 128: return mfma_by_group<128>(a, n_il, G, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvattn

@@ -1,0 +1,45 @@
+// Small device helpers shared by the gfx950 kernels (64-wide wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace kvattn {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+#define KVATTN_DEV __device__ __forceinline__
+
+KVATTN_DEV uint64_t ballot(bool p) { return __ballot(p); }
+KVATTN_DEV int lane_id() { return threadIdx.x & 63; }
+KVATTN_DEV uint64_t lanemask_lt() { return (1ULL << lane_id()) - 1ULL; }
+KVATTN_DEV int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+
+KVATTN_DEV int wave_min_i(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+KVATTN_DEV int wave_max_i(int v) {
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane l receives element l % 4 of the 8-byte rows addressed by lanes
+// l / 4, 4 + l / 4, 8 + l / 4 and 12 + l / 4 of its group.  So when source
+// lane s points at row (r0 + s / 4), column (c0 + 4 * (s % 4)) of a
+// row-major 16-bit tile, lane l gets rows r0 .. r0+3 of column c0 + l.
+KVATTN_DEV half4 lds_read_tr16(const _Float16* p) {
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4v*)(p));
+  return __builtin_bit_cast(half4, v);
+}
+
+// Accumulator register r of lane l in a 32x32 MFMA block holds row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32.
+KVATTN_DEV int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+}  // namespace kvattn

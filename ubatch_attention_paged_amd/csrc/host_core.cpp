@@ -425,12 +425,12 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
       int32_t c;
       if (budget > 0) {
         c = static_cast<int32_t>(P.classes.size());
-        P.classes.push_back(ClassInfo{kv.first, s, kv.second, 0, 0, 0, 1});
+        P.classes.push_back(ClassInfo{kv.first, s, kv.second, 0, 0, 0, 1, 0, 0});
         --budget;
       } else {
         if (merged < 0) {
           merged = static_cast<int32_t>(P.classes.size());
-          P.classes.push_back(ClassInfo{0, s, 0, 0, 0, 0, 0});
+          P.classes.push_back(ClassInfo{0, s, 0, 0, 0, 0, 0, 0, 0});
         }
         c = merged;
         P.classes[c].mask |= kv.first;
@@ -440,12 +440,16 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
     }
   }
   P.lookup_off[S] = static_cast<int32_t>(P.lookup.size());
-  int32_t off = 0;
+  int32_t off = 0, tiles = 0;
   for (auto& c : P.classes) {
     c.cell_off = off;
+    c.tile_base = tiles;
     off += c.n_cells;
+    tiles += ceil_div(c.n_cells, kTileCells);
+    P.max_class_tiles = std::max(P.max_class_tiles, ceil_div(c.n_cells, kTileCells));
   }
   P.total_cells = off;
+  P.total_tiles = tiles;
 
   // queries of each class, grouped by sequence then position
   std::vector<int32_t> qorder(NQ);

@@ -42,6 +42,8 @@ struct Plan {
   int32_t n_kv = 0;
   int32_t n_seg = 0;                  // counting segments per stream (n_kv / 64, rounded up)
   int32_t total_cells = 0;            // csr entries
+  int32_t total_tiles = 0;            // 64-cell tiles over all classes
+  int32_t max_class_tiles = 0;
   int32_t n_partial_rows = 0;
   std::vector<SlotInfo> slots;
   std::vector<ClassInfo> classes;

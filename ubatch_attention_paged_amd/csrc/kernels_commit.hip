@@ -1,0 +1,189 @@
+// gfx950 kernels of the store/commit half of the path:
+//
+//   k_store          K/V rows of a ubatch -> F16 (nearest-even) into their cells
+//   k_apply_updates  cell-table changes -> device mirror (pos, sequence set)
+//   k_csr_*          per-class lists of visible cells, ascending cell index
+//   k_tile_minmax    smallest / largest position of every 64-cell tile of a list
+//   k_mask_dense     dense F16 KQ mask (diagnostic form of the same predicate)
+//
+// Visibility ("llama.cpp and the ubatch", "The mask is doing the work"): a
+// cell is seen by a query when it is occupied, its sequence set holds the
+// query's first sequence id and, under causal attention, its position is
+// not later than the query's.  The class lists group cells by sequence set;
+// the attention kernels apply the position test per (query, cell).
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace kvattn {
+
+// fp32 rows -> F16 rows of the cache; each thread converts 8 consecutive
+// values (two 16 B loads, one 16 B store).
+__global__ __launch_bounds__(256) void k_store(StoreArgs a) {
+  const int il = blockIdx.y;
+  const int which = blockIdx.z;             // 0 = K, 1 = V
+  const int vec_per_row = a.E >> 3;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= static_cast<int64_t>(a.n_rows) * vec_per_row) return;
+  const int r = static_cast<int>(t / vec_per_row);
+  const int c = static_cast<int>(t % vec_per_row);
+  const float* src = (which ? a.v_cur[il] : a.k_cur[il]) + static_cast<int64_t>(r) * a.E + c * 8;
+  _Float16* dst = (which ? a.v[il] : a.k[il]) + static_cast<int64_t>(a.dst_rows[r]) * a.E + c * 8;
+  const float4 x0 = *reinterpret_cast<const float4*>(src);
+  const float4 x1 = *reinterpret_cast<const float4*>(src + 4);
+  half8 h;
+  h[0] = static_cast<_Float16>(x0.x); h[1] = static_cast<_Float16>(x0.y);
+  h[2] = static_cast<_Float16>(x0.z); h[3] = static_cast<_Float16>(x0.w);
+  h[4] = static_cast<_Float16>(x1.x); h[5] = static_cast<_Float16>(x1.y);
+  h[6] = static_cast<_Float16>(x1.z); h[7] = static_cast<_Float16>(x1.w);
+  *reinterpret_cast<half8*>(dst) = h;
+}
+
+hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(a.n_rows) * (a.E / 8);
+  if (n == 0 || n_il == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((n + 255) / 256), n_il, 2);
+  hipLaunchKernelGGL(k_store, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_apply_updates(CsrArgs a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.n_updates) return;
+  const CellUpdate u = a.updates[i];
+  a.cpos[u.idx] = u.pos;
+  a.cmask[u.idx] = u.mask;
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(int32_t* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Class of each cell j < n_kv of stream blockIdx.y, by binary search of its
+// sequence set among the ubatch's classes; per 64-cell segment counts.
+__global__ __launch_bounds__(256) void k_csr_classify(CsrArgs a) {
+  const int s = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  int cls = -1;
+  if (j < a.n_kv) {
+    const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
+    if (a.cpos[idx] >= 0) {
+      const uint64_t m = a.cmask[idx];
+      int lo = a.lookup_off[s], hi = a.lookup_off[s + 1] - 1;
+      while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const uint64_t mm = a.lookup[mid].mask;
+        if (mm == m) { cls = a.lookup[mid].cls; break; }
+        if (mm < m) lo = mid + 1; else hi = mid - 1;
+      }
+    }
+    a.cellcls[idx] = cls;
+  }
+  const int seg = j >> 6;
+  uint64_t active = ballot(cls >= 0);
+  while (active) {
+    const int leader = __builtin_ctzll(active);
+    const int c = readlane_i(cls, leader);
+    const uint64_t same = ballot(cls == c);
+    if (lane_id() == leader) a.counts[static_cast<int64_t>(c) * a.n_seg + seg] = __popcll(same);
+    active &= ~same;
+  }
+}
+
+// Per class: segment counts -> absolute start offsets in the csr arrays.
+__global__ __launch_bounds__(64) void k_csr_scan(CsrArgs a) {
+  const int c = blockIdx.x;
+  const int lane = threadIdx.x;
+  int32_t running = a.classes[c].cell_off;
+  int32_t* row = a.counts + static_cast<int64_t>(c) * a.n_seg;
+  for (int base = 0; base < a.n_seg; base += 64) {
+    const int k = base + lane;
+    const int v = k < a.n_seg ? row[k] : 0;
+    int incl = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (k < a.n_seg) row[k] = running + incl - v;
+    running += __shfl(incl, 63);
+  }
+}
+
+// Every classified cell goes to its class offset + its rank among the earlier
+// cells of its class in the segment: ascending cell index within a class.
+__global__ __launch_bounds__(256) void k_csr_scatter(CsrArgs a) {
+  const int s = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
+  const int cls = j < a.n_kv ? a.cellcls[idx] : -1;
+  const int seg = j >> 6;
+  uint64_t active = ballot(cls >= 0);
+  while (active) {
+    const int leader = __builtin_ctzll(active);
+    const int c = readlane_i(cls, leader);
+    const uint64_t same = ballot(cls == c);
+    if (cls == c) {
+      const int dst = a.counts[static_cast<int64_t>(c) * a.n_seg + seg] + __popcll(same & lanemask_lt());
+      if (dst < a.csr_cap) {
+        a.csr_cell[dst] = j;
+        a.csr_pos[dst] = a.cpos[idx];
+        a.csr_mask[dst] = a.cmask[idx];
+      }
+    }
+    active &= ~same;
+  }
+}
+
+// One wavefront per 64-cell tile of a class list: its position range.
+__global__ __launch_bounds__(256) void k_tile_minmax(CsrArgs a) {
+  const ClassInfo ci = a.classes[blockIdx.x];
+  const int nt = (ci.n_cells + kTileCells - 1) / kTileCells;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int k_end = min(nt, static_cast<int>(blockIdx.y) * 16 + 16);
+  for (int k = blockIdx.y * 16 + w; k < k_end; k += 4) {
+    const int j = k * kTileCells + lane;
+    const bool in = j < ci.n_cells;
+    const int p = in ? a.csr_pos[ci.cell_off + j] : INT32_MAX;
+    const int mn = wave_min_i(p);
+    const int mx = wave_max_i(in ? p : INT32_MIN);
+    if (lane == 0) {
+      a.tile_min[ci.tile_base + k] = mn;
+      a.tile_max[ci.tile_base + k] = mx;
+    }
+  }
+}
+
+hipError_t launch_commit(const CsrArgs& a, hipStream_t s) {
+  if (a.n_updates > 0)
+    hipLaunchKernelGGL(k_apply_updates, dim3((a.n_updates + 255) / 256), dim3(256), 0, s, a);
+  if (a.n_classes == 0) return hipGetLastError();
+  const int64_t nc = static_cast<int64_t>(a.n_classes) * a.n_seg;
+  hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, s, a.counts, nc);
+  const dim3 grid((a.n_kv + 255) / 256, a.n_stream);
+  hipLaunchKernelGGL(k_csr_classify, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_csr_scan, dim3(a.n_classes), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(k_csr_scatter, grid, dim3(256), 0, s, a);
+  if (a.max_class_tiles > 0)
+    hipLaunchKernelGGL(k_tile_minmax, dim3(a.n_classes, (a.max_class_tiles + 15) / 16), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// 0x0000 visible, 0xFC00 (-inf) hidden
+__global__ __launch_bounds__(256) void k_mask_dense(MaskArgs a) {
+  const int i = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= a.n_kv) return;
+  const SlotInfo q = a.slots[i];
+  const int64_t idx = static_cast<int64_t>(q.stream) * a.kv_size + j;
+  const int32_t p = a.cpos[idx];
+  const bool vis = p >= 0 && ((a.cmask[idx] >> q.seq0) & 1ULL) && (!a.causal || p <= q.pos);
+  a.mask[static_cast<int64_t>(i) * a.n_kv + j] = vis ? 0x0000 : 0xFC00;
+}
+
+hipError_t launch_mask(const MaskArgs& a, hipStream_t s) {
+  if (a.n_rows == 0 || a.n_kv == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_mask_dense, dim3((a.n_kv + 255) / 256, a.n_rows), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvattn

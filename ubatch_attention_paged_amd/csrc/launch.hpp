@@ -34,6 +34,9 @@ struct CsrArgs {
   const CellUpdate* updates;
   int32_t n_updates, n_classes, n_seg, kv_size, n_kv, n_stream;
   int32_t csr_cap;            // entries of csr_*: n_stream * kv_size
+  int32_t* tile_min;          // per 64-cell tile of each class: smallest / largest position
+  int32_t* tile_max;
+  int32_t max_class_tiles;
 };
 
 struct AttnArgs {
@@ -48,6 +51,8 @@ struct AttnArgs {
   const int32_t* csr_cell;
   const int32_t* csr_pos;
   const uint64_t* csr_mask;
+  const int32_t* tile_min;
+  const int32_t* tile_max;
   float* part_acc;            // [n_il][rows][n_head * head_dim]
   float* part_ml;             // [n_il][rows][n_head][2]  (max in log2 units, sum)
   const int32_t* red_slot;

@@ -18,6 +18,7 @@ constexpr int kMaxSeq = 64;            // sequence ids are bits of a uint64_t
 constexpr int kMaxLayersPerLaunch = 32;
 constexpr int kMaxClasses = 1024;      // per ubatch; extra sequence sets are merged
 constexpr int kSegCells = 64;          // cells per counting segment (one wavefront)
+constexpr int kTileCells = 64;         // cells per attention tile; chunk starts are multiples of it
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
 
 struct SlotInfo {        // one query slot
@@ -49,6 +50,8 @@ struct ClassInfo {
   int32_t q_off;         // first entry in qlist
   int32_t n_q;
   int32_t pure;          // 1: one sequence set, which every listed query belongs to
+  int32_t tile_base;     // first entry of this class in the per-64-cell tile tables
+  int32_t pad;
 };
 
 struct WorkItem {        // one workgroup (per KV head for the MFMA kernel)
