@@ -46,11 +46,21 @@ def gen_tensors(wl, b, layers, with_q, dev):
     jobs = [(l, k) for l in layers for k in kinds]
     with ThreadPoolExecutor(16) as ex:
         arrs = list(ex.map(lambda lk: wl.tensor(b, lk[0], lk[1]), jobs))
-    d = {jk: torch.from_numpy(a).to(dev, non_blocking=False) for jk, a in zip(jobs, arrs)}
-    K = [d[(l, W.KIND_K)] for l in layers]
-    V = [d[(l, W.KIND_V)] for l in layers]
-    Q = [d[(l, W.KIND_Q)] for l in layers] if with_q else None
+    d = dict(zip(jobs, arrs))
+    # one [layers][tokens][width] allocation per tensor kind: a ubatch's rows of
+    # every layer are then addressed by pointer arithmetic, no per-layer views
+    stack = lambda kind: torch.from_numpy(np.stack([d[(l, kind)] for l in layers])).to(dev)
+    K = stack(W.KIND_K)
+    V = stack(W.KIND_V)
+    Q = stack(W.KIND_Q) if with_q else None
     return K, V, Q
+
+
+def row_ptrs(t, l0, l1, row0):
+    """Addresses of row ``row0`` of layers l0..l1-1 of a [L][n][w] fp32 tensor."""
+    L, n, wdt = t.shape
+    base = t.data_ptr() + 4 * row0 * wdt
+    return [base + 4 * l * n * wdt for l in range(l0, l1)]
 
 
 def make_ctx(wl, dev):
@@ -72,26 +82,31 @@ class Runner:
         self.store_calls = 0
 
     def run_batch(self, n, pos, seqs, out_flags, K, V, Q, outs, timed):
+        """K, V, Q: [layers][n][width] fp32 device tensors in batch order;
+        outs: [layers][>= n_ubatch][n_head*head_dim]."""
         import torch
-        from ubatch_attention_paged_amd.harness import ubatch_rows
+        from ubatch_attention_paged_amd import kvattn_store, kvattn_attend
         ctx = self.ctx
         st, ubs, _ = ctx.split(n, pos, seqs, out_flags)
         if st != 0:
             raise RuntimeError("cache full")
-        L = len(K)
+        L = K.shape[0]
+        stream = torch.cuda.current_stream().cuda_stream
         for ub in ubs:
-            kr = [ubatch_rows(ub, x) for x in K]
-            vr = [ubatch_rows(ub, x) for x in V]
-            qr = [ubatch_rows(ub, x) for x in Q]
-            orow = [o[:ub.n_tokens] for o in outs]
+            src = ub.src
+            if ub.n_tokens and not (src[-1] - src[0] == ub.n_tokens - 1):
+                idx = torch.as_tensor(src, device=K.device, dtype=torch.long)
+                Kb, Vb, Qb, r0 = K.index_select(1, idx), V.index_select(1, idx), Q.index_select(1, idx), 0
+            else:
+                Kb, Vb, Qb, r0 = K, V, Q, int(src[0]) if ub.n_tokens else 0
             for a in range(0, L, self.chunk):
                 b = min(L, a + self.chunk)
-                ctx.store(ub, a, kr[a:b], vr[a:b])
+                kvattn_store(ctx.ctx, ub, a, row_ptrs(Kb, a, b, r0), row_ptrs(Vb, a, b, r0), stream)
                 if timed:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record()
-                ctx.attend(ub, a, qr[a:b], orow[a:b])
+                kvattn_attend(ctx.ctx, ub, a, row_ptrs(Qb, a, b, r0), row_ptrs(outs, a, b, 0), 0, stream)
                 if timed:
                     e1.record()
                     self.attend_ms.append((e0, e1))
@@ -122,7 +137,7 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
     data = [gen_tensors(wl, b, layers, True, dev) for b in range(len(wl.batches))]
     sids = [SeqIds(bt.seq_ids) for bt in wl.batches]
     HD = wl.n_head * wl.head_dim
-    outs = [torch.empty((wl.n_ubatch, HD), dtype=torch.float32, device=dev) for _ in layers]
+    outs = torch.empty((len(layers), wl.n_ubatch, HD), dtype=torch.float32, device=dev)
     runner = Runner(ctx, layer_chunk)
 
     def step(timed):
@@ -179,7 +194,7 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
         if bt.measured:
             continue
         K, V, _ = gen_tensors(wl, b, layers, False, dev)
-        st, _, _ = decode(ctx, bt.n_tokens, bt.pos, bt.seq_ids, bt.output, K, V)
+        st, _, _ = decode(ctx, bt.n_tokens, bt.pos, bt.seq_ids, bt.output, list(K), list(V))
         assert st == 0
         del K, V
     torch.cuda.synchronize()
@@ -190,7 +205,7 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
     from ubatch_attention_paged_amd import SeqIds
     sid = SeqIds(bt.seq_ids)
     HD = wl.n_head * wl.head_dim
-    outs = [torch.empty((bt.n_tokens, HD), dtype=torch.float32, device=dev) for _ in layers]
+    outs = torch.empty((len(layers), bt.n_tokens, HD), dtype=torch.float32, device=dev)
     runner = Runner(ctx, layer_chunk)
     t = 0
     for _ in range(warmup):

@@ -18,27 +18,42 @@
 //    32x32x16 steps of that block.  The matching A operand (V^T, 8 cells of
 //    one d per lane) comes from the row-major V tile through the LDS
 //    transpose read, in the same cell order.
+//  * The running maximum is only moved (and O rescaled) when a row's tile
+//    maximum exceeds it by more than 2^8, so most tiles skip the rescale; the
+//    F16 weights then stay below 256.  Row sums use v_dot2 on the same F16
+//    weights the PV product consumes.
 //  * Tiles entirely in the future of every query of the item are never
-//    loaded (per-tile position ranges from the commit step); tiles entirely
-//    visible skip the per-element mask.
+//    loaded and tiles entirely visible skip the per-element mask, both from
+//    per-tile position ranges built at commit.
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace kvattn {
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+
+KVATTN_DEV float dot2_sum(half2v h, float acc) {
+  const half2v one = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h), __builtin_bit_cast(fp16x2, one), acc, false);
+}
+
+constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag the true max
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   constexpr int QT = 128 / G;                     // queries per item
   constexpr int KT = kTileCells;                  // cells per tile (64)
   constexpr int DP = D < 32 ? 32 : D;             // O^T rows, padded to a 32-row block
-  constexpr int KS = D + 16;                      // halfs per LDS row: rows shift by 8 banks
+  constexpr int KSK = D + 8;                      // K row stride (halfs): rows shift 4 banks (16 B reads)
+  constexpr int KSV = D + 16;                     // V row stride: rows shift 8 banks (8 B transpose reads)
   constexpr int SEGS = D / 8;                     // 16 B segments per row
   constexpr int RPP = 256 / SEGS;                 // rows one pass of 256 threads loads
   constexpr int ROW_STEP = RPP >= KT ? KT : RPP;
   constexpr int NP = KT / ROW_STEP;               // passes per tile
-  static_assert(KS >= DP, "V rows must hold the padded columns");
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KT * KS];
-  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KT * KS];
+  static_assert(KSV >= DP, "V rows must hold the padded columns");
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KT * KSK];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KT * KSV];
   __shared__ int32_t kpos_s[2][KT];
   __shared__ uint64_t kmask_s[2][KT];
 
@@ -84,7 +99,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   if (D < DP) {   // columns D .. DP-1 of every V row are read as O^T rows >= D: keep them zero
     for (int i = tid; i < 2 * KT * (DP - D); i += 256) {
       const int b = i / (KT * (DP - D)), rem = i % (KT * (DP - D));
-      Vs[b][(rem / (DP - D)) * KS + D + rem % (DP - D)] = static_cast<_Float16>(0.f);
+      Vs[b][(rem / (DP - D)) * KSV + D + rem % (DP - D)] = static_cast<_Float16>(0.f);
     }
   }
 
@@ -147,6 +162,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
   const int s16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
+  const int qpos = si.pos, qseq = si.seq0;
   for (int i = 0; i < ntile; ++i) {
     const int buf = i & 1;
     // stage tile i
@@ -154,8 +170,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int rr = row0 + p * ROW_STEP;
-        *reinterpret_cast<uint4*>(&Ks[buf][rr * KS + seg * 8]) = kreg[p];
-        *reinterpret_cast<uint4*>(&Vs[buf][rr * KS + seg * 8]) = vreg[p];
+        *reinterpret_cast<uint4*>(&Ks[buf][rr * KSK + seg * 8]) = kreg[p];
+        *reinterpret_cast<uint4*>(&Vs[buf][rr * KSV + seg * 8]) = vreg[p];
       }
     }
     if (tid < KT) {
@@ -171,11 +187,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     }
 
     const int nk = min(KT, it.c1 - (it.c0 + i * KT));
-    const int pl = kpos_s[buf][lane];
-    const int kmin = wave_min_i(pl);
-    const int kmax = wave_max_i(lane < nk ? pl : INT32_MIN);
-    if (a.causal && kmin > it.qpos_max) continue;
-    const bool full = nk == KT && pure && (!a.causal || kmax <= it.qpos_min);
+    const int tmin = a.tile_min[tb + i], tmax = a.tile_max[tb + i];
+    if (a.causal && tmin > it.qpos_max) continue;
+    const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min);
 
     floatx16 sacc[2];
 #pragma unroll
@@ -185,19 +199,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const half8 ka =
-            *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + (lane & 31)) * KS + 16 * ks + 8 * half_id]);
+            *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + (lane & 31)) * KSK + 16 * ks + 8 * half_id]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], sacc[kb], 0, 0, 0);
       }
     }
     if (!full) {
+      // cells past the list end hold position INT32_MAX, so the causal test
+      // also removes them
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb * 32 + acc_row(e, lane);
-          bool vis = key < nk && (!a.causal || kpos_s[buf][key] <= si.pos);
-          if (!pure) vis = vis && ((kmask_s[buf][key] >> si.seq0) & 1ULL);
-          if (!vis) sacc[kb][e] = -INFINITY;
+          bool vis = a.causal ? (kpos_s[buf][key] <= qpos) : (key < nk);
+          if (!pure) vis = vis & static_cast<bool>((kmask_s[buf][key] >> qseq) & 1ULL);
+          sacc[kb][e] = vis ? sacc[kb][e] : -INFINITY;
         }
     }
     // online softmax over this lane's row (the other half-wave holds the rest)
@@ -207,27 +223,33 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    const bool grow = mx > m_run + kRescaleSlack;     // false while the row sees nothing
+    if (ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float rs = 0.f;
     half8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        // the row sum uses the same F16-rounded weights the PV product sees
-        const _Float16 ph = static_cast<_Float16>(exp2f(sacc[kb][e] - m_use));
-        rs += static_cast<float>(ph);
-        pb[kb][e >> 3][e & 7] = ph;
+      for (int e = 0; e < 16; e += 2) {
+        half2v ph;
+        ph[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[kb][e] - m_use));
+        ph[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[kb][e + 1] - m_use));
+        rs = dot2_sum(ph, rs);          // the row sum sees the F16 weights the PV product sees
+        pb[kb][e >> 3][e & 7] = ph[0];
+        pb[kb][e >> 3][(e & 7) + 1] = ph[1];
       }
     rs += __shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DP / 32; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    l_run += rs;
     // O^T += V^T P^T: source lane s of each 16-lane group points at cell row
     // key0 + s/4, column dsub + 4*(s%4); lane gets cells key0..key0+3 of column
     // db*32 + lane%32 (and key0+8.. for the upper four k-values)
@@ -236,14 +258,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int key0 = kb * 32 + 16 * st + 4 * half_id;
-        const _Float16* vb = &Vs[buf][(key0 + (s16 >> 2)) * KS + 4 * (s16 & 3) + dsub];
+        const _Float16* vb = &Vs[buf][(key0 + (s16 >> 2)) * KSV + 4 * (s16 & 3) + dsub];
 #pragma unroll
         for (int db = 0; db < DP / 32; ++db) {
           const half4 lo = lds_read_tr16(vb + db * 32);
-          const half4 hi = lds_read_tr16(vb + db * 32 + 8 * KS);
-          half8 va;
-          va[0] = lo[0]; va[1] = lo[1]; va[2] = lo[2]; va[3] = lo[3];
-          va[4] = hi[0]; va[5] = hi[1]; va[6] = hi[2]; va[7] = hi[3];
+          const half4 hi = lds_read_tr16(vb + db * 32 + 8 * KSV);
+          const half8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kb][st], oacc[db], 0, 0, 0);
         }
       }
