@@ -118,6 +118,11 @@ class Runner:
         vals = [a.elapsed_time(b) for a, b in self.attend_ms]
         return float(np.mean(vals)) if vals else float("nan"), len(vals)
 
+    def attend_by_position(self, per_step):
+        """Mean attend time of the k-th attend call of a step, k < per_step."""
+        vals = np.array([a.elapsed_time(b) for a, b in self.attend_ms]).reshape(-1, per_step)
+        return vals.mean(axis=0).tolist()
+
 
 # ---------------------------------------------------------------------------
 # prefill (headline)
@@ -159,6 +164,16 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
     pairs = prefill_pairs(wl)
     flops_step = 4.0 * wl.n_head * wl.head_dim * wl.n_layer * pairs
     n_ub_step = n_launch / steps
+    per_ub = runner.attend_by_position(int(round(n_launch / steps)))
+    # flops of each ubatch (split_simple over the caller calls, positions in order)
+    ub_flops = []
+    for bt in wl.batches:
+        for a0 in range(0, bt.n_tokens, wl.n_ubatch):
+            p = bt.pos[a0:a0 + wl.n_ubatch].astype(np.int64)
+            ub_flops.append(4.0 * wl.n_head * wl.head_dim * wl.n_layer * float((p + 1).sum()))
+    if len(ub_flops) == len(per_ub) and layer_chunk >= wl.n_layer:
+        log("[bench] prefill per ubatch: " + ", ".join(
+            f"{ms:.3f} ms {f / (ms * 1e-3) / 1e12:.0f} TF/s" for ms, f in zip(per_ub, ub_flops)))
     res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens=wl.measured_tokens(),
                flops_step=flops_step, attend_launches_per_step=n_ub_step, attend_avg_ms=avg_ms,
                attend_ms_per_step=avg_ms * n_ub_step, last_plan=stats)
@@ -273,6 +288,24 @@ def cpu_baseline(wl, budget_s=25.0):
                        f"{wl.n_layer / done_layers:.1f}")
 
 
+def committed_traffic(kernel, source):
+    """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE /
+    WRITE_SIZE summary, scaled by the copy-kernel calibration recorded there;
+    None when no summary exists or the kernel source changed since it was
+    taken (the summary stores the source's sha256)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    src = os.path.join(ROOT, "ubatch_attention_paged_amd", "csrc", source)
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return round(rec["bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +316,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--per-layer", action="store_true", help="also time one call per layer")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode workloads (for profiling their kernels alone)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is not sharded "
@@ -294,6 +329,13 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.decode_only:
+        dec = {name: bench_decode(w, dev, args.steps, args.warmup, args.layer_chunk)
+               for name, w in (("cb_decode", W.cb_decode()), ("prefix_decode", W.prefix_decode()))}
+        print(json.dumps({"decode_only": {k: {"tokens_per_s": v["tokens_per_s"], "kv_read_gbs": v["kv_read_gbs"],
+                                              "hbm_frac": v["hbm_frac"], "attend_avg_ms": v["attend_avg_ms"]}
+                                          for k, v in dec.items()}}), flush=True)
+        return
     wl = W.qwen_prefill()
     pre = bench_prefill(wl, dev, args.steps, args.warmup, args.layer_chunk)
     tok_s = pre["tokens"] * args.steps / pre["wall_s"]
@@ -321,7 +363,8 @@ def main():
                    "layers_per_call": args.layer_chunk, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "k_attn_mfma",
                      "achieved": round(mfma_tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(mfma_tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(mfma_tf / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": committed_traffic("k_attn_mfma", "attn_mfma.hip"),
                      "per_launch": f"{pre['flops_step'] / pre['attend_launches_per_step'] / 1e9:.2f} GFLOP "
                                    f"(4*H*d per visible (query, cell) pair x 28 layers of one ubatch), "
                                    f"avg {pre['attend_avg_ms']:.3f} ms"},

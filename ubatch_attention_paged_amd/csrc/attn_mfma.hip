@@ -42,7 +42,8 @@ constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag the
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
-  constexpr int QT = 128 / G;                     // queries per item
+  constexpr int QT = kMfmaRowsPerItem / G;        // queries per item (128 rows)
+  static_assert(kMfmaRowsPerItem == 128, "4 wavefronts x 32 rows");
   constexpr int KT = kTileCells;                  // cells per tile (64)
   constexpr int DP = D < 32 ? 32 : D;             // O^T rows, padded to a 32-row block
   constexpr int KSK = D + 8;                      // K row stride (halfs): rows shift 4 banks (16 B reads)

@@ -470,7 +470,7 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   // work items
   const int D = g_.head_dim, G = g_.G();
   const bool valu_ok = g_.E() == 1024 && (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4);
-  const int32_t QT = 128 / G;
+  const int32_t QT = kMfmaRowsPerItem / G;   // query rows of one matrix-core workgroup
   int64_t valu_cells = 0;
   for (const auto& c : P.classes)
     if (valu_ok && c.n_q <= kValuMaxQueries) valu_cells += static_cast<int64_t>(c.n_q) * c.n_cells;

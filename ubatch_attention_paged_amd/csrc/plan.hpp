@@ -20,6 +20,7 @@ constexpr int kMaxClasses = 1024;      // per ubatch; extra sequence sets are me
 constexpr int kSegCells = 64;          // cells per counting segment (one wavefront)
 constexpr int kTileCells = 64;         // cells per attention tile; chunk starts are multiples of it
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
+constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV head) per MFMA item
 
 struct SlotInfo {        // one query slot
   int32_t stream;
