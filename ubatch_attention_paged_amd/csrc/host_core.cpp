@@ -474,7 +474,9 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   int64_t valu_cells = 0;
   for (const auto& c : P.classes)
     if (valu_ok && c.n_q <= kValuMaxQueries) valu_cells += static_cast<int64_t>(c.n_q) * c.n_cells;
-  int32_t chv = 64;
+  // at least 256 cells per vector-ALU item: its fixed costs (q, merge of the
+  // four wavefronts, the partial row) stay small next to 1 MiB of K/V rows
+  int32_t chv = 256;
   while (chv < 8192 && valu_cells > static_cast<int64_t>(chv) * valu_target_items) chv *= 2;
   int32_t chm_lowreuse = 256;
 

@@ -82,7 +82,7 @@ class HostCore {
 
   // limits used by the planner (bounded by the workspace)
   int32_t prow_max = 4096;            // split-K partial rows
-  int32_t valu_target_items = 1024;   // vector-ALU items aimed for per layer
+  int32_t valu_target_items = 256;    // vector-ALU items aimed for per layer
 
  private:
   struct Stream {
