@@ -63,11 +63,11 @@ def row_ptrs(t, l0, l1, row0):
     return [base + 4 * l * n * wdt for l in range(l0, l1)]
 
 
-def make_ctx(wl, dev):
+def make_ctx(wl, dev, layer_chunk):
     from ubatch_attention_paged_amd import Context
     return Context(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
                    wl.n_seq_max, wl.n_batch, wl.n_ubatch, wl.causal, cell_order=wl.cell_order,
-                   device=dev)
+                   device=dev, attend_layers=layer_chunk)
 
 
 class Runner:
@@ -135,7 +135,7 @@ def prefill_pairs(wl):
 
 def bench_prefill(wl, dev, steps, warmup, layer_chunk):
     import torch
-    ctx = make_ctx(wl, dev)
+    ctx = make_ctx(wl, dev, layer_chunk)
     layers = list(range(wl.n_layer))
     log(f"[bench] prefill: generating inputs ({wl.note})")
     from ubatch_attention_paged_amd import SeqIds
@@ -201,7 +201,7 @@ def decode_step_cells(wl, t):
 def bench_decode(wl, dev, steps, warmup, layer_chunk):
     import torch
     from ubatch_attention_paged_amd.harness import decode
-    ctx = make_ctx(wl, dev)
+    ctx = make_ctx(wl, dev, layer_chunk)
     layers = list(range(wl.n_layer))
     log(f"[bench] decode {wl.name}: filling the context ({wl.note})")
     t0 = time.perf_counter()

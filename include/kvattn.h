@@ -83,6 +83,8 @@ typedef struct kvattn_params {
   void *workspace;        /* device, >= kvattn_workspace_bytes(); NULL with k_layers NULL */
   size_t workspace_bytes;
   int32_t device;         /* HIP device ordinal of every device pointer */
+  int32_t attend_layers;  /* scheduling hint, no effect on results: layers per kvattn_attend
+                             call the caller will use (0 = 1); sizes the work items */
 } kvattn_params;
 
 /* A batch as submitted: llama_batch without token/embd ("Batch、Ubatch 与解码主循环",

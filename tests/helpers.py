@@ -51,23 +51,26 @@ def oracle_run(wl, layers, measured_only=True, keep_masks=False, n_ubatch=None):
     return eng, res, masks, ubmeta
 
 
-def make_ctx(wl, device="cuda:0", n_ubatch=None):
+def make_ctx(wl, device="cuda:0", n_ubatch=None, attend_layers=0):
     from ubatch_attention_paged_amd import Context
     # every layer of the workload gets a cache; tests may run a subset
     return Context(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream, wl.n_seq_max,
                    wl.n_batch, wl.n_ubatch if n_ubatch is None else n_ubatch, wl.causal,
-                   cell_order=wl.cell_order, device=device)
+                   cell_order=wl.cell_order, device=device, attend_layers=attend_layers)
 
 
-def gpu_run(wl, layers, layer_chunk=None, only_outputs=False, on_ubatch=None, ctx=None, n_ubatch=None):
+def gpu_run(wl, layers, layer_chunk=None, only_outputs=False, on_ubatch=None, ctx=None, n_ubatch=None,
+            keep_layers=None):
     """Returns (ctx, results) with results[(b, l)] float64 numpy in batch
-    order.  on_ubatch(ctx, b, ub) runs after each ubatch is stored."""
+    order (only for keep_layers when given).  on_ubatch(ctx, b, ub) runs
+    after each ubatch is stored."""
     import torch
     from ubatch_attention_paged_amd.harness import ubatch_rows
     dev = torch.device("cuda:0")
-    ctx = ctx or make_ctx(wl, n_ubatch=n_ubatch)
-    res = {}
     chunk = len(layers) if layer_chunk is None else layer_chunk
+    ctx = ctx or make_ctx(wl, n_ubatch=n_ubatch, attend_layers=chunk)
+    res = {}
+    keep = set(layers if keep_layers is None else keep_layers)
     assert layers == list(range(layers[0], layers[0] + len(layers)))
     HD = wl.n_head * wl.head_dim
     for b, bt in enumerate(wl.batches):
@@ -99,7 +102,9 @@ def gpu_run(wl, layers, layer_chunk=None, only_outputs=False, on_ubatch=None, ct
         if bt.measured:
             torch.cuda.synchronize()
             for i, l in enumerate(layers):
-                res[(b, l)] = outs[i].double().cpu().numpy()
+                if l in keep:
+                    res[(b, l)] = outs[i].double().cpu().numpy()
+        del K, V, Q, outs
     torch.cuda.synchronize()
     return ctx, res
 

@@ -1,0 +1,91 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times: every layer of the 28-layer cache stored and attended in one
+call per ubatch (layer_chunk = attend_layers = 28).  The oracle computes a
+sample of layers (first, middle, last) completely; for those layers every
+output element of every measured ubatch is compared, and the cells, the dense
+mask and the cache bytes must match bit for bit.
+
+The decode workload additionally runs extra decode steps (the benchmark's
+steps append one token per sequence at the next position).
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from synthetic import workloads as W
+from tests.helpers import assert_parity, gpu_run, oracle_run
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(300)]
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+K = pytest.importorskip("ubatch_attention_paged_amd")
+
+# layers the oracle computes; the mixed workload's oracle costs ~35 s per
+# layer (512 queries against 32768 cells of 8 streams, in fp64), so it keeps
+# only the last layer, whose cache and row addresses are the furthest offset
+KEEP = {"qwen_prefill": [0, 13, 27], "cb_decode": [0, 13, 27], "prefix_decode": [0, 13, 27], "mixed": [27]}
+
+
+def with_decode_steps(wl, extra):
+    """The workload followed by ``extra`` more decode calls, each one token per
+    sequence at the next position (the benchmark's decode steps)."""
+    last = wl.batches[-1]
+    more = [dataclasses.replace(last, pos=last.pos + t) for t in range(1, extra + 1)]
+    return dataclasses.replace(wl, batches=list(wl.batches) + more)
+
+
+def full(name):
+    if name == "qwen_prefill":
+        return W.qwen_prefill()
+    if name == "cb_decode":
+        return with_decode_steps(W.cb_decode(), 2)
+    if name == "prefix_decode":
+        return with_decode_steps(W.prefix_decode(), 1)
+    if name == "mixed":
+        return W.mixed()
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["qwen_prefill", "cb_decode", "prefix_decode", "mixed"])
+def test_full_size_sampled_layers(name):
+    wl = full(name)
+    assert wl.n_layer == 28
+    layers = list(range(wl.n_layer))
+    keep = KEEP[name]
+    print(f"[gpu] full size {name}: {wl.note}; oracle layers {keep}", flush=True)
+    eng, ref, _, meta = oracle_run(wl, keep, measured_only=True)
+    print(f"[gpu] full size {name}: oracle done ({len(ref)} outputs)", flush=True)
+    ub_index = {b: 0 for b in range(len(wl.batches))}
+    seen = {"cells": 0, "mask": 0}
+
+    def check(ctx, b, ub):
+        u = ub_index[b]
+        r = meta[(b, u)]
+        assert ub.cells.tolist() == r.cells, f"cells differ (batch {b}, ubatch {u})"
+        seen["cells"] += 1
+        if wl.batches[b].measured:
+            m = ctx.mask(ub).cpu().numpy().view(np.uint16)
+            assert np.array_equal(m, r.mask.view(np.uint16)), f"mask differs (batch {b}, ubatch {u})"
+            seen["mask"] += 1
+        ub_index[b] += 1
+
+    ctx, got = gpu_run(wl, layers, on_ubatch=check, keep_layers=keep)
+    print(f"[gpu] full size {name}: gpu done", flush=True)
+    assert seen["cells"] == len(meta) and seen["mask"] > 0
+    assert set(got) == set(ref)
+    worst = 0.0
+    for key in sorted(ref):
+        ma, _ = assert_parity(got[key], ref[key], tag=f"{name} batch {key[0]} layer {key[1]}")
+        worst = max(worst, ma)
+    bound = 2e-5 if name == "cb_decode" else 1.6e-3
+    assert worst < bound, worst
+    occ = eng.cells.pos >= 0
+    for l in keep:
+        assert np.array_equal(ctx.K[l].cpu().numpy().view(np.uint16)[occ], eng.K[l][occ].view(np.uint16))
+        assert np.array_equal(ctx.V[l].cpu().numpy().view(np.uint16)[occ], eng.V[l][occ].view(np.uint16))
+    print(f"[gpu] full size {name}: max abs err {worst:.2e}", flush=True)
+    ctx.close()

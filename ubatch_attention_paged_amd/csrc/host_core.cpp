@@ -57,6 +57,7 @@ int make_geometry(const kvattn_params& p, Geometry& g, std::string& err) {
   g.n_batch = g.causal ? std::min(n_ctx, nb_in) : nb_in;
   g.n_ubatch = std::min(g.n_batch, p.n_ubatch == 0 ? nb_in : p.n_ubatch);
   g.kq_scale = p.kq_scale != 0.f ? p.kq_scale : 1.0f / std::sqrt(static_cast<float>(p.head_dim));
+  g.attend_layers = std::max(1, std::min(p.attend_layers, p.n_layer));
   return KVATTN_OK;
 }
 
@@ -471,14 +472,27 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   const int D = g_.head_dim, G = g_.G();
   const bool valu_ok = g_.E() == 1024 && (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4);
   const int32_t QT = kMfmaRowsPerItem / G;   // query rows of one matrix-core workgroup
-  int64_t valu_cells = 0;
-  for (const auto& c : P.classes)
+  // Item sizing.  One attend call launches (items x layers per call)
+  // workgroups; aim for about kTargetWorkgroups of them so every CU gets
+  // several and the last round is short, with at least 256 cells per item
+  // (an item's fixed costs -- q, the merge, a partial row -- stay small).
+  int64_t valu_cells = 0, lowreuse_cells = 0;
+  for (const auto& c : P.classes) {
     if (valu_ok && c.n_q <= kValuMaxQueries) valu_cells += static_cast<int64_t>(c.n_q) * c.n_cells;
-  // at least 256 cells per vector-ALU item: its fixed costs (q, merge of the
-  // four wavefronts, the partial row) stay small next to 1 MiB of K/V rows
-  int32_t chv = 256;
-  while (chv < 8192 && valu_cells > static_cast<int64_t>(chv) * valu_target_items) chv *= 2;
-  int32_t chm_lowreuse = 256;
+    else if (c.n_q * G <= 64) lowreuse_cells += static_cast<int64_t>(ceil_div(c.n_q, QT)) * c.n_cells;
+  }
+  const int64_t target_items = std::max<int64_t>(64, kTargetWorkgroups / std::max(1, g_.attend_layers));
+  auto pow2_floor = [](int64_t x, int32_t lo, int32_t hi) {
+    int32_t v = lo;
+    while (v < hi && 2 * static_cast<int64_t>(v) <= x) v *= 2;
+    return v;
+  };
+  // vector-ALU items: the chunk bounds the cells per item; a class's cells
+  // are then cut into equal parts (no near-empty remainder item)
+  int32_t chv = pow2_floor(valu_cells / target_items, 256, 8192);
+  // matrix-core items with few query rows are bandwidth-bound too: split
+  // their cells (in multiples of the 64-cell tile) across KV heads x chunks
+  int32_t chm_lowreuse = pow2_floor(lowreuse_cells * g_.n_head_kv / target_items, 256, 4096);
 
   for (int attempt = 0; attempt < 16; ++attempt) {
     P.items_valu.clear();
@@ -492,10 +506,12 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
       if (c.n_q == 0 || c.n_cells == 0) continue;
       const bool valu = valu_ok && c.n_q <= kValuMaxQueries;
       if (valu) {
+        const int32_t parts = ceil_div(c.n_cells, chv);
+        const int32_t len = ceil_div(c.n_cells, parts);
         for (int32_t t = 0; t < c.n_q; ++t) {
           const int32_t q = P.qlist[c.q_off + t];
-          for (int32_t a = 0; a < c.n_cells; a += chv) {
-            WorkItem it{ci, c.q_off + t, 1, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + chv), -1,
+          for (int32_t a = 0; a < c.n_cells; a += len) {
+            WorkItem it{ci, c.q_off + t, 1, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + len), -1,
                         P.slots[q].pos, P.slots[q].pos};
             pend.push_back({it, true});
             ++coverage[q];

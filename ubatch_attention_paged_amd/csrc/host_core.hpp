@@ -19,6 +19,7 @@ struct Geometry {
   int32_t n_batch = 0, n_ubatch = 0;    // clamped
   int32_t causal = 1;
   float kq_scale = 0.f;
+  int32_t attend_layers = 1;            // layers per attend call (work-item sizing hint)
   int32_t E() const { return n_head_kv * head_dim; }
   int32_t G() const { return n_head / n_head_kv; }
 };
@@ -82,7 +83,6 @@ class HostCore {
 
   // limits used by the planner (bounded by the workspace)
   int32_t prow_max = 4096;            // split-K partial rows
-  int32_t valu_target_items = 256;    // vector-ALU items aimed for per layer
 
  private:
   struct Stream {

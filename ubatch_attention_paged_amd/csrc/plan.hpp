@@ -21,6 +21,7 @@ constexpr int kSegCells = 64;          // cells per counting segment (one wavefr
 constexpr int kTileCells = 64;         // cells per attention tile; chunk starts are multiples of it
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
 constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV head) per MFMA item
+constexpr int kTargetWorkgroups = 3072; // attention workgroups aimed for per launch (256 CUs)
 
 struct SlotInfo {        // one query slot
   int32_t stream;
