@@ -318,6 +318,8 @@ def main():
     ap.add_argument("--per-layer", action="store_true", help="also time one call per layer")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode workloads (for profiling their kernels alone)")
+    ap.add_argument("--decode-workload", choices=["cb_decode", "prefix_decode"], action="append",
+                    help="restrict the decode runs to this workload (repeatable)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is not sharded "
@@ -329,9 +331,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    decode_names = args.decode_workload or ["cb_decode", "prefix_decode"]
+    decode_wls = [(name, W.by_name(name)) for name in decode_names]
     if args.decode_only:
-        dec = {name: bench_decode(w, dev, args.steps, args.warmup, args.layer_chunk)
-               for name, w in (("cb_decode", W.cb_decode()), ("prefix_decode", W.prefix_decode()))}
+        dec = {name: bench_decode(w, dev, args.steps, args.warmup, args.layer_chunk) for name, w in decode_wls}
         print(json.dumps({"decode_only": {k: {"tokens_per_s": v["tokens_per_s"], "kv_read_gbs": v["kv_read_gbs"],
                                               "hbm_frac": v["hbm_frac"], "attend_avg_ms": v["attend_avg_ms"]}
                                           for k, v in dec.items()}}), flush=True)
@@ -376,7 +379,7 @@ def main():
                                    "attend_avg_ms": round(pl["attend_avg_ms"], 4)}
     if not args.no_decode:
         dec = {}
-        for name, w in (("cb_decode", W.cb_decode()), ("prefix_decode", W.prefix_decode())):
+        for name, w in decode_wls:
             r = bench_decode(w, dev, args.steps, args.warmup, args.layer_chunk)
             log(f"[bench] {name}: {r['tokens_per_s']:,.0f} tok/s, attend {r['attend_avg_ms']:.3f} ms, "
                 f"{r['kv_read_gbs']:.0f} GB/s ({100 * r['hbm_frac']:.1f}% of HBM)")

@@ -161,7 +161,7 @@ int kvattn_store(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t 
  * [n_tokens][n_head*head_dim], out fp32 [n_tokens][n_head*head_dim] in
  * ubatch slot order -- or, with only_outputs, [n_outputs][...] holding the
  * flagged slots in slot order.  A slot with no visible cell yields zeros.
- * Repeatable. */
+ * Repeatable.  Asynchronous on hip_stream. */
 int kvattn_attend(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t n_il,
                   const void *const *q, void *const *out, int32_t only_outputs, void *hip_stream);
 

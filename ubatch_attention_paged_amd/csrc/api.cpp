@@ -444,12 +444,14 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
       a.k[i] = static_cast<const _Float16*>(c->K[il0 + l0 + i]);
       a.v[i] = static_cast<const _Float16*>(c->V[il0 + l0 + i]);
     }
-    a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
-    a.n_items = static_cast<int32_t>(P.items_valu.size());
-    HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s));
+    // matrix-core items first: their workgroups need most of a CU's LDS and
+    // would otherwise wait for vector-ALU workgroups to drain
     a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_mfma);
     a.n_items = static_cast<int32_t>(P.items_mfma.size());
     HIP_TRY(c, launch_attn_mfma(a, n, g.head_dim, g.G(), s));
+    a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
+    a.n_items = static_cast<int32_t>(P.items_valu.size());
+    HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s));
     HIP_TRY(c, launch_reduce(a, static_cast<int32_t>(P.red_slot.size()), n, g.head_dim, s));
   }
   return KVATTN_OK;

@@ -8,9 +8,12 @@
 // wherever the cell sits in the cache.  Scores are reduced over the LPH lanes
 // of a head with DPP lane moves; the softmax runs online in base 2 with the
 // scale folded into q (fp32 throughout; the F16 rows are widened inside
-// v_fma_mix).  The cell indices, positions and sequence sets of the next
-// group of cells are fetched while the current group computes, and the
-// running maximum moves (rescaling O) only when it grows by more than 2^8.
+// v_fma_mix).  Each wavefront keeps the K/V rows of its next group of cells
+// and the list entries of the group after that in flight while it computes
+// the current group, and the running maximum moves (rescaling O) only when
+// it grows by more than 2^8.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -47,8 +50,11 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   static_assert(LPH == 4 || LPH == 8, "head_dim 64 or 128");
   __shared__ float red[3][64][G * 18];
 
-  const WorkItem it = a.items[blockIdx.x];
-  const int il = blockIdx.y;
+  // item-major, layer-minor: the items are sorted longest first, so the
+  // shortest (item, layer) pairs of the whole launch are dispatched last
+  const int n_il = gridDim.x / a.n_items;
+  const WorkItem it = a.items[blockIdx.x / n_il];
+  const int il = blockIdx.x % n_il;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int kvh = lane / LPH, part = lane % LPH;
   const int qslot = a.qlist[it.q_off];
@@ -78,39 +84,36 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   }
   const int64_t sbase = static_cast<int64_t>(si.stream) * a.kv_size;
   const int last = it.c1 - 1;
+  constexpr int STEP = 4 * U;          // cells the workgroup covers per step
 
-  // list entries of the first step
-  int ncell[U], npos[U];
-  uint64_t nmask[U];
-  const int c_first = it.c0 + w * U;
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int idx = min(c_first + u, last);
-    ncell[u] = a.csr_cell[idx];
-    npos[u] = a.csr_pos[idx];
-    nmask[u] = check_mask ? a.csr_mask[idx] : ~0ULL;
-  }
-
-  for (int c = c_first; c < it.c1; c += 4 * U) {
-    half8 kr[U][2], vr[U][2];
-    bool vis[U];
+  // Software pipeline over this wavefront's steps (U cells each): while
+  // step s computes, the K/V rows of step s+1 and the list entries (cell,
+  // position, sequence set) of step s+2 are in flight.  Two register sets
+  // A/B alternate; visibility is decided when a step's rows are issued, so
+  // its list entries are dead by then.
+  int lc[U], lp[U];
+  uint64_t lm[U];
+  auto fetch_list = [&](int c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t off = (sbase + ncell[u]) * E + kvh * D + part * 16;
+      const int idx = min(c + u, last);
+      lc[u] = a.csr_cell[idx];
+      lp[u] = a.csr_pos[idx];
+      lm[u] = check_mask ? a.csr_mask[idx] : ~0ULL;
+    }
+  };
+  auto issue = [&](int c, half8 (&kr)[U][2], half8 (&vr)[U][2], bool (&vis)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = (sbase + lc[u]) * E + kvh * D + part * 16;
       const half8* kp = reinterpret_cast<const half8*>(Kl + off);
       const half8* vp = reinterpret_cast<const half8*>(Vl + off);
       kr[u][0] = kp[0]; kr[u][1] = kp[1];
       vr[u][0] = vp[0]; vr[u][1] = vp[1];
-      vis[u] = c + u < it.c1 && (!a.causal || npos[u] <= si.pos) && ((nmask[u] >> si.seq0) & 1ULL);
+      vis[u] = c + u < it.c1 && (!a.causal || lp[u] <= si.pos) && ((lm[u] >> si.seq0) & 1ULL);
     }
-    // list entries of the next step fly while this one computes
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = min(c + 4 * U + u, last);
-      ncell[u] = a.csr_cell[idx];
-      npos[u] = a.csr_pos[idx];
-      nmask[u] = check_mask ? a.csr_mask[idx] : ~0ULL;
-    }
+  };
+  auto compute = [&](const half8 (&kr)[U][2], const half8 (&vr)[U][2], const bool (&vis)[U]) {
     float sc[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -152,6 +155,31 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
         for (int u = 0; u < U; ++u) v += p[u] * static_cast<float>(vr[u][e >> 3][e & 7]);
         acc[g][e] = v;
       }
+    }
+  };
+
+  half8 kA[U][2], vA[U][2], kB[U][2], vB[U][2];
+  bool visA[U], visB[U];
+  const int c_first = it.c0 + w * U;   // wave-uniform, as is every step bound below
+  if (c_first < it.c1) {
+    fetch_list(c_first);
+    issue(c_first, kA, vA, visA);
+    fetch_list(c_first + STEP);
+    for (int c = c_first;; c += 2 * STEP) {
+      const bool more1 = c + STEP < it.c1;
+      if (more1) {
+        issue(c + STEP, kB, vB, visB);
+        fetch_list(c + 2 * STEP);
+      }
+      compute(kA, vA, visA);
+      if (!more1) break;
+      const bool more2 = c + 2 * STEP < it.c1;
+      if (more2) {
+        issue(c + 2 * STEP, kA, vA, visA);
+        fetch_list(c + 3 * STEP);
+      }
+      compute(kB, vB, visB);
+      if (!more2) break;
     }
   }
 
@@ -207,7 +235,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
 
 template <int D, int G>
 static void valu_launch(const AttnArgs& a, int n_il, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn_valu<D, G>), dim3(a.n_items, n_il), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_attn_valu<D, G>), dim3(a.n_items * n_il), dim3(256), 0, s, a);
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int D, int G, hipStream_t s) {
@@ -222,9 +250,12 @@ hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int D, int G, hipStream
   return hipGetLastError();
 }
 
-// split-K merge, one pass: the running (M, L, O) absorbs record k as
-// M' = max(M, m_k), O' = 2^(M-M') O + 2^(m_k-M') acc_k, L' likewise.
-__global__ __launch_bounds__(256) void k_attn_reduce(AttnArgs a, int D) {
+// split-K merge.  Record k of a query holds (m_k, l_k, acc_k) for each head;
+// the merged row is sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k with
+// M = max_k m_k.  Two passes over the records (the maximum, then the sums),
+// each with independent loads, so a query's records are fetched in parallel
+// rather than as a chain.  One thread per 4 consecutive output numbers.
+__global__ __launch_bounds__(1024) void k_attn_reduce(AttnArgs a, int D) {
   const int rr = blockIdx.x, il = blockIdx.y;
   const int H = a.n_head;
   const SlotInfo si = a.slots[a.red_slot[rr]];
@@ -232,20 +263,21 @@ __global__ __launch_bounds__(256) void k_attn_reduce(AttnArgs a, int D) {
   const int64_t lbase = static_cast<int64_t>(il) * a.rows_per_layer;
   for (int x = threadIdx.x * 4; x < H * D; x += blockDim.x * 4) {
     const int h = x / D;
-    float M = -INFINITY, L = 0.f;
+    float M = -INFINITY;
+#pragma unroll 4
+    for (int k = b; k < e; ++k) M = fmaxf(M, a.part_ml[((lbase + a.red_rows[k]) * H + h) * 2]);
+    float L = 0.f;
     float4 o = make_float4(0, 0, 0, 0);
-    for (int k = b; k < e; ++k) {
-      const int64_t row = lbase + a.red_rows[k];
-      const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (row * H + h) * 2);
-      const float4 v = *reinterpret_cast<const float4*>(a.part_acc + row * H * D + x);
-      if (ml.x == -INFINITY) continue;
-      const float Mn = fmaxf(M, ml.x);
-      const float so = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-      const float sk = __builtin_amdgcn_exp2f(ml.x - Mn);
-      L = L * so + ml.y * sk;
-      o.x = o.x * so + v.x * sk; o.y = o.y * so + v.y * sk;
-      o.z = o.z * so + v.z * sk; o.w = o.w * so + v.w * sk;
-      M = Mn;
+    if (M != -INFINITY) {
+#pragma unroll 4
+      for (int k = b; k < e; ++k) {
+        const int64_t row = lbase + a.red_rows[k];
+        const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (row * H + h) * 2);
+        const float4 v = *reinterpret_cast<const float4*>(a.part_acc + row * H * D + x);
+        const float w = __builtin_amdgcn_exp2f(ml.x - M);     // 0 for an empty record (m = -inf)
+        L += ml.y * w;
+        o.x += v.x * w; o.y += v.y * w; o.z += v.z * w; o.w += v.w * w;
+      }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     *reinterpret_cast<float4*>(a.o[il] + static_cast<int64_t>(si.out_row) * H * D + x) =
@@ -255,7 +287,9 @@ __global__ __launch_bounds__(256) void k_attn_reduce(AttnArgs a, int D) {
 
 hipError_t launch_reduce(const AttnArgs& a, int n_reduced, int n_il, int D, hipStream_t s) {
   if (n_reduced == 0 || n_il == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_attn_reduce, dim3(n_reduced, n_il), dim3(256), 0, s, a, D);
+  const int quads = a.n_head * D / 4;
+  const int threads = std::min(1024, (quads + 63) / 64 * 64);
+  hipLaunchKernelGGL(k_attn_reduce, dim3(n_reduced, n_il), dim3(threads), 0, s, a, D);
   return hipGetLastError();
 }
 

@@ -473,26 +473,32 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   const bool valu_ok = g_.E() == 1024 && (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4);
   const int32_t QT = kMfmaRowsPerItem / G;   // query rows of one matrix-core workgroup
   // Item sizing.  One attend call launches (items x layers per call)
-  // workgroups; aim for about kTargetWorkgroups of them so every CU gets
-  // several and the last round is short, with at least 256 cells per item
-  // (an item's fixed costs -- q, the merge, a partial row -- stay small).
-  int64_t valu_cells = 0, lowreuse_cells = 0;
+  // workgroups.  Each bandwidth-bound class is cut into chunks of at most
+  // `ch` cells; ch is the largest power of two (256 .. 8192 cells) for which
+  // the launch still reaches its workgroup target, so a long context is
+  // split only when there are too few queries to fill the GPU.
+  const int64_t L = std::max(1, g_.attend_layers);
+  std::vector<std::pair<int32_t, int32_t>> valu_lists, low_lists;   // (cells, copies)
   for (const auto& c : P.classes) {
-    if (valu_ok && c.n_q <= kValuMaxQueries) valu_cells += static_cast<int64_t>(c.n_q) * c.n_cells;
-    else if (c.n_q * G <= 64) lowreuse_cells += static_cast<int64_t>(ceil_div(c.n_q, QT)) * c.n_cells;
+    if (c.n_q == 0 || c.n_cells == 0) continue;
+    if (valu_ok && c.n_q <= kValuMaxQueries) valu_lists.push_back({c.n_cells, c.n_q});
+    else if (c.n_q * G <= 64) low_lists.push_back({c.n_cells, ceil_div(c.n_q, QT) * g_.n_head_kv});
   }
-  const int64_t target_items = std::max<int64_t>(64, kTargetWorkgroups / std::max(1, g_.attend_layers));
-  auto pow2_floor = [](int64_t x, int32_t lo, int32_t hi) {
-    int32_t v = lo;
-    while (v < hi && 2 * static_cast<int64_t>(v) <= x) v *= 2;
-    return v;
+  auto pick_chunk = [&](const std::vector<std::pair<int32_t, int32_t>>& lists, int64_t target, int32_t lo,
+                        int32_t hi) {
+    int32_t ch = hi;
+    while (ch > lo) {
+      int64_t wg = 0;
+      for (const auto& x : lists) wg += static_cast<int64_t>(ceil_div(x.first, ch)) * x.second;
+      if (wg * L >= target) break;
+      ch /= 2;
+    }
+    return ch;
   };
-  // vector-ALU items: the chunk bounds the cells per item; a class's cells
-  // are then cut into equal parts (no near-empty remainder item)
-  int32_t chv = pow2_floor(valu_cells / target_items, 256, 8192);
-  // matrix-core items with few query rows are bandwidth-bound too: split
-  // their cells (in multiples of the 64-cell tile) across KV heads x chunks
-  int32_t chm_lowreuse = pow2_floor(lowreuse_cells * g_.n_head_kv / target_items, 256, 4096);
+  int32_t chv = pick_chunk(valu_lists, kValuTargetWorkgroups, 256, 8192);
+  // matrix-core items with few query rows are bandwidth-bound too: their
+  // cells (multiples of the 64-cell tile) are cut the same way
+  int32_t chm_lowreuse = pick_chunk(low_lists, kMfmaTargetWorkgroups, 256, 4096);
 
   for (int attempt = 0; attempt < 16; ++attempt) {
     P.items_valu.clear();
@@ -563,7 +569,11 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
       P.red_rows.insert(P.red_rows.end(), qrows[q].begin(), qrows[q].end());
       P.red_off.push_back(static_cast<int32_t>(P.red_rows.size()));
     }
-    // biggest MFMA items first: causal tiles late in a prompt see the most cells
+    // longest first in both sets (the kernels dispatch items in this order):
+    // the last workgroups of a launch are then the shortest ones
+    std::stable_sort(P.items_valu.begin(), P.items_valu.end(),
+                     [](const WorkItem& a, const WorkItem& b) { return a.c1 - a.c0 > b.c1 - b.c0; });
+    // MFMA items: causal tiles late in a prompt see the most cells
     std::stable_sort(P.items_mfma.begin(), P.items_mfma.end(), [](const WorkItem& a, const WorkItem& b) {
       return std::min(a.c1 - a.c0, a.qpos_max) > std::min(b.c1 - b.c0, b.qpos_max);
     });

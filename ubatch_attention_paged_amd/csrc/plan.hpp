@@ -21,7 +21,12 @@ constexpr int kSegCells = 64;          // cells per counting segment (one wavefr
 constexpr int kTileCells = 64;         // cells per attention tile; chunk starts are multiples of it
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
 constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV head) per MFMA item
-constexpr int kTargetWorkgroups = 3072; // attention workgroups aimed for per launch (256 CUs)
+// Workgroups a split-K launch should reach before its items are cut finer:
+// about 1.2 rounds of resident workgroups on 256 CUs (the vector-ALU kernel
+// keeps 5 per CU, the matrix-core kernel 2).  Cutting further only adds
+// partial rows and merge work.
+constexpr int kValuTargetWorkgroups = 1536;
+constexpr int kMfmaTargetWorkgroups = 640;
 
 struct SlotInfo {        // one query slot
   int32_t stream;
