@@ -67,7 +67,8 @@ typedef struct kvattn_params {
   int32_t n_head;         /* query heads; a multiple of n_head_kv */
   int32_t n_head_kv;      /* KV heads */
   int32_t head_dim;       /* 16, 32, 64 or 128 */
-  int32_t kv_size;        /* cells PER STREAM (tensor dimension 1) */
+  int32_t kv_size;        /* cells PER STREAM (tensor dimension 1); one layer's tensor,
+                             n_stream * kv_size * n_head_kv * head_dim * 2 bytes, < 2 GiB */
   int32_t n_stream;       /* 1 = unified cache; a slot's stream is seq_id[0] % n_stream */
   int32_t n_seq_max;      /* sequence ids must lie in [0, n_seq_max); <= KVATTN_MAX_SEQ */
   int32_t n_batch;        /* <= 0: 2048; clamped to kv_size*n_stream when causal */

@@ -251,3 +251,21 @@ def test_workspace_and_cache_bytes():
     assert 0 < ws < 512 * 2 ** 20
     p.head_dim = 24
     assert K.kvattn_workspace_bytes(p) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=48), dict(n_head=3, n_head_kv=2), dict(n_head=32, n_head_kv=2),
+                                dict(n_seq_max=65), dict(kv_size=0),
+                                # one layer's K tensor at 2 GiB: 2^20 cells x 8 heads x 128 x 2 B
+                                dict(kv_size=1 << 20, n_head=8, n_head_kv=8, head_dim=128)])
+def test_create_rejects_bad_geometry(kw):
+    args = dict(n_layer=1, n_head=2, n_head_kv=1, head_dim=16, kv_size=64, n_seq_max=1)
+    args.update(kw)
+    with pytest.raises(K.KvattnError) as e:
+        K.Context(args.pop("n_layer"), args.pop("n_head"), args.pop("n_head_kv"), args.pop("head_dim"), **args)
+    assert e.value.code == K.KVATTN_EINVAL
+
+
+def test_create_accepts_largest_layer_tensor():
+    # just below 2 GiB per layer tensor: (2^20 - 64) cells x 1024 numbers x 2 B
+    ctx = K.Context(1, 8, 8, 128, kv_size=(1 << 20) - 64, n_seq_max=1)
+    assert 0 < ctx.n_kv() <= (1 << 20) - 64

@@ -433,6 +433,7 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   a.n_head_kv = g.n_head_kv;
   a.causal = g.causal;
   a.scale_log2e = g.kq_scale * 1.4426950408889634f;
+  a.layer_bytes = static_cast<uint32_t>(static_cast<size_t>(g.n_stream) * g.kv_size * g.E() * 2);
   const int64_t per = std::max<int64_t>(1, P.n_partial_rows);
   const int32_t chunk = static_cast<int32_t>(std::min<int64_t>(kMaxLayersPerLaunch, kPartialRowsCap / per));
   for (int32_t l0 = 0; l0 < n_il; l0 += chunk) {

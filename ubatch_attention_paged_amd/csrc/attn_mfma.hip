@@ -68,9 +68,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const int half_id = lane >> 5;
   const ClassInfo ci = a.classes[it.cls];
   const bool pure = ci.pure;
-  const _Float16* __restrict__ Kl = a.k[il];
-  const _Float16* __restrict__ Vl = a.v[il];
-  const int64_t sbase = static_cast<int64_t>(ci.stream) * a.kv_size;
+  // K / V rows are gathered with range-checked buffer loads: 32-bit byte
+  // offsets, and an empty slot reads zeros from an out-of-range offset
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(a.k[il], a.layer_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(a.v[il], a.layer_bytes);
+  const uint32_t row_bytes = static_cast<uint32_t>(E) * 2;
+  const uint32_t sbase_bytes = static_cast<uint32_t>(ci.stream) * static_cast<uint32_t>(a.kv_size) * row_bytes;
 
   // this lane's query row
   const int r = 32 * w + (lane & 31);
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const int seg = tid % SEGS;
   const int row0 = tid / SEGS;
   const bool loader = row0 < ROW_STEP;
-  uint4 kreg[NP], vreg[NP];
+  u32x4 kreg[NP], vreg[NP];
   int cnext[NP];
   int pk = INT32_MAX;
   uint64_t mk = 0;
@@ -133,17 +136,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const int idx = it.c0 + tile * KT + row;
     return idx < it.c1 ? a.csr_cell[idx] : -1;
   };
+  const uint32_t col_bytes = static_cast<uint32_t>(kvh * D + seg * 8) * 2;
   auto issue = [&](int tile, const int* cells) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      if (loader && cells[p] >= 0) {
-        const int64_t off = (sbase + cells[p]) * E + kvh * D + seg * 8;
-        kreg[p] = *reinterpret_cast<const uint4*>(Kl + off);
-        vreg[p] = *reinterpret_cast<const uint4*>(Vl + off);
-      } else {
-        kreg[p] = make_uint4(0, 0, 0, 0);
-        vreg[p] = make_uint4(0, 0, 0, 0);
-      }
+      const uint32_t off =
+          cells[p] >= 0 ? sbase_bytes + static_cast<uint32_t>(cells[p]) * row_bytes + col_bytes : kOobOffset;
+      kreg[p] = buffer_load16(krs, off);
+      vreg[p] = buffer_load16(vrs, off);
     }
     if (tid < KT) {
       const int idx = it.c0 + tile * KT + tid;
@@ -171,8 +171,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int rr = row0 + p * ROW_STEP;
-        *reinterpret_cast<uint4*>(&Ks[buf][rr * KSK + seg * 8]) = kreg[p];
-        *reinterpret_cast<uint4*>(&Vs[buf][rr * KSV + seg * 8]) = vreg[p];
+        *reinterpret_cast<u32x4*>(&Ks[buf][rr * KSK + seg * 8]) = kreg[p];
+        *reinterpret_cast<u32x4*>(&Vs[buf][rr * KSV + seg * 8]) = vreg[p];
       }
     }
     if (tid < KT) {

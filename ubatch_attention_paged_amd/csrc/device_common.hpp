@@ -38,6 +38,20 @@ KVATTN_DEV half4 lds_read_tr16(const _Float16* p) {
   return __builtin_bit_cast(half4, v);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over [p, p + bytes) (gfx9-family descriptor word 3,
+// stride 0).  Loads through it are range-checked by the hardware: a load at
+// an offset at or past `bytes` returns zeros instead of touching memory.
+KVATTN_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
+                                          0x00020000);
+}
+constexpr uint32_t kOobOffset = 0x80000000u;   // past any buffer (buffers stay below 2 GiB)
+KVATTN_DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+}
+
 // Accumulator register r of lane l in a 32x32 MFMA block holds row
 // 8*(r/4) + 4*(l/32) + r%4, column l%32.
 KVATTN_DEV int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }

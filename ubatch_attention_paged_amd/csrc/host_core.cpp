@@ -42,6 +42,11 @@ int make_geometry(const kvattn_params& p, Geometry& g, std::string& err) {
     err = "kv_size * n_stream too large";
     return KVATTN_EINVAL;
   }
+  // the kernels address a layer's K or V tensor with 32-bit byte offsets
+  if (static_cast<int64_t>(p.kv_size) * p.n_stream * p.n_head_kv * p.head_dim * 2 >= (1LL << 31)) {
+    err = "one layer's K (or V) tensor must stay below 2 GiB";
+    return KVATTN_EINVAL;
+  }
   if (p.n_ubatch < 0) {
     err = "n_ubatch must be >= 0";
     return KVATTN_EINVAL;

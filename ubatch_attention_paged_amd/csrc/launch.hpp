@@ -65,6 +65,7 @@ struct AttnArgs {
   int32_t n_head_kv;
   int32_t causal;
   float scale_log2e;          // kq_scale * log2(e)
+  uint32_t layer_bytes;       // bytes of one layer's K (= V) tensor, < 2 GiB
 };
 
 struct MaskArgs {

@@ -21,12 +21,14 @@ constexpr int kSegCells = 64;          // cells per counting segment (one wavefr
 constexpr int kTileCells = 64;         // cells per attention tile; chunk starts are multiples of it
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
 constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV head) per MFMA item
-// Workgroups a split-K launch should reach before its items are cut finer:
-// about 1.2 rounds of resident workgroups on 256 CUs (the vector-ALU kernel
-// keeps 5 per CU, the matrix-core kernel 2).  Cutting further only adds
-// partial rows and merge work.
-constexpr int kValuTargetWorkgroups = 1536;
-constexpr int kMfmaTargetWorkgroups = 640;
+// Workgroups a split-K launch should reach before its items are cut finer
+// (256 CUs; the vector-ALU kernel keeps 5 workgroups per CU, the
+// matrix-core kernel 2).  Measured on decode steps: long items win over a
+// short tail -- each cut adds a partial row, merge work and per-item fixed
+// costs (query load, pipeline ramp) -- so the targets sit near one round of
+// resident workgroups or below.
+constexpr int kValuTargetWorkgroups = 1024;
+constexpr int kMfmaTargetWorkgroups = 320;
 
 struct SlotInfo {        // one query slot
   int32_t stream;
