@@ -388,6 +388,10 @@ def main():
                          "kv_read_gbs": round(r["kv_read_gbs"], 1), "hbm_frac": round(r["hbm_frac"], 4),
                          "attend_avg_ms": round(r["attend_avg_ms"], 4),
                          "unique_cells_per_step": r["unique_cells"], "plan": r["plan"]}
+            if name == "cb_decode":
+                # the vector-ALU kernel's HBM bytes per launch from the committed
+                # FETCH_SIZE / WRITE_SIZE summary of this workload (None if stale)
+                dec[name]["traffic_k_attn_valu"] = committed_traffic("k_attn_valu", "attn_valu.hip")
         line["decode"] = dec
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
