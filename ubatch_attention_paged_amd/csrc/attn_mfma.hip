@@ -164,6 +164,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const int s16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
   const int qpos = si.pos, qseq = si.seq0;
+  const int pos_lim = a.causal ? qpos : INT32_MAX - 1;   // largest visible cell position
   for (int i = 0; i < ntile; ++i) {
     const int buf = i & 1;
     // stage tile i
@@ -192,70 +193,71 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     if (a.causal && tmin > it.qpos_max) continue;
     const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min);
 
-    floatx16 sacc[2];
+    // The tile is two 32-cell blocks, each with its own online-softmax step.
+    // Source order interleaves them so that the matrix core always has
+    // independent work next to the vector ALU's: S(1) is issued beside the
+    // exponentials of block 0 and PV(0) beside those of block 1 (the
+    // rescale branches sit between these regions, not inside them).
+    float rs = 0.f;    // this lane's share of the row sum of this tile
+    auto s_block = [&](int kb) {
+      floatx16 acc;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const half8 ka =
             *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + (lane & 31)) * KSK + 16 * ks + 8 * half_id]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], sacc[kb], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], acc, 0, 0, 0);
       }
-    }
-    if (!full) {
-      // cells past the list end hold position INT32_MAX, so the causal test
-      // also removes them
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      return acc;
+    };
+    // mask + running-max update of one block; returns the offset to subtract
+    auto max_block = [&](int kb, floatx16& sb) {
+      if (!full) {
+        // branch-free: cells past the list end hold position INT32_MAX and an
+        // empty sequence set, so both tests remove them
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb * 32 + acc_row(e, lane);
-          bool vis = a.causal ? (kpos_s[buf][key] <= qpos) : (key < nk);
-          if (!pure) vis = vis & static_cast<bool>((kmask_s[buf][key] >> qseq) & 1ULL);
-          sacc[kb][e] = vis ? sacc[kb][e] : -INFINITY;
+          const bool vis = (kpos_s[buf][key] <= pos_lim) & static_cast<bool>((kmask_s[buf][key] >> qseq) & 1ULL);
+          sb[e] = vis ? sb[e] : -INFINITY;
         }
-    }
-    // online softmax over this lane's row (the other half-wave holds the rest)
-    float mx = -INFINITY;
+      }
+      // lane l ^ 32 holds the other 16 cells of the block for the same row
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sb[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool grow = mx > m_run + kRescaleSlack;     // false while the row sees nothing
+      if (ballot(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+        rs *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[kb][e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = mx > m_run + kRescaleSlack;     // false while the row sees nothing
-    if (ballot(grow)) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+        for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
-      for (int db = 0; db < DP / 32; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float rs = 0.f;
-    half8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        m_run = m_new;
+      }
+      return m_run == -INFINITY ? 0.f : m_run;
+    };
+    // F16 weights of one block (B operand of the PV product) and their sum
+    auto weights = [&](const floatx16& sb, float m_use, half8 (&pb)[2]) {
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         half2v ph;
-        ph[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[kb][e] - m_use));
-        ph[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sacc[kb][e + 1] - m_use));
+        ph[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sb[e] - m_use));
+        ph[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sb[e + 1] - m_use));
         rs = dot2_sum(ph, rs);          // the row sum sees the F16 weights the PV product sees
-        pb[kb][e >> 3][e & 7] = ph[0];
-        pb[kb][e >> 3][(e & 7) + 1] = ph[1];
+        pb[e >> 3][e & 7] = ph[0];
+        pb[e >> 3][(e & 7) + 1] = ph[1];
       }
-    rs += __shfl_xor(rs, 32);
-    l_run += rs;
+    };
     // O^T += V^T P^T: source lane s of each 16-lane group points at cell row
-    // key0 + s/4, column dsub + 4*(s%4); lane gets cells key0..key0+3 of column
-    // db*32 + lane%32 (and key0+8.. for the upper four k-values)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    // key0 + s/4, column dsub + 4*(s%4); lane gets cells key0..key0+3 of
+    // column db*32 + lane%32 (and key0+8.. for the upper four k-values)
+    auto pv_block = [&](int kb, const half8 (&pb)[2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int key0 = kb * 32 + 16 * st + 4 * half_id;
@@ -265,9 +267,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           const half4 lo = lds_read_tr16(vb + db * 32);
           const half4 hi = lds_read_tr16(vb + db * 32 + 8 * KSV);
           const half8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[kb][st], oacc[db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[st], oacc[db], 0, 0, 0);
         }
       }
+    };
+    floatx16 s0 = s_block(0);
+    const float mu0 = max_block(0, s0);
+    floatx16 s1 = s_block(1);
+    half8 p0[2], p1[2];
+    weights(s0, mu0, p0);
+    const float mu1 = max_block(1, s1);
+    pv_block(0, p0);
+    weights(s1, mu1, p1);
+    pv_block(1, p1);
+    rs += __shfl_xor(rs, 32);
+    l_run += rs;
   }
 
   if (!qvalid) return;
