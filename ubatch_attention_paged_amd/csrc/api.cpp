@@ -87,6 +87,9 @@ struct kvattn_ctx {
   int32_t plan_serial = -1;
   std::vector<CellUpdate> upd;
   std::vector<char> blob;
+  CsrArgs pending{};          // commit kernels' arguments, built by upload_commit
+  bool commit_pending = false;
+  char* arena() { return ws + wl.arena; }
 
   int fail(int code, const std::string& msg) {
     err = msg;
@@ -198,7 +201,7 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
     copy(A.v[v].red_rows, P.red_rows.data(), P.red_rows.size() * 4);
   }
   copy(A.updates, c->upd.data(), c->upd.size() * sizeof(CellUpdate));
-  char* arena = c->ws + c->wl.arena;
+  char* arena = c->arena();
   if (A.total) HIP_TRY(c, hipMemcpyAsync(arena, b, A.total, hipMemcpyHostToDevice, s));
   HIP_TRY(c, hipEventRecord(c->ev[st], s));
   c->ev_used[st] = true;
@@ -225,7 +228,9 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
   ca.tile_min = c->dptr<int32_t>(c->wl.tile_min);
   ca.tile_max = c->dptr<int32_t>(c->wl.tile_max);
   ca.max_class_tiles = P0.max_class_tiles;
-  HIP_TRY(c, launch_commit(ca, s));
+  // launched by the caller: alone, or inside the first store launch
+  c->pending = ca;
+  c->commit_pending = true;
   c->plan_ubatch = k;
   c->plan_serial = c->core.split_serial();
   if (!c->plan_ok) return c->fail(rc0 ? rc0 : rc1, rc0 ? e0 : e1);
@@ -310,6 +315,7 @@ void kvattn_destroy(kvattn_ctx* c) {
       if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
       if (c->stage[i]) (void)hipHostFree(c->stage[i]);
     }
+
   }
   delete c;
 }
@@ -358,6 +364,8 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
   int k, rc;
   if ((rc = check_ubatch(c, ub, &k)) || (rc = check_layers(c, il0, n_il))) return rc;
   if (n_il > 0 && (!k_cur || !v_cur)) return c->fail(KVATTN_EINVAL, "k_cur / v_cur is NULL");
+  for (int32_t i = 0; i < n_il; ++i)
+    if (!k_cur[i] || !v_cur[i]) return c->fail(KVATTN_EINVAL, "NULL k_cur / v_cur entry");
   UbatchRec& u = c->core.ubatches()[k];
   if (!c->has_dev && n_il == 0) {
     // host-only context: a zero-layer store commits the placement and nothing else
@@ -377,21 +385,29 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
   } else if (c->core.latest_committed() != k || !plan_current(c, k)) {
     return c->fail(KVATTN_ESTATE, "only the most recently committed ubatch can be stored again");
   }
+  // a small commit rides in one extra workgroup of the first store launch
+  // (it does not depend on the stores); otherwise it runs first on its own
+  bool fuse = false;
+  if (c->commit_pending) {
+    c->commit_pending = false;
+    fuse = n_il > 0 && commit_is_small(c->pending);
+    if (!fuse) HIP_TRY(c, launch_commit(c->pending, s));
+  }
   const Geometry& g = c->core.geo();
   StoreArgs a{};
-  a.dst_rows = reinterpret_cast<const int32_t*>(c->ws + c->wl.arena + c->al.dst_rows);
+  a.dst_rows = reinterpret_cast<const int32_t*>(c->arena() + c->al.dst_rows);
   a.n_rows = static_cast<int32_t>(u.cells.size());
   a.E = g.E();
   for (int32_t l0 = 0; l0 < n_il; l0 += kMaxLayersPerLaunch) {
     const int n = std::min<int32_t>(kMaxLayersPerLaunch, n_il - l0);
     for (int i = 0; i < n; ++i) {
-      if (!k_cur[l0 + i] || !v_cur[l0 + i]) return c->fail(KVATTN_EINVAL, "NULL k_cur / v_cur entry");
       a.k_cur[i] = static_cast<const float*>(k_cur[l0 + i]);
       a.v_cur[i] = static_cast<const float*>(v_cur[l0 + i]);
       a.k[i] = static_cast<_Float16*>(c->K[il0 + l0 + i]);
       a.v[i] = static_cast<_Float16*>(c->V[il0 + l0 + i]);
     }
-    HIP_TRY(c, launch_store(a, n, s));
+    if (fuse && l0 == 0) HIP_TRY(c, launch_store_commit(a, n, c->pending, s));
+    else HIP_TRY(c, launch_store(a, n, s));
   }
   return rc;
 }
@@ -412,7 +428,7 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   const Plan& P = c->plan[v];
   if (P.slots.empty()) return KVATTN_OK;      // no query rows (e.g. no flagged slot)
   const VariantLayout& VL = c->al.v[v];
-  char* arena = c->ws + c->wl.arena;
+  char* arena = c->arena();
   AttnArgs a{};
   a.slots = reinterpret_cast<const SlotInfo*>(arena + VL.slots);
   a.classes = reinterpret_cast<const ClassInfo*>(arena + c->al.classes);
@@ -474,7 +490,7 @@ int kvattn_get_mask(kvattn_ctx* c, const kvattn_ubatch* ub, void* d_mask, size_t
   MaskArgs a{};
   a.cpos = c->dptr<int32_t>(c->wl.cpos);
   a.cmask = c->dptr<uint64_t>(c->wl.cmask);
-  a.slots = reinterpret_cast<const SlotInfo*>(c->ws + c->wl.arena + c->al.v[0].slots);
+  a.slots = reinterpret_cast<const SlotInfo*>(c->arena() + c->al.v[0].slots);
   a.mask = static_cast<uint16_t*>(d_mask);
   a.n_rows = T;
   a.n_kv = P.n_kv;

@@ -1,6 +1,8 @@
 // gfx950 kernels of the store/commit half of the path:
 //
 //   k_store          K/V rows of a ubatch -> F16 (nearest-even) into their cells
+//   k_store_commit   the same, with one extra workgroup doing the whole commit
+//                    below for a small cache (overlapped with the stores)
 //   k_apply_updates  cell-table changes -> device mirror (pos, sequence set)
 //   k_csr_*          per-class lists of visible cells, ascending cell index
 //   k_tile_minmax    smallest / largest position of every 64-cell tile of a list
@@ -18,7 +20,7 @@ namespace kvattn {
 
 // fp32 rows -> F16 rows of the cache; each thread converts 8 consecutive
 // values (two 16 B loads, one 16 B store).
-__global__ __launch_bounds__(256) void k_store(StoreArgs a) {
+KVATTN_DEV void store_rows(const StoreArgs& a) {
   const int il = blockIdx.y;
   const int which = blockIdx.z;             // 0 = K, 1 = V
   const int vec_per_row = a.E >> 3;
@@ -37,6 +39,8 @@ __global__ __launch_bounds__(256) void k_store(StoreArgs a) {
   h[6] = static_cast<_Float16>(x1.z); h[7] = static_cast<_Float16>(x1.w);
   *reinterpret_cast<half8*>(dst) = h;
 }
+
+__global__ __launch_bounds__(256) void k_store(StoreArgs a) { store_rows(a); }
 
 hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(a.n_rows) * (a.E / 8);
@@ -151,6 +155,114 @@ __global__ __launch_bounds__(256) void k_tile_minmax(CsrArgs a) {
       a.tile_max[ci.tile_base + k] = mx;
     }
   }
+}
+
+// The whole commit in one 256-thread workgroup, for caches of at most
+// kSmallCommitCells (stream, cell) pairs below n_kv and kSmallCommitClasses
+// classes: mirror updates, classification (kept in LDS), the ordered
+// per-class lists (256 cells at a time in (stream, cell) order: a cell's
+// slot is its class's running offset + the same-class cells of earlier
+// wavefronts of the chunk + its rank in its wavefront), then the per-tile
+// position ranges.  Produces exactly what the multi-kernel path produces.
+KVATTN_DEV void commit_small(const CsrArgs& a) {
+  __shared__ int16_t cls_s[kSmallCommitCells];
+  __shared__ int32_t wc[4][kSmallCommitClasses];
+  __shared__ int32_t base[kSmallCommitClasses];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int i = tid; i < a.n_updates; i += 256) {
+    const CellUpdate u = a.updates[i];
+    a.cpos[u.idx] = u.pos;
+    a.cmask[u.idx] = u.mask;
+  }
+  __syncthreads();
+  const int nc = a.n_classes;
+  if (nc == 0) return;
+  const int total = a.n_stream * a.n_kv;
+  for (int i = tid; i < total; i += 256) {
+    const int s = i / a.n_kv, j = i % a.n_kv;
+    const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
+    int cls = -1;
+    if (a.cpos[idx] >= 0) {
+      const uint64_t m = a.cmask[idx];
+      int lo = a.lookup_off[s], hi = a.lookup_off[s + 1] - 1;
+      while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const uint64_t mm = a.lookup[mid].mask;
+        if (mm == m) { cls = a.lookup[mid].cls; break; }
+        if (mm < m) lo = mid + 1; else hi = mid - 1;
+      }
+    }
+    cls_s[i] = static_cast<int16_t>(cls);
+  }
+  if (tid < nc) base[tid] = a.classes[tid].cell_off;
+  __syncthreads();
+  for (int i0 = 0; i0 < total; i0 += 256) {
+    const int i = i0 + tid;
+    const int cls = i < total ? cls_s[i] : -1;
+    for (int z = tid; z < 4 * kSmallCommitClasses; z += 256) wc[z / kSmallCommitClasses][z % kSmallCommitClasses] = 0;
+    __syncthreads();
+    int rank = 0;
+    uint64_t active = ballot(cls >= 0);
+    while (active) {
+      const int leader = __builtin_ctzll(active);
+      const int c = readlane_i(cls, leader);
+      const uint64_t same = ballot(cls == c);
+      if (cls == c) rank = __popcll(same & lanemask_lt());
+      if (lane == leader) wc[w][c] = __popcll(same);
+      active &= ~same;
+    }
+    __syncthreads();
+    if (cls >= 0) {
+      int dst = base[cls] + rank;
+      for (int w2 = 0; w2 < w; ++w2) dst += wc[w2][cls];
+      const int s = i / a.n_kv, j = i % a.n_kv;
+      const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
+      if (dst < a.csr_cap) {
+        a.csr_cell[dst] = j;
+        a.csr_pos[dst] = a.cpos[idx];
+        a.csr_mask[dst] = a.cmask[idx];
+      }
+    }
+    __syncthreads();
+    if (tid < nc) base[tid] += wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
+    __syncthreads();
+  }
+  for (int c = 0; c < nc; ++c) {
+    const ClassInfo ci = a.classes[c];
+    const int nt = (ci.n_cells + kTileCells - 1) / kTileCells;
+    for (int k = w; k < nt; k += 4) {
+      const int j = k * kTileCells + lane;
+      const bool in = j < ci.n_cells;
+      const int p = in ? a.csr_pos[ci.cell_off + j] : INT32_MAX;
+      const int mn = wave_min_i(p);
+      const int mx = wave_max_i(in ? p : INT32_MIN);
+      if (lane == 0) {
+        a.tile_min[ci.tile_base + k] = mn;
+        a.tile_max[ci.tile_base + k] = mx;
+      }
+    }
+  }
+}
+
+bool commit_is_small(const CsrArgs& a) {
+  return static_cast<int64_t>(a.n_stream) * a.n_kv <= kSmallCommitCells && a.n_classes <= kSmallCommitClasses;
+}
+
+// the store grid plus one trailing x-block; that block's (y, z) = (0, 0)
+// instance runs the small commit
+__global__ __launch_bounds__(256) void k_store_commit(StoreArgs a, CsrArgs c) {
+  if (blockIdx.x == gridDim.x - 1) {
+    if (blockIdx.y == 0 && blockIdx.z == 0) commit_small(c);
+    return;
+  }
+  store_rows(a);
+}
+
+hipError_t launch_store_commit(const StoreArgs& a, int n_il, const CsrArgs& c, hipStream_t s) {
+  const int64_t n = static_cast<int64_t>(a.n_rows) * (a.E / 8);
+  dim3 grid(static_cast<unsigned>((n + 255) / 256) + 1, n_il, 2);
+  hipLaunchKernelGGL(k_store_commit, grid, dim3(256), 0, s, a, c);
+  return hipGetLastError();
 }
 
 hipError_t launch_commit(const CsrArgs& a, hipStream_t s) {

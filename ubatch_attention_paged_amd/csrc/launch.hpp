@@ -78,6 +78,10 @@ struct MaskArgs {
 
 hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s);
 hipError_t launch_commit(const CsrArgs& a, hipStream_t s);
+// a commit small enough for one workgroup (launch_store_commit can carry it)
+bool commit_is_small(const CsrArgs& a);
+// the stores of n_il >= 1 layers and, in one extra workgroup, a small commit
+hipError_t launch_store_commit(const StoreArgs& a, int n_il, const CsrArgs& c, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
 // head_dim / group size are dispatched at run time
 hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s);
