@@ -77,6 +77,7 @@ struct kvattn_ctx {
   bool dev_ready = false;
   void* stage[kStages] = {};
   size_t stage_cap[kStages] = {};
+  char* stage_dev[kStages] = {};     // device view of each pinned staging buffer
   hipEvent_t ev[kStages] = {};
   bool ev_used[kStages] = {};
   int stage_next = 0;
@@ -89,6 +90,11 @@ struct kvattn_ctx {
   std::vector<char> blob;
   CsrArgs pending{};          // commit kernels' arguments, built by upload_commit
   bool commit_pending = false;
+  // fused: the commit rides in the first store launch and reads the plan
+  // from staging buffer fused_stage (whose event is recorded after it)
+  bool pending_fused = false;
+  int fused_stage = 0;
+  const int32_t* fused_dst_rows = nullptr;
   char* arena() { return ws + wl.arena; }
 
   int fail(int code, const std::string& msg) {
@@ -133,7 +139,7 @@ size_t put(std::vector<char>& blob, size_t at, const std::vector<T>& v) {
 
 // Plan of the committed ubatch k -> pinned staging -> device arena, then the
 // mirror update and the cell-list build, all on stream s.
-int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
+int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
   const Geometry& g = c->core.geo();
   UbatchRec& u = c->core.ubatches()[k];
   std::string e0, e1;
@@ -183,6 +189,9 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
     const size_t cap = std::max<size_t>(A.total, 1 << 20);
     HIP_TRY(c, hipHostMalloc(&c->stage[st], cap, hipHostMallocDefault));
     c->stage_cap[st] = cap;
+    void* dv = nullptr;
+    HIP_TRY(c, hipHostGetDevicePointer(&dv, c->stage[st], 0));
+    c->stage_dev[st] = static_cast<char*>(dv);
   }
   char* b = static_cast<char*>(c->stage[st]);
   auto copy = [&](size_t at, const void* src, size_t bytes) { if (bytes) std::memcpy(b + at, src, bytes); };
@@ -202,10 +211,6 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
   }
   copy(A.updates, c->upd.data(), c->upd.size() * sizeof(CellUpdate));
   char* arena = c->arena();
-  if (A.total) HIP_TRY(c, hipMemcpyAsync(arena, b, A.total, hipMemcpyHostToDevice, s));
-  HIP_TRY(c, hipEventRecord(c->ev[st], s));
-  c->ev_used[st] = true;
-
   CsrArgs ca{};
   ca.cpos = c->dptr<int32_t>(c->wl.cpos);
   ca.cmask = c->dptr<uint64_t>(c->wl.cmask);
@@ -214,10 +219,6 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
   ca.csr_cell = c->dptr<int32_t>(c->wl.csr_cell);
   ca.csr_pos = c->dptr<int32_t>(c->wl.csr_pos);
   ca.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);
-  ca.classes = reinterpret_cast<const ClassInfo*>(arena + A.classes);
-  ca.lookup = reinterpret_cast<const LookupEntry*>(arena + A.lookup);
-  ca.lookup_off = reinterpret_cast<const int32_t*>(arena + A.lookup_off);
-  ca.updates = reinterpret_cast<const CellUpdate*>(arena + A.updates);
   ca.n_updates = static_cast<int32_t>(c->upd.size());
   ca.n_classes = c->plan_ok ? static_cast<int32_t>(P0.classes.size()) : 0;
   ca.n_seg = P0.n_seg;
@@ -228,7 +229,29 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s) {
   ca.tile_min = c->dptr<int32_t>(c->wl.tile_min);
   ca.tile_max = c->dptr<int32_t>(c->wl.tile_max);
   ca.max_class_tiles = P0.max_class_tiles;
+  ca.n_lookup = static_cast<int32_t>(P0.lookup.size());
+  // A small commit that a store launch will carry reads its tables straight
+  // from the pinned staging buffer, and that launch copies the plan into the
+  // device arena: no separate copy (and its latency) sits in the stream.
+  const bool fused = may_fuse && commit_is_small(ca);
+  const char* src = fused ? c->stage_dev[st] : arena;
+  ca.classes = reinterpret_cast<const ClassInfo*>(src + A.classes);
+  ca.lookup = reinterpret_cast<const LookupEntry*>(src + A.lookup);
+  ca.lookup_off = reinterpret_cast<const int32_t*>(src + A.lookup_off);
+  ca.updates = reinterpret_cast<const CellUpdate*>(src + A.updates);
+  if (fused) {
+    ca.plan_src = c->stage_dev[st];
+    ca.plan_dst = arena;
+    ca.plan_n16 = static_cast<int32_t>((A.total + 15) / 16);
+    c->fused_stage = st;
+    c->fused_dst_rows = reinterpret_cast<const int32_t*>(c->stage_dev[st] + A.dst_rows);
+  } else {
+    if (A.total) HIP_TRY(c, hipMemcpyAsync(arena, b, A.total, hipMemcpyHostToDevice, s));
+    HIP_TRY(c, hipEventRecord(c->ev[st], s));
+    c->ev_used[st] = true;
+  }
   // launched by the caller: alone, or inside the first store launch
+  c->pending_fused = fused;
   c->pending = ca;
   c->commit_pending = true;
   c->plan_ubatch = k;
@@ -380,7 +403,7 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
     if (il0 != 0) return c->fail(KVATTN_ESTATE, "the first store of a ubatch must start at layer 0");
     c->upd.clear();
     if ((rc = c->core.commit(k, &c->upd, c->err))) return rc;
-    rc = upload_commit(c, k, s);
+    rc = upload_commit(c, k, s, n_il > 0);
     if (rc && rc != KVATTN_ENOMEM) return rc;
   } else if (c->core.latest_committed() != k || !plan_current(c, k)) {
     return c->fail(KVATTN_ESTATE, "only the most recently committed ubatch can be stored again");
@@ -390,7 +413,7 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
   bool fuse = false;
   if (c->commit_pending) {
     c->commit_pending = false;
-    fuse = n_il > 0 && commit_is_small(c->pending);
+    fuse = c->pending_fused;
     if (!fuse) HIP_TRY(c, launch_commit(c->pending, s));
   }
   const Geometry& g = c->core.geo();
@@ -406,8 +429,15 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
       a.k[i] = static_cast<_Float16*>(c->K[il0 + l0 + i]);
       a.v[i] = static_cast<_Float16*>(c->V[il0 + l0 + i]);
     }
-    if (fuse && l0 == 0) HIP_TRY(c, launch_store_commit(a, n, c->pending, s));
-    else HIP_TRY(c, launch_store(a, n, s));
+    if (fuse && l0 == 0) {
+      StoreArgs af = a;
+      af.dst_rows = c->fused_dst_rows;     // the arena copy lands during this launch
+      HIP_TRY(c, launch_store_commit(af, n, c->pending, s));
+      HIP_TRY(c, hipEventRecord(c->ev[c->fused_stage], s));
+      c->ev_used[c->fused_stage] = true;
+    } else {
+      HIP_TRY(c, launch_store(a, n, s));
+    }
   }
   return rc;
 }

@@ -158,49 +158,73 @@ __global__ __launch_bounds__(256) void k_tile_minmax(CsrArgs a) {
 }
 
 // The whole commit in one 256-thread workgroup, for caches of at most
-// kSmallCommitCells (stream, cell) pairs below n_kv and kSmallCommitClasses
-// classes: mirror updates, classification (kept in LDS), the ordered
-// per-class lists (256 cells at a time in (stream, cell) order: a cell's
-// slot is its class's running offset + the same-class cells of earlier
-// wavefronts of the chunk + its rank in its wavefront), then the per-tile
-// position ranges.  Produces exactly what the multi-kernel path produces.
+// kSmallCommitCells (stream, cell) pairs below n_kv, kSmallCommitClasses
+// classes and lookup entries and kSmallCommitStreams streams: mirror
+// updates, classification (kept in LDS), the ordered per-class lists (256
+// cells at a time in (stream, cell) order: a cell's slot is its class's
+// running offset + the same-class cells of earlier wavefronts of the chunk +
+// its rank in its wavefront), then the per-tile position ranges.  Produces
+// exactly what the multi-kernel path produces.  The class and lookup tables
+// are read once into LDS (they may sit in host memory); each thread reads
+// its cells' mirror entries once, up front, and keeps them in registers.
 KVATTN_DEV void commit_small(const CsrArgs& a) {
-  __shared__ int16_t cls_s[kSmallCommitCells];
+  constexpr int KMAX = kSmallCommitCells / 256;     // cells per thread at most
   __shared__ int32_t wc[4][kSmallCommitClasses];
   __shared__ int32_t base[kSmallCommitClasses];
+  __shared__ LookupEntry lk[kSmallCommitClasses];
+  __shared__ ClassInfo cl[kSmallCommitClasses];
+  __shared__ int32_t lko[kSmallCommitStreams + 1];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nc = a.n_classes;
+  if (tid < a.n_lookup) lk[tid] = a.lookup[tid];
+  if (tid < nc) cl[tid] = a.classes[tid];
+  if (tid <= a.n_stream && nc > 0) lko[tid] = a.lookup_off[tid];
   for (int i = tid; i < a.n_updates; i += 256) {
     const CellUpdate u = a.updates[i];
     a.cpos[u.idx] = u.pos;
     a.cmask[u.idx] = u.mask;
   }
   __syncthreads();
-  const int nc = a.n_classes;
   if (nc == 0) return;
   const int total = a.n_stream * a.n_kv;
-  for (int i = tid; i < total; i += 256) {
-    const int s = i / a.n_kv, j = i % a.n_kv;
-    const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
+  // every cell this thread will place (cell tid + 256 k), read once: its
+  // position, sequence set and class stay in registers
+  int pos_r[KMAX], cls_r[KMAX];
+  uint64_t msk_r[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    const int i = tid + 256 * k;
+    pos_r[k] = -1;
+    msk_r[k] = 0;
+    if (i < total) {
+      const int64_t idx = static_cast<int64_t>(i / a.n_kv) * a.kv_size + i % a.n_kv;
+      pos_r[k] = a.cpos[idx];
+      msk_r[k] = a.cmask[idx];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
     int cls = -1;
-    if (a.cpos[idx] >= 0) {
-      const uint64_t m = a.cmask[idx];
-      int lo = a.lookup_off[s], hi = a.lookup_off[s + 1] - 1;
+    const int i = tid + 256 * k;
+    if (i < total && pos_r[k] >= 0) {
+      const int s = i / a.n_kv;
+      int lo = lko[s], hi = lko[s + 1] - 1;
       while (lo <= hi) {
         const int mid = (lo + hi) >> 1;
-        const uint64_t mm = a.lookup[mid].mask;
-        if (mm == m) { cls = a.lookup[mid].cls; break; }
-        if (mm < m) lo = mid + 1; else hi = mid - 1;
+        const uint64_t mm = lk[mid].mask;
+        if (mm == msk_r[k]) { cls = lk[mid].cls; break; }
+        if (mm < msk_r[k]) lo = mid + 1; else hi = mid - 1;
       }
     }
-    cls_s[i] = static_cast<int16_t>(cls);
+    cls_r[k] = cls;
   }
-  if (tid < nc) base[tid] = a.classes[tid].cell_off;
+  if (tid < nc) base[tid] = cl[tid].cell_off;
+  for (int z = tid; z < 4 * kSmallCommitClasses; z += 256) wc[z / kSmallCommitClasses][z % kSmallCommitClasses] = 0;
   __syncthreads();
-  for (int i0 = 0; i0 < total; i0 += 256) {
-    const int i = i0 + tid;
-    const int cls = i < total ? cls_s[i] : -1;
-    for (int z = tid; z < 4 * kSmallCommitClasses; z += 256) wc[z / kSmallCommitClasses][z % kSmallCommitClasses] = 0;
-    __syncthreads();
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (256 * k >= total) break;
+    const int cls = cls_r[k];
     int rank = 0;
     uint64_t active = ballot(cls >= 0);
     while (active) {
@@ -215,20 +239,23 @@ KVATTN_DEV void commit_small(const CsrArgs& a) {
     if (cls >= 0) {
       int dst = base[cls] + rank;
       for (int w2 = 0; w2 < w; ++w2) dst += wc[w2][cls];
-      const int s = i / a.n_kv, j = i % a.n_kv;
-      const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
       if (dst < a.csr_cap) {
-        a.csr_cell[dst] = j;
-        a.csr_pos[dst] = a.cpos[idx];
-        a.csr_mask[dst] = a.cmask[idx];
+        a.csr_cell[dst] = (tid + 256 * k) % a.n_kv;
+        a.csr_pos[dst] = pos_r[k];
+        a.csr_mask[dst] = msk_r[k];
       }
     }
     __syncthreads();
-    if (tid < nc) base[tid] += wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
+    // the thread that folds class tid's counts into its offset also clears
+    // them (only classes < nc are ever counted)
+    if (tid < nc) {
+      base[tid] += wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
+      wc[0][tid] = wc[1][tid] = wc[2][tid] = wc[3][tid] = 0;
+    }
     __syncthreads();
   }
   for (int c = 0; c < nc; ++c) {
-    const ClassInfo ci = a.classes[c];
+    const ClassInfo ci = cl[c];
     const int nt = (ci.n_cells + kTileCells - 1) / kTileCells;
     for (int k = w; k < nt; k += 4) {
       const int j = k * kTileCells + lane;
@@ -245,15 +272,24 @@ KVATTN_DEV void commit_small(const CsrArgs& a) {
 }
 
 bool commit_is_small(const CsrArgs& a) {
-  return static_cast<int64_t>(a.n_stream) * a.n_kv <= kSmallCommitCells && a.n_classes <= kSmallCommitClasses;
+  return static_cast<int64_t>(a.n_stream) * a.n_kv <= kSmallCommitCells && a.n_classes <= kSmallCommitClasses &&
+         a.n_lookup <= kSmallCommitClasses && a.n_stream <= kSmallCommitStreams;
 }
 
-// the store grid plus one trailing x-block; that block's (y, z) = (0, 0)
-// instance runs the small commit
+// The store grid plus one trailing x-block; that block's (y, z) = (0, 0)
+// instance runs the small commit.  The other (y, z) = (0, 0) blocks also copy
+// the plan from pinned host memory into the device plan arena, which the
+// attention launches read after this kernel.
 __global__ __launch_bounds__(256) void k_store_commit(StoreArgs a, CsrArgs c) {
   if (blockIdx.x == gridDim.x - 1) {
     if (blockIdx.y == 0 && blockIdx.z == 0) commit_small(c);
     return;
+  }
+  if (blockIdx.y == 0 && blockIdx.z == 0 && c.plan_n16 > 0) {
+    const u32x4* src = static_cast<const u32x4*>(c.plan_src);
+    u32x4* dst = static_cast<u32x4*>(c.plan_dst);
+    const int stride = (gridDim.x - 1) * blockDim.x;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < c.plan_n16; i += stride) dst[i] = src[i];
   }
   store_rows(a);
 }

@@ -37,6 +37,13 @@ struct CsrArgs {
   int32_t* tile_min;          // per 64-cell tile of each class: smallest / largest position
   int32_t* tile_max;
   int32_t max_class_tiles;
+  int32_t n_lookup;           // lookup entries (lookup_off[n_stream])
+  // fused path only: the plan still sits in pinned host memory (classes,
+  // lookup, lookup_off, updates point into it); the store workgroups copy
+  // its plan_n16 16-byte units to the device plan arena
+  const void* plan_src;
+  void* plan_dst;
+  int32_t plan_n16;
 };
 
 struct AttnArgs {

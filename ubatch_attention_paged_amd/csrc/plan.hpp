@@ -19,8 +19,9 @@ constexpr int kMaxLayersPerLaunch = 32;
 constexpr int kMaxClasses = 1024;      // per ubatch; extra sequence sets are merged
 constexpr int kSegCells = 64;          // cells per counting segment (one wavefront)
 constexpr int kTileCells = 64;         // cells per attention tile; chunk starts are multiples of it
-constexpr int kSmallCommitCells = 8192;   // commits of at most this many (stream, cell) pairs below n_kv
-constexpr int kSmallCommitClasses = 64;   // and this many classes run in one workgroup beside the stores
+constexpr int kSmallCommitCells = 4096;   // commits of at most this many (stream, cell) pairs below n_kv
+constexpr int kSmallCommitClasses = 64;   // and this many classes (and lookup entries)
+constexpr int kSmallCommitStreams = 64;   // and streams run in one workgroup beside the stores
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
 constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV head) per MFMA item
 // Workgroups a split-K launch should reach before its items are cut finer
