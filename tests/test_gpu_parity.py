@@ -245,3 +245,43 @@ def test_cache_full_and_empty_batch_on_gpu():
     st, ubs, _ = ctx.split(1)
     assert st == K.KVATTN_NO_SLOT
     ctx.close()
+
+
+@pytest.mark.parametrize("needle_pos", [40, 100, 180])
+def test_mfma_running_max_jumps(needle_pos):
+    """A prompt whose keys are small except one large key at a cell in the
+    second 32-cell block of a tile: for the queries aligned with it, that
+    block's maximum exceeds the running maximum by far more than the lazy
+    rescale slack, after the first block of the same tile was already
+    weighted.  Against the oracle on the same inputs (matrix-core path)."""
+    from oracle import OracleEngine
+    from ubatch_attention_paged_amd.harness import decode
+    dev = torch.device("cuda:0")
+    H, Hk, D, T = 16, 8, 128, 200
+    E = Hk * D
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((T, H * D)).astype(np.float32)
+    k = (rng.standard_normal((T, E)) * 0.1).astype(np.float32)
+    v = rng.standard_normal((T, E)).astype(np.float32)
+    u = rng.standard_normal(E).astype(np.float32)
+    # each head's slice of the needle has norm ~80: its score is ~N(0, 10^2) in
+    # log2 units, so for a good share of queries it jumps past every earlier
+    # score by more than 2^8 (the F16 rounding of q moves such a score by
+    # ~0.005, well inside the tolerance)
+    k[needle_pos] = 226.0 * u / np.linalg.norm(u)
+    pos = np.arange(T, dtype=np.int32)
+    seqs = [[0]] * T
+    ctx = K.Context(1, H, Hk, D, kv_size=512, n_seq_max=1, device="cuda:0")
+    Tt = lambda a: [torch.from_numpy(np.ascontiguousarray(a)).to(dev)]
+    st, ubs, outs = decode(ctx, T, pos, seqs, None, Tt(k), Tt(v), Q=Tt(q))
+    assert st == 0 and len(ubs) == 1
+    got = outs[0].cpu().numpy().astype(np.float64)
+    ctx.close()
+    eng = OracleEngine(1, H, Hk, D, 512, 1, 1, 2048, 2048, True, layers=[0])
+    _, oubs, _ = eng.split(T, pos, [tuple(s) for s in seqs], None)
+    ref = np.zeros((T, H * D))
+    for ub in oubs:
+        eng.commit(ub)
+        eng.store(ub, 0, k[ub.src], v[ub.src])
+        ref[ub.src] = eng.attend(ub, 0, q[ub.src])
+    assert_parity(got, ref, tag=f"needle at {needle_pos}")

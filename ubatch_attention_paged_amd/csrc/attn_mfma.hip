@@ -194,10 +194,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min);
 
     // The tile is two 32-cell blocks, each with its own online-softmax step.
-    // Source order interleaves them so that the matrix core always has
-    // independent work next to the vector ALU's: S(1) is issued beside the
-    // exponentials of block 0 and PV(0) beside those of block 1 (the
-    // rescale branches sit between these regions, not inside them).
+    // Source order interleaves them so that the matrix core has independent
+    // work next to the vector ALU's: S(1) is issued beside the exponentials
+    // of block 0, PV(0) beside the mask and maximum of block 1.  PV(0) must
+    // be accumulated before block 1's step may rescale O: its weights are
+    // relative to the maximum in force before that step.
     float rs = 0.f;    // this lane's share of the row sum of this tile
     auto s_block = [&](int kb) {
       floatx16 acc;
@@ -276,8 +277,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     floatx16 s1 = s_block(1);
     half8 p0[2], p1[2];
     weights(s0, mu0, p0);
-    const float mu1 = max_block(1, s1);
     pv_block(0, p0);
+    const float mu1 = max_block(1, s1);
     weights(s1, mu1, p1);
     pv_block(1, p1);
     rs += __shfl_xor(rs, 32);
