@@ -285,3 +285,38 @@ def test_mfma_running_max_jumps(needle_pos):
         eng.store(ub, 0, k[ub.src], v[ub.src])
         ref[ub.src] = eng.attend(ub, 0, q[ub.src])
     assert_parity(got, ref, tag=f"needle at {needle_pos}")
+
+
+@pytest.mark.parametrize("needle_pos", [3, 150, 199])
+def test_decode_running_max_jumps(needle_pos):
+    """The same kind of large key, read by single-token decode queries (the
+    fp32 vector-ALU split-K path) against the oracle."""
+    from oracle import OracleEngine
+    from ubatch_attention_paged_amd.harness import decode
+    dev = torch.device("cuda:0")
+    H, Hk, D, T, S = 16, 8, 128, 200, 6
+    E = Hk * D
+    rng = np.random.default_rng(22)
+    k = (rng.standard_normal((T + S, E)) * 0.1).astype(np.float32)
+    v = rng.standard_normal((T + S, E)).astype(np.float32)
+    q = rng.standard_normal((S, H * D)).astype(np.float32)
+    u = rng.standard_normal(E).astype(np.float32)
+    k[needle_pos] = 226.0 * u / np.linalg.norm(u)
+    ctx = K.Context(1, H, Hk, D, kv_size=512, n_seq_max=1, device="cuda:0")
+    eng = OracleEngine(1, H, Hk, D, 512, 1, 1, 2048, 2048, True, layers=[0])
+    Tt = lambda a: [torch.from_numpy(np.ascontiguousarray(a)).to(dev)]
+    decode(ctx, T, np.arange(T), [[0]] * T, None, Tt(k[:T]), Tt(v[:T]))
+    _, oubs, _ = eng.split(T, np.arange(T, dtype=np.int32), [(0,)] * T, None)
+    for ub in oubs:
+        eng.commit(ub, build_mask=False)
+        eng.store(ub, 0, k[:T][ub.src], v[:T][ub.src])
+    for s in range(S):
+        p = T + s
+        st, ubs, outs = decode(ctx, 1, [p], [[0]], None, Tt(k[p:p + 1]), Tt(v[p:p + 1]), Q=Tt(q[s:s + 1]))
+        got = outs[0].cpu().numpy().astype(np.float64)
+        _, oubs, _ = eng.split(1, np.array([p], np.int32), [(0,)], None)
+        eng.commit(oubs[0])
+        eng.store(oubs[0], 0, k[p:p + 1], v[p:p + 1])
+        ref = eng.attend(oubs[0], 0, q[s:s + 1])
+        assert_parity(got, ref, tag=f"decode step {s}, needle at {needle_pos}")
+    ctx.close()
