@@ -41,9 +41,10 @@ KVATTN_DEV float dot2_sum(half2v h, float acc) {
 constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag the true max
 
 template <int D, int G>
-__global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
-  constexpr int QT = kMfmaRowsPerItem / G;        // queries per item (128 rows)
-  static_assert(kMfmaRowsPerItem == 128, "4 wavefronts x 32 rows");
+__global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(AttnArgs a) {
+  constexpr int RB = kMfmaRowBlocks;              // 32-row blocks per wavefront
+  constexpr int QT = kMfmaRowsPerItem / G;        // queries per item
+  static_assert(kMfmaRowsPerItem == 128 * RB, "4 wavefronts x RB x 32 rows");
   constexpr int KT = kTileCells;                  // cells per tile (64)
   constexpr int DP = D < 32 ? 32 : D;             // O^T rows, padded to a 32-row block
   constexpr int KSK = D + 8;                      // K row stride (halfs): rows shift 4 banks (16 B reads)
@@ -75,35 +76,49 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
   const uint32_t row_bytes = static_cast<uint32_t>(E) * 2;
   const uint32_t sbase_bytes = static_cast<uint32_t>(ci.stream) * static_cast<uint32_t>(a.kv_size) * row_bytes;
 
-  // this lane's query row
-  const int r = 32 * w + (lane & 31);
-  const int hg = r / QT, t = r % QT;
-  const bool qvalid = t < it.n_q;
-  const SlotInfo si = a.slots[a.qlist[it.q_off + (qvalid ? t : 0)]];
-  const int h = kvh * G + hg;
+  // this lane's query rows: row block b of wavefront w is rows
+  // 32 * (w * RB + b) .. +31, the lane owning row lane % 32 of it
+  int t_r[RB], h_r[RB], pos_lim[RB], qseq[RB];
+  bool qvalid[RB];
+  SlotInfo si[RB];
+  bool any_row = false;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int r = 32 * (w * RB + b) + (lane & 31);
+    const int hg = r / QT;
+    t_r[b] = r % QT;
+    qvalid[b] = t_r[b] < it.n_q;
+    si[b] = a.slots[a.qlist[it.q_off + (qvalid[b] ? t_r[b] : 0)]];
+    h_r[b] = kvh * G + hg;
+    pos_lim[b] = a.causal ? si[b].pos : INT32_MAX - 1;   // largest visible cell position
+    qseq[b] = si[b].seq0;
+    any_row |= qvalid[b];
+  }
+  const bool wave_rows = ballot(any_row) != 0ULL;   // wave-uniform: padding-only waves skip the math
 
   // B operand of S^T = K Q^T: q[row][16*ks + 8*half + 0..7], scaled, F16
-  half8 qb[D / 16];
-  {
-    const float* qp = a.q[il] + static_cast<int64_t>(si.q_row) * H * D + h * D + 8 * half_id;
+  half8 qb[RB][D / 16];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const float* qp = a.q[il] + static_cast<int64_t>(si[b].q_row) * H * D + h_r[b] * D + 8 * half_id;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const float4 x0 = qvalid ? *reinterpret_cast<const float4*>(qp + 16 * ks) : make_float4(0, 0, 0, 0);
-      const float4 x1 = qvalid ? *reinterpret_cast<const float4*>(qp + 16 * ks + 4) : make_float4(0, 0, 0, 0);
-      qb[ks][0] = static_cast<_Float16>(x0.x * a.scale_log2e);
-      qb[ks][1] = static_cast<_Float16>(x0.y * a.scale_log2e);
-      qb[ks][2] = static_cast<_Float16>(x0.z * a.scale_log2e);
-      qb[ks][3] = static_cast<_Float16>(x0.w * a.scale_log2e);
-      qb[ks][4] = static_cast<_Float16>(x1.x * a.scale_log2e);
-      qb[ks][5] = static_cast<_Float16>(x1.y * a.scale_log2e);
-      qb[ks][6] = static_cast<_Float16>(x1.z * a.scale_log2e);
-      qb[ks][7] = static_cast<_Float16>(x1.w * a.scale_log2e);
+      const float4 x0 = qvalid[b] ? *reinterpret_cast<const float4*>(qp + 16 * ks) : make_float4(0, 0, 0, 0);
+      const float4 x1 = qvalid[b] ? *reinterpret_cast<const float4*>(qp + 16 * ks + 4) : make_float4(0, 0, 0, 0);
+      qb[b][ks][0] = static_cast<_Float16>(x0.x * a.scale_log2e);
+      qb[b][ks][1] = static_cast<_Float16>(x0.y * a.scale_log2e);
+      qb[b][ks][2] = static_cast<_Float16>(x0.z * a.scale_log2e);
+      qb[b][ks][3] = static_cast<_Float16>(x0.w * a.scale_log2e);
+      qb[b][ks][4] = static_cast<_Float16>(x1.x * a.scale_log2e);
+      qb[b][ks][5] = static_cast<_Float16>(x1.y * a.scale_log2e);
+      qb[b][ks][6] = static_cast<_Float16>(x1.z * a.scale_log2e);
+      qb[b][ks][7] = static_cast<_Float16>(x1.w * a.scale_log2e);
     }
   }
   if (D < DP) {   // columns D .. DP-1 of every V row are read as O^T rows >= D: keep them zero
     for (int i = tid; i < 2 * KT * (DP - D); i += 256) {
-      const int b = i / (KT * (DP - D)), rem = i % (KT * (DP - D));
-      Vs[b][(rem / (DP - D)) * KSV + D + rem % (DP - D)] = static_cast<_Float16>(0.f);
+      const int bb = i / (KT * (DP - D)), rem = i % (KT * (DP - D));
+      Vs[bb][(rem / (DP - D)) * KSV + D + rem % (DP - D)] = static_cast<_Float16>(0.f);
     }
   }
 
@@ -117,12 +132,17 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     ntile = wave_max_i(last) + 1;
   }
 
-  floatx16 oacc[DP / 32];
+  floatx16 oacc[RB][DP / 32];
+  float m_run[RB], l_run[RB];
 #pragma unroll
-  for (int db = 0; db < DP / 32; ++db)
+  for (int b = 0; b < RB; ++b) {
+    m_run[b] = -INFINITY;
+    l_run[b] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[b][db][i] = 0.f;
+  }
 
   // loader geometry: thread -> (row0 + p * ROW_STEP, 16 B segment seg)
   const int seg = tid % SEGS;
@@ -163,8 +183,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 
   const int s16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
-  const int qpos = si.pos, qseq = si.seq0;
-  const int pos_lim = a.causal ? qpos : INT32_MAX - 1;   // largest visible cell position
   for (int i = 0; i < ntile; ++i) {
     const int buf = i & 1;
     // stage tile i
@@ -187,40 +205,46 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) cnext[p] = (loader && i + 2 < ntile) ? cell_at(i + 2, row0 + p * ROW_STEP) : -1;
     }
+    if (!wave_rows) continue;
 
     const int nk = min(KT, it.c1 - (it.c0 + i * KT));
     const int tmin = a.tile_min[tb + i], tmax = a.tile_max[tb + i];
     if (a.causal && tmin > it.qpos_max) continue;
     const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min);
 
-    // The tile is two 32-cell blocks, each with its own online-softmax step.
-    // Source order interleaves them so that the matrix core has independent
-    // work next to the vector ALU's: S(1) is issued beside the exponentials
-    // of block 0, PV(0) beside the mask and maximum of block 1.  PV(0) must
-    // be accumulated before block 1's step may rescale O: its weights are
-    // relative to the maximum in force before that step.
-    float rs = 0.f;    // this lane's share of the row sum of this tile
-    auto s_block = [&](int kb) {
-      floatx16 acc;
+    // The tile is two 32-cell blocks, each with its own online-softmax step
+    // per row block.  Every K or V fragment read from LDS feeds the RB row
+    // blocks' MFMAs.  Source order interleaves matrix and vector work: S(1)
+    // is issued beside the exponentials of block 0, PV(0) beside the mask
+    // and maximum of block 1.  PV(0) is accumulated before block 1's step may
+    // rescale O: its weights are relative to the maximum in force before.
+    float rs[RB];      // this lane's share of each row's sum over this tile
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int b = 0; b < RB; ++b) rs[b] = 0.f;
+    auto s_block = [&](int kb, floatx16 (&acc)[RB]) {
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         const half8 ka =
             *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + (lane & 31)) * KSK + 16 * ks + 8 * half_id]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[b][ks], acc[b], 0, 0, 0);
       }
-      return acc;
     };
-    // mask + running-max update of one block; returns the offset to subtract
-    auto max_block = [&](int kb, floatx16& sb) {
+    // mask + running-max update of one block of row block b; returns the
+    // offset to subtract
+    auto max_block = [&](int b, int kb, floatx16& sb) {
       if (!full) {
         // branch-free: cells past the list end hold position INT32_MAX and an
         // empty sequence set, so both tests remove them
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb * 32 + acc_row(e, lane);
-          const bool vis = (kpos_s[buf][key] <= pos_lim) & static_cast<bool>((kmask_s[buf][key] >> qseq) & 1ULL);
+          const bool vis =
+              (kpos_s[buf][key] <= pos_lim[b]) & static_cast<bool>((kmask_s[buf][key] >> qseq[b]) & 1ULL);
           sb[e] = vis ? sb[e] : -INFINITY;
         }
       }
@@ -229,28 +253,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sb[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool grow = mx > m_run + kRescaleSlack;     // false while the row sees nothing
+      const bool grow = mx > m_run[b] + kRescaleSlack;     // false while the row sees nothing
       if (ballot(grow)) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-        l_run *= alpha;
-        rs *= alpha;
+        const float m_new = grow ? mx : m_run[b];
+        const float alpha = m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[b] - m_new);
+        l_run[b] *= alpha;
+        rs[b] *= alpha;
 #pragma unroll
         for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-        m_run = m_new;
+          for (int e = 0; e < 16; ++e) oacc[b][db][e] *= alpha;
+        m_run[b] = m_new;
       }
-      return m_run == -INFINITY ? 0.f : m_run;
+      return m_run[b] == -INFINITY ? 0.f : m_run[b];
     };
     // F16 weights of one block (B operand of the PV product) and their sum
-    auto weights = [&](const floatx16& sb, float m_use, half8 (&pb)[2]) {
+    auto weights = [&](int b, const floatx16& sb, float m_use, half8 (&pb)[2]) {
 #pragma unroll
       for (int e = 0; e < 16; e += 2) {
         half2v ph;
         ph[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sb[e] - m_use));
         ph[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sb[e + 1] - m_use));
-        rs = dot2_sum(ph, rs);          // the row sum sees the F16 weights the PV product sees
+        rs[b] = dot2_sum(ph, rs[b]);     // the row sum sees the F16 weights the PV product sees
         pb[e >> 3][e & 7] = ph[0];
         pb[e >> 3][(e & 7) + 1] = ph[1];
       }
@@ -258,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
     // O^T += V^T P^T: source lane s of each 16-lane group points at cell row
     // key0 + s/4, column dsub + 4*(s%4); lane gets cells key0..key0+3 of
     // column db*32 + lane%32 (and key0+8.. for the upper four k-values)
-    auto pv_block = [&](int kb, const half8 (&pb)[2]) {
+    auto pv_block = [&](int kb, const half8 (&pb)[RB][2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int key0 = kb * 32 + 16 * st + 4 * half_id;
@@ -268,52 +292,66 @@ __global__ __launch_bounds__(256, 2) void k_attn_mfma(AttnArgs a) {
           const half4 lo = lds_read_tr16(vb + db * 32);
           const half4 hi = lds_read_tr16(vb + db * 32 + 8 * KSV);
           const half8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[st], oacc[db], 0, 0, 0);
+#pragma unroll
+          for (int b = 0; b < RB; ++b)
+            oacc[b][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[b][st], oacc[b][db], 0, 0, 0);
         }
       }
     };
-    floatx16 s0 = s_block(0);
-    const float mu0 = max_block(0, s0);
-    floatx16 s1 = s_block(1);
-    half8 p0[2], p1[2];
-    weights(s0, mu0, p0);
+    floatx16 s0[RB], s1[RB];
+    float mu[RB];
+    half8 p0[RB][2], p1[RB][2];
+    s_block(0, s0);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) mu[b] = max_block(b, 0, s0[b]);
+    s_block(1, s1);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) weights(b, s0[b], mu[b], p0[b]);
     pv_block(0, p0);
-    const float mu1 = max_block(1, s1);
-    weights(s1, mu1, p1);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) mu[b] = max_block(b, 1, s1[b]);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) weights(b, s1[b], mu[b], p1[b]);
     pv_block(1, p1);
-    rs += __shfl_xor(rs, 32);
-    l_run += rs;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      rs[b] += __shfl_xor(rs[b], 32);
+      l_run[b] += rs[b];
+    }
   }
 
-  if (!qvalid) return;
-  if (it.prow < 0) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    float* op = a.o[il] + static_cast<int64_t>(si.out_row) * H * D + h * D;
 #pragma unroll
-    for (int db = 0; db < DP / 32; ++db)
+  for (int b = 0; b < RB; ++b) {
+    if (!qvalid[b]) continue;
+    if (it.prow < 0) {
+      const float inv = l_run[b] > 0.f ? 1.f / l_run[b] : 0.f;
+      float* op = a.o[il] + static_cast<int64_t>(si[b].out_row) * H * D + h_r[b] * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + acc_row(4 * g4, lane);
-        if (d < D)
-          *reinterpret_cast<float4*>(op + d) =
-              make_float4(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv, oacc[db][4 * g4 + 2] * inv,
-                          oacc[db][4 * g4 + 3] * inv);
+      for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + acc_row(4 * g4, lane);
+          if (d < D)
+            *reinterpret_cast<float4*>(op + d) =
+                make_float4(oacc[b][db][4 * g4] * inv, oacc[b][db][4 * g4 + 1] * inv, oacc[b][db][4 * g4 + 2] * inv,
+                            oacc[b][db][4 * g4 + 3] * inv);
+        }
+    } else {
+      const int64_t row = static_cast<int64_t>(il) * a.rows_per_layer + it.prow + t_r[b];
+      float* pp = a.part_acc + row * H * D + h_r[b] * D;
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + acc_row(4 * g4, lane);
+          if (d < D)
+            *reinterpret_cast<float4*>(pp + d) = make_float4(oacc[b][db][4 * g4], oacc[b][db][4 * g4 + 1],
+                                                             oacc[b][db][4 * g4 + 2], oacc[b][db][4 * g4 + 3]);
+        }
+      if (half_id == 0) {
+        a.part_ml[(row * H + h_r[b]) * 2] = m_run[b];
+        a.part_ml[(row * H + h_r[b]) * 2 + 1] = l_run[b];
       }
-  } else {
-    const int64_t row = static_cast<int64_t>(il) * a.rows_per_layer + it.prow + t;
-    float* pp = a.part_acc + row * H * D + h * D;
-#pragma unroll
-    for (int db = 0; db < DP / 32; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d = db * 32 + acc_row(4 * g4, lane);
-        if (d < D)
-          *reinterpret_cast<float4*>(pp + d) =
-              make_float4(oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]);
-      }
-    if (half_id == 0) {
-      a.part_ml[(row * H + h) * 2] = m_run;
-      a.part_ml[(row * H + h) * 2 + 1] = l_run;
     }
   }
 }

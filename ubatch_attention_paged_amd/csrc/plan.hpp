@@ -23,7 +23,8 @@ constexpr int kSmallCommitCells = 4096;   // commits of at most this many (strea
 constexpr int kSmallCommitClasses = 64;   // and this many classes (and lookup entries)
 constexpr int kSmallCommitStreams = 64;   // and streams run in one workgroup beside the stores
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
-constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV head) per MFMA item
+constexpr int kMfmaRowBlocks = 1;      // 32-row blocks per wavefront of the matrix-core kernel
+constexpr int kMfmaRowsPerItem = 128 * kMfmaRowBlocks;  // query rows (queries x heads of one KV head) per item
 // Workgroups a split-K launch should reach before its items are cut finer
 // (256 CUs; the vector-ALU kernel keeps 5 workgroups per CU, the
 // matrix-core kernel 2).  Measured on decode steps: long items win over a
