@@ -320,3 +320,20 @@ def test_decode_running_max_jumps(needle_pos):
         ref = eng.attend(oubs[0], 0, q[s:s + 1])
         assert_parity(got, ref, tag=f"decode step {s}, needle at {needle_pos}")
     ctx.close()
+
+
+@pytest.mark.parametrize("name", ["prefill", "cb_decode", "mixed", "prefix"])
+def test_noncausal_parity(name):
+    """causal = 0: cells at later positions (already stored) are visible too,
+    in both attention kernels and the split-K merge."""
+    import dataclasses
+    wl = dataclasses.replace(small(name), causal=False)
+    layers = list(range(wl.n_layer))
+    print(f"[gpu] non-causal {name}", flush=True)
+    _, ref, _, _ = oracle_run(wl, layers)
+    _, got = gpu_run(wl, layers)
+    worst = 0.0
+    for key in ref:
+        ma, _ = assert_parity(got[key], ref[key], tag=f"non-causal {name} {key}")
+        worst = max(worst, ma)
+    assert worst < (2e-5 if name == "cb_decode" else 1.6e-3), worst

@@ -285,3 +285,42 @@ def test_workload_context_total_matches_page4_duty_cycle():
     assert int(measured.pos.sum()) == 8 * 5568
     assert 5568 / (8 * 2048) == pytest.approx(0.34, abs=0.005)
     assert (20 + 2000) / (2 * 2000) == pytest.approx(0.505)
+
+
+def test_single_ubatch_noncausal_equals_torch_sdpa():
+    """Non-causal attention ("llama.cpp and the ubatch", "The mask is doing
+    the work": the position test applies only under causal attention): one
+    sequence stored as one ubatch sees every one of its cells, which is
+    torch's scaled_dot_product_attention without a mask."""
+    import dataclasses
+    torch = pytest.importorskip("torch")
+    wl = W.qwen_prefill(n_prompt=150, n_layer=1, kv_size=256, n_batch=256, n_ubatch=256)
+    wl = dataclasses.replace(wl, causal=False)
+    wl.n_head, wl.n_head_kv, wl.head_dim = 8, 2, 32
+    got, _ = run_oracle(wl)
+    assert len(wl.batches) == 1
+    q = wl.tensor(0, 0, W.KIND_Q)
+    k = f16_round(wl.tensor(0, 0, W.KIND_K)).astype(np.float64)
+    v = f16_round(wl.tensor(0, 0, W.KIND_V)).astype(np.float64)
+    T, d, H, Hk = q.shape[0], wl.head_dim, wl.n_head, wl.n_head_kv
+    qt = torch.tensor(q, dtype=torch.float64).view(T, H, d).transpose(0, 1)
+    kt = torch.tensor(k).view(T, Hk, d).transpose(0, 1).repeat_interleave(H // Hk, dim=0)
+    vt = torch.tensor(v).view(T, Hk, d).transpose(0, 1).repeat_interleave(H // Hk, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=False)
+    ref = ref.transpose(0, 1).reshape(T, H * d).numpy()
+    np.testing.assert_allclose(got[(0, 0)], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_noncausal_multi_sequence_matches_brute_force():
+    """Non-causal, several sequences, one ubatch per call: every query sees
+    all cells of its sequence stored so far, its own call included."""
+    import dataclasses
+    wl = W.prefix_decode(n_seq=3, prefix=5, private=4, n_layer=1, kv_size=64)
+    wl = dataclasses.replace(wl, causal=False)
+    wl.n_head, wl.n_head_kv, wl.head_dim = 4, 2, 8
+    for bt in wl.batches:
+        bt.measured = True
+    got, _ = run_oracle(wl)
+    ref = brute(wl)
+    for key in ref:
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-12, atol=1e-12)
