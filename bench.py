@@ -250,6 +250,92 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
 
 
 # ---------------------------------------------------------------------------
+# mixed prefill + decode (non-unified cache, split_equal)
+
+def bench_mixed(wl, dev, steps, warmup, layer_chunk):
+    """Every measured call of the mixed workload (one decode token per decoder
+    plus prompt chunks, split_equal into ubatches) per step; the prompts and
+    the decoders' new tokens are retired between steps.  Ubatches whose
+    sequences each contribute one slot run on the vector-ALU decode kernel
+    (HBM-bound); prompt-chunk ubatches on the matrix cores."""
+    import torch
+    from ubatch_attention_paged_amd.harness import decode
+    from ubatch_attention_paged_amd import SeqIds
+    ctx = make_ctx(wl, dev, layer_chunk)
+    layers = list(range(wl.n_layer))
+    log(f"[bench] mixed: filling the decoders' contexts ({wl.note})")
+    t0 = time.perf_counter()
+    ctx_len = {}
+    for b, bt in enumerate(wl.batches):
+        if bt.measured:
+            continue
+        K, V, _ = gen_tensors(wl, b, layers, False, dev)
+        st, _, _ = decode(ctx, bt.n_tokens, bt.pos, bt.seq_ids, bt.output, list(K), list(V))
+        assert st == 0
+        del K, V
+        for p, s in zip(bt.pos, bt.seq_ids):
+            ctx_len[s[0]] = max(ctx_len.get(s[0], 0), int(p) + 1)
+    meas = [b for b, bt in enumerate(wl.batches) if bt.measured]
+    data = {b: gen_tensors(wl, b, layers, True, dev) for b in meas}
+    sids = {b: SeqIds(wl.batches[b].seq_ids) for b in meas}
+    torch.cuda.synchronize()
+    log(f"[bench] mixed: ready in {time.perf_counter() - t0:.1f}s, {len(meas)} measured calls")
+    prompts = sorted({s[0] for b in meas for s in wl.batches[b].seq_ids} - set(ctx_len))
+    HD = wl.n_head * wl.head_dim
+    outs = torch.empty((len(layers), wl.n_ubatch, HD), dtype=torch.float32, device=dev)
+    runner = Runner(ctx, layer_chunk)
+
+    def step(timed):
+        for k in prompts:
+            ctx.seq_rm(k)
+        for d, n in ctx_len.items():
+            ctx.seq_rm(d, n, -1)
+        shapes = []
+        for b in meas:
+            bt = wl.batches[b]
+            K, V, Q = data[b]
+            for ub in runner.run_batch(bt.n_tokens, bt.pos, sids[b], bt.output, K, V, Q, outs, timed):
+                shapes.append((ub.n_seq_tokens, np.asarray(ub.pos, np.int64).copy()))
+        return shapes
+
+    for _ in range(warmup):
+        shapes = step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    chunk_calls = (wl.n_layer + layer_chunk - 1) // layer_chunk
+    per_call = runner.attend_by_position(len(shapes) * chunk_calls)
+    per_ub = [sum(per_call[u * chunk_calls:(u + 1) * chunk_calls]) for u in range(len(shapes))]
+    single = [u for u, (nst, _) in enumerate(shapes) if nst == 1]
+    chunks = [u for u in range(len(shapes)) if u not in single]
+    row = 2 * wl.n_head_kv * wl.head_dim * 2
+    # one sequence id per slot, contiguous positions from 0: a slot at
+    # position p sees p + 1 cells, none shared with another slot
+    cells = lambda u: float((shapes[u][1] + 1).sum())
+    ms_single = sum(per_ub[u] for u in single)
+    ms_chunks = sum(per_ub[u] for u in chunks)
+    kv_bytes = sum(cells(u) for u in single) * row * wl.n_layer
+    qo_bytes = sum(2 * len(shapes[u][1]) * HD * 4 * wl.n_layer for u in single)
+    flops = sum(cells(u) for u in chunks) * 4.0 * HD * wl.n_layer
+    tokens = sum(wl.batches[b].n_tokens for b in meas)
+    res = dict(workload=wl.note, tokens_per_s=round(tokens * steps / wall, 1), ms_per_step=round(1e3 * wall / steps, 4),
+               tokens_per_step=tokens, ubatches_per_step=len(shapes))
+    if single:
+        gbs = (kv_bytes + qo_bytes) / (ms_single * 1e-3) / 1e9
+        res["single_token_ubatches"] = dict(count=len(single), attend_ms=round(ms_single, 4),
+                                            kv_read_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    if chunks:
+        tf = flops / (ms_chunks * 1e-3) / 1e12
+        res["prompt_chunk_ubatches"] = dict(count=len(chunks), attend_ms=round(ms_chunks, 4),
+                                            tflops=round(tf, 1), mfma_frac=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
+    ctx.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # oracle on the host cores
 
 def cpu_baseline(wl, budget_s=25.0):
@@ -318,6 +404,7 @@ def main():
     ap.add_argument("--per-layer", action="store_true", help="also time one call per layer")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode workloads (for profiling their kernels alone)")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode workload")
     ap.add_argument("--decode-workload", choices=["cb_decode", "prefix_decode"], action="append",
                     help="restrict the decode runs to this workload (repeatable)")
     args = ap.parse_args()
@@ -393,6 +480,11 @@ def main():
                 # FETCH_SIZE / WRITE_SIZE summary of this workload (None if stale)
                 dec[name]["traffic_k_attn_valu"] = committed_traffic("k_attn_valu", "attn_valu.hip")
         line["decode"] = dec
+    if not args.no_mixed:
+        m = bench_mixed(W.mixed(), dev, max(2, args.steps // 2), 1, args.layer_chunk)
+        log(f"[bench] mixed: {m['tokens_per_s']:,.0f} tok/s; " + "; ".join(
+            f"{k}: {v}" for k, v in m.items() if k.endswith("_ubatches")))
+        line["mixed"] = m
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(wl)
