@@ -8,7 +8,8 @@
  *
  *   1. a batch of token slots (position, sequence-id set, output flag) is
  *      validated and split into ubatches -- split_simple for one stream,
- *      split_equal for several ("Batch、Ubatch 与解码主循环", Part C);
+ *      split_equal for several, or split_seq on request ("Batch、Ubatch 与解码
+ *      主循环", Part C);
  *   2. every slot of every ubatch is given a cache cell, all-or-nothing for
  *      the batch (same page, Part C "strategy choice"; Part F);
  *   3. each ubatch writes its K/V rows, rounded to F16, into per-layer
@@ -86,7 +87,20 @@ typedef struct kvattn_params {
   int32_t device;         /* HIP device ordinal of every device pointer */
   int32_t attend_layers;  /* scheduling hint, no effect on results: layers per kvattn_attend
                              call the caller will use (0 = 1); sizes the work items */
+  int32_t split_mode;     /* KVATTN_SPLIT_*: how kvattn_split cuts a batch into ubatches */
 } kvattn_params;
+
+/* Batch -> ubatch split strategies ("Batch、Ubatch 与解码主循环", Part C).
+ * AUTO is the init_batch choice: split_simple for one stream, split_equal
+ * (n_ubatch, sequential) for several.  SEQ is split_seq: every ubatch holds
+ * the slots of one sequence set only (the set of the first unused slot, its
+ * unused slots in submission order, at most n_ubatch). */
+enum {
+  KVATTN_SPLIT_AUTO = 0,
+  KVATTN_SPLIT_SIMPLE = 1,  /* the next <= n_ubatch slots, sequence ids ignored */
+  KVATTN_SPLIT_EQUAL = 2,   /* equal slot counts from pairwise-disjoint sequence sets */
+  KVATTN_SPLIT_SEQ = 3
+};
 
 /* A batch as submitted: llama_batch without token/embd ("Batch、Ubatch 与解码主循环",
  * Part A).  pos, seq_id and output may each be NULL and are then filled:

@@ -31,14 +31,14 @@ library special case and invariants in ``tests/test_oracle_*.py``.
 """
 
 from .batching import (clamp_params, fill_batch, split_simple, split_equal,
-                       split_batch, output_ids, SplitError)
+                       split_batch, split_seq, output_ids, SplitError)
 from .kvcache import (CellTable, f16_round, row_bytes, cache_bytes,
                       k_elem_offset, N_PAD_FLOOR, MASK_VISIBLE, MASK_HIDDEN)
 from .attention import masked_attention, brute_force_attention
 from .engine import OracleEngine
 
 __all__ = [
-    "clamp_params", "fill_batch", "split_simple", "split_equal", "split_batch",
+    "clamp_params", "fill_batch", "split_simple", "split_equal", "split_seq", "split_batch",
     "output_ids", "SplitError", "CellTable", "f16_round", "row_bytes",
     "cache_bytes", "k_elem_offset", "N_PAD_FLOOR", "MASK_VISIBLE", "MASK_HIDDEN",
     "masked_attention", "brute_force_attention", "OracleEngine",

@@ -156,24 +156,49 @@ def split_equal(unused: list, seq_sets: list, n_ubatch: int):
     return take, n_seq_tokens, len(adopted)
 
 
-def split_batch(seq_sets: list, n_ubatch: int, n_stream: int):
+def split_seq(unused: list, seq_sets: list, n_ubatch: int):
+    """One split_seq(n_ubatch) step (P2 Part C item 3: every ubatch holds the
+    tokens of one sequence set, sequences are never mixed; meant for
+    independent decoding).  Reading of what the page leaves open: the set is
+    that of the first unused slot in submission order, and the ubatch takes
+    the unused slots with exactly that set, in submission order, at most
+    n_ubatch of them.  Returns (slot list, n_seq_tokens, n_seqs)."""
+    first = next((i for i, u in enumerate(unused) if u), None)
+    if first is None:
+        return [], 0, 0
+    s = frozenset(seq_sets[first])
+    take = [i for i, u in enumerate(unused) if u and frozenset(seq_sets[i]) == s][:n_ubatch]
+    for i in take:
+        unused[i] = False
+    return take, len(take), 1
+
+
+SPLIT_MODES = ("auto", "simple", "equal", "seq")
+
+
+def split_batch(seq_sets: list, n_ubatch: int, n_stream: int, mode: str = "auto"):
     """The init_batch split loop (P2 Part C, strategy choice): one stream ->
-    split_simple, several streams -> split_equal(n_ubatch, true); repeat
-    until a split returns no slot.  Returns a list of
-    (slots, n_seq_tokens, n_seqs) tuples in ubatch order."""
+    split_simple, several streams -> split_equal(n_ubatch, true) ("auto");
+    a caller may instead name one of the three strategies.  Repeat until a
+    split returns no slot.  Returns a list of (slots, n_seq_tokens, n_seqs)
+    tuples in ubatch order."""
+    if mode not in SPLIT_MODES:
+        raise SplitError(f"unknown split mode {mode!r}")
+    if mode == "auto":
+        mode = "simple" if n_stream == 1 else "equal"
     unused = [True] * len(seq_sets)
     out = []
     while True:
-        if n_stream == 1:
+        if mode == "simple":
             take = split_simple(unused, n_ubatch)
-            if not take:
-                break
-            out.append((take, len(take), 1))
-        else:
+            nst, ns = len(take), 1
+        elif mode == "equal":
             take, nst, ns = split_equal(unused, seq_sets, n_ubatch)
-            if not take:
-                break
-            out.append((take, nst, ns))
+        else:
+            take, nst, ns = split_seq(unused, seq_sets, n_ubatch)
+        if not take:
+            break
+        out.append((take, nst, ns))
     return out
 
 

@@ -45,11 +45,12 @@ class OracleEngine:
 
     def __init__(self, n_layer, n_head, n_head_kv, head_dim, kv_size, n_stream=1,
                  n_seq_max=1, n_batch=0, n_ubatch=512, causal=True, kq_scale=None,
-                 cell_order=None, layers=None):
+                 cell_order=None, layers=None, split_mode="auto"):
         self.n_layer, self.n_head, self.n_head_kv, self.head_dim = n_layer, n_head, n_head_kv, head_dim
         self.kv_size, self.n_stream, self.n_seq_max = kv_size, n_stream, n_seq_max
         self.causal = bool(causal)
         self.kq_scale = kq_scale
+        self.split_mode = split_mode          # "auto", "simple", "equal" or "seq"
         self.n_batch, self.n_ubatch = clamp_params(kv_size * n_stream, n_batch, n_ubatch, causal)
         self.cells = CellTable(kv_size, n_stream, n_seq_max, cell_order)
         self.E = n_head_kv * head_dim
@@ -75,7 +76,7 @@ class OracleEngine:
                 next_pos[s] = self.cells.seq_pos_max(s) + 1
         p, sids, out = fill_batch(n_tokens, pos, seq_id, output, next_pos,
                                   self.n_seq_max, self.n_stream)
-        parts = split_batch([set(x) for x in sids], self.n_ubatch, self.n_stream)
+        parts = split_batch([set(x) for x in sids], self.n_ubatch, self.n_stream, self.split_mode)
         streams = [sids[i][0] % self.n_stream for (slots, _, _) in parts for i in slots]
         cells = self.cells.reserve(streams)
         if cells is None:

@@ -56,6 +56,7 @@ class Workload:
     n_ubatch: int = 512
     causal: bool = True
     cell_order: Optional[np.ndarray] = field(default=None, repr=False)
+    split_mode: str = "auto"          # "auto", "simple", "equal" or "seq"
     note: str = ""
 
     @property

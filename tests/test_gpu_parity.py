@@ -337,3 +337,29 @@ def test_noncausal_parity(name):
         ma, _ = assert_parity(got[key], ref[key], tag=f"non-causal {name} {key}")
         worst = max(worst, ma)
     assert worst < (2e-5 if name == "cb_decode" else 1.6e-3), worst
+
+
+@pytest.mark.parametrize("name,mode", [("mixed", "seq"), ("prefix", "seq"), ("prefill", "seq"), ("mixed", "simple")])
+def test_split_mode_parity(name, mode):
+    """Explicitly requested split strategies end to end: split_seq keeps every
+    ubatch to one sequence set; split_simple over several streams mixes
+    streams inside a ubatch."""
+    import dataclasses
+    wl = dataclasses.replace(small(name), split_mode=mode)
+    layers = list(range(wl.n_layer))
+    print(f"[gpu] split mode {mode} on {name}", flush=True)
+    eng, ref, masks, meta = oracle_run(wl, layers, keep_masks=True)
+    ub_index = {b: 0 for b in range(len(wl.batches))}
+
+    def check(ctx, b, ub):
+        r = meta[(b, ub_index[b])]
+        assert ub.cells.tolist() == r.cells
+        if mode == "seq":
+            assert ub.n_seqs == 1 and len(set(ub.seq_ids)) == 1
+        m = ctx.mask(ub).cpu().numpy().view(np.uint16)
+        assert np.array_equal(m, masks[(b, ub_index[b])].view(np.uint16))
+        ub_index[b] += 1
+
+    _, got = gpu_run(wl, layers, on_ubatch=check)
+    for key in ref:
+        assert_parity(got[key], ref[key], tag=f"{mode} {name} {key}")

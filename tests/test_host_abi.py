@@ -43,14 +43,14 @@ def host_ctx(wl, order="auto", n_ubatch=None):
     order = wl.cell_order if order == "auto" else order
     return K.Context(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
                      wl.n_seq_max, wl.n_batch, wl.n_ubatch if n_ubatch is None else n_ubatch,
-                     wl.causal, cell_order=order)
+                     wl.causal, cell_order=order, split_mode=wl.split_mode)
 
 
 def oracle_for(wl, order="auto", n_ubatch=None):
     order = wl.cell_order if order == "auto" else order
     return OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
                         wl.n_seq_max, wl.n_batch, wl.n_ubatch if n_ubatch is None else n_ubatch,
-                        wl.causal, cell_order=order, layers=[])
+                        wl.causal, cell_order=order, layers=[], split_mode=wl.split_mode)
 
 
 def compare_split(ctx, eng, n, pos, seqs, out):
@@ -110,6 +110,22 @@ def test_host_split_placement_matches_oracle(make):
     ctx, eng = host_ctx(wl), oracle_for(wl)
     for bt in wl.batches:
         ubs, rubs = compare_split(ctx, eng, bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        commit_all(ctx, eng, ubs, rubs)
+    compare_tables(ctx, eng)
+
+
+@pytest.mark.parametrize("mode", ["simple", "equal", "seq"])
+@pytest.mark.parametrize("make", WORKLOADS, ids=["tiny", "prefill", "cb_decode", "mixed", "prefix"])
+def test_host_split_modes_match_oracle(make, mode):
+    """Each split strategy requested explicitly, on every workload shape."""
+    import dataclasses
+    wl = dataclasses.replace(make(), split_mode=mode)
+    ctx, eng = host_ctx(wl), oracle_for(wl)
+    for bt in wl.batches:
+        ubs, rubs = compare_split(ctx, eng, bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        if mode == "seq":
+            for u in ubs:
+                assert u.n_seqs == 1 and len(set(u.seq_ids)) == 1
         commit_all(ctx, eng, ubs, rubs)
     compare_tables(ctx, eng)
 
@@ -254,7 +270,7 @@ def test_workspace_and_cache_bytes():
 
 
 @pytest.mark.parametrize("kw", [dict(head_dim=48), dict(n_head=3, n_head_kv=2), dict(n_head=32, n_head_kv=2),
-                                dict(n_seq_max=65), dict(kv_size=0),
+                                dict(n_seq_max=65), dict(kv_size=0), dict(split_mode=4), dict(split_mode=-1),
                                 # one layer's K tensor at 2 GiB: 2^20 cells x 8 heads x 128 x 2 B
                                 dict(kv_size=1 << 20, n_head=8, n_head_kv=8, head_dim=128)])
 def test_create_rejects_bad_geometry(kw):

@@ -161,3 +161,37 @@ def test_engine_rejects_batch_larger_than_n_batch():
         eng.split(17)
     st, ubs, ids = eng.split(16)
     assert st == 0 and [u.n_tokens for u in ubs] == [8, 8]
+
+
+def test_split_seq_one_set_per_ubatch():
+    """split_seq (P2 Part C item 3): every ubatch holds the tokens of one
+    sequence set; different sequences are never mixed.  Interleaved decode
+    slots of three sequences, a prefix-shared slot {0, 1} and a cap of 2."""
+    sets = [{0}, {1}, {0}, {1}, {2}, {0}, {0, 1}, {0}]
+    parts = B.split_batch(sets, 2, 1, mode="seq")
+    assert [p[0] for p in parts] == [[0, 2], [1, 3], [4], [5, 7], [6]]
+    assert all(p[2] == 1 and p[1] == len(p[0]) for p in parts)
+    # invariants: a partition of the batch, one set per ubatch, at most
+    # n_ubatch slots, submission order inside a ubatch
+    for n_ubatch in (1, 2, 3, 8):
+        parts = B.split_batch(sets, n_ubatch, 1, mode="seq")
+        flat = sorted(i for p in parts for i in p[0])
+        assert flat == list(range(len(sets)))
+        for slots, _, _ in parts:
+            assert len({frozenset(sets[i]) for i in slots}) == 1
+            assert 0 < len(slots) <= n_ubatch and slots == sorted(slots)
+
+
+def test_split_seq_long_sequence_is_cut_at_n_ubatch():
+    sets = [{3}] * 1000
+    parts = B.split_batch(sets, 512, 4, mode="seq")
+    assert [len(p[0]) for p in parts] == [512, 488]
+
+
+def test_split_modes_auto_matches_init_batch_choice():
+    rng = np.random.default_rng(5)
+    sets = [{int(s)} for s in rng.integers(0, 4, size=40)]
+    assert B.split_batch(sets, 8, 1) == B.split_batch(sets, 8, 1, mode="simple")
+    assert B.split_batch(sets, 8, 3) == B.split_batch(sets, 8, 3, mode="equal")
+    with pytest.raises(SplitError):
+        B.split_batch(sets, 8, 1, mode="nope")

@@ -63,6 +63,13 @@ int make_geometry(const kvattn_params& p, Geometry& g, std::string& err) {
   g.n_ubatch = std::min(g.n_batch, p.n_ubatch == 0 ? nb_in : p.n_ubatch);
   g.kq_scale = p.kq_scale != 0.f ? p.kq_scale : 1.0f / std::sqrt(static_cast<float>(p.head_dim));
   g.attend_layers = std::max(1, std::min(p.attend_layers, p.n_layer));
+  if (p.split_mode < KVATTN_SPLIT_AUTO || p.split_mode > KVATTN_SPLIT_SEQ) {
+    err = "split_mode must be one of KVATTN_SPLIT_AUTO, _SIMPLE, _EQUAL, _SEQ";
+    return KVATTN_EINVAL;
+  }
+  // AUTO: the init_batch choice ("Batch、Ubatch 与解码主循环", Part C)
+  g.split_mode = p.split_mode != KVATTN_SPLIT_AUTO ? p.split_mode
+                 : (p.n_stream == 1 ? KVATTN_SPLIT_SIMPLE : KVATTN_SPLIT_EQUAL);
   return KVATTN_OK;
 }
 
@@ -200,12 +207,32 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
     out[n - 1] = 1;
   }
 
-  // -- split: one stream -> split_simple, several -> split_equal(n_ubatch, true)
-  // ("Batch、Ubatch 与解码主循环", Part C, strategy choice)
+  // -- split ("Batch、Ubatch 与解码主循环", Part C): the strategy resolved at
+  // create (by default split_simple for one stream, split_equal(n_ubatch,
+  // true) for several)
   struct Part { std::vector<int32_t> slots; int32_t nst, ns; };
   std::vector<Part> parts;
   const int32_t U = g_.n_ubatch;
-  if (g_.n_stream == 1) {
+  if (g_.split_mode == KVATTN_SPLIT_SEQ) {
+    // split_seq: the set of the first unused slot; its unused slots in
+    // submission order, at most U of them; sets are never mixed
+    std::vector<uint8_t> used(n, 0);
+    int32_t first = 0;
+    while (true) {
+      while (first < n && used[first]) ++first;
+      if (first == n) break;
+      const uint64_t set = setmask[first];
+      Part p;
+      for (int32_t i = first; i < n && static_cast<int32_t>(p.slots.size()) < U; ++i)
+        if (!used[i] && setmask[i] == set) {
+          used[i] = 1;
+          p.slots.push_back(i);
+        }
+      p.nst = static_cast<int32_t>(p.slots.size());
+      p.ns = 1;
+      parts.push_back(std::move(p));
+    }
+  } else if (g_.split_mode == KVATTN_SPLIT_SIMPLE) {
     // split_simple: next U slots in submission order, sequence ids ignored
     for (int32_t a = 0; a < n; a += U) {
       Part p;

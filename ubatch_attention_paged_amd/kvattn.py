@@ -17,6 +17,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvattn.so")
 
 KVATTN_OK, KVATTN_NO_SLOT = 0, 1
+KVATTN_SPLIT_AUTO, KVATTN_SPLIT_SIMPLE, KVATTN_SPLIT_EQUAL, KVATTN_SPLIT_SEQ = 0, 1, 2, 3
+SPLIT_MODES = {"auto": KVATTN_SPLIT_AUTO, "simple": KVATTN_SPLIT_SIMPLE, "equal": KVATTN_SPLIT_EQUAL,
+               "seq": KVATTN_SPLIT_SEQ}
 KVATTN_EINVAL, KVATTN_ESTATE, KVATTN_ENOMEM, KVATTN_EHIP, KVATTN_ENODEV = -1, -2, -3, -4, -5
 MAX_SEQ = 64
 
@@ -34,7 +37,8 @@ class kvattn_params(ctypes.Structure):
                 ("kq_scale", ctypes.c_float), ("cell_order", _i32p),
                 ("k_layers", _vpp), ("v_layers", _vpp),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("device", ctypes.c_int32), ("attend_layers", ctypes.c_int32)]
+                ("device", ctypes.c_int32), ("attend_layers", ctypes.c_int32),
+                ("split_mode", ctypes.c_int32)]
 
 
 class kvattn_batch(ctypes.Structure):
@@ -319,7 +323,7 @@ class Context:
 
     def __init__(self, n_layer, n_head, n_head_kv, head_dim, kv_size, n_stream=1, n_seq_max=1,
                  n_batch=0, n_ubatch=512, causal=True, kq_scale=0.0, cell_order=None, device=None,
-                 attend_layers=0):
+                 attend_layers=0, split_mode=0):
         self.n_layer, self.n_head, self.n_head_kv, self.head_dim = n_layer, n_head, n_head_kv, head_dim
         self.kv_size, self.n_stream, self.n_seq_max = kv_size, n_stream, n_seq_max
         self.E = n_head_kv * head_dim
@@ -328,6 +332,7 @@ class Context:
         p.kv_size, p.n_stream, p.n_seq_max = kv_size, n_stream, n_seq_max
         p.n_batch, p.n_ubatch, p.causal, p.kq_scale = n_batch, n_ubatch, int(bool(causal)), kq_scale
         p.attend_layers = attend_layers
+        p.split_mode = SPLIT_MODES[split_mode] if isinstance(split_mode, str) else int(split_mode)
         self._order = None
         if cell_order is not None:
             self._order, p.cell_order = _arr(np.asarray(cell_order).reshape(-1), np.int32)
