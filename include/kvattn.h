@@ -222,6 +222,11 @@ int kvattn_plan_stats(const kvattn_ctx *ctx, int32_t only_outputs, int32_t *n_cl
                       int32_t *n_items_valu, int32_t *n_items_mfma, int32_t *n_partial_rows,
                       int32_t *n_reduced);
 
+/* HOST-ONLY.  The context's parameters as in effect: n_batch and n_ubatch
+ * clamped, kq_scale and attend_layers defaulted, split_mode resolved (never
+ * AUTO).  Pointer fields and workspace_bytes are zero. */
+int kvattn_get_params(const kvattn_ctx *ctx, kvattn_params *out);
+
 /* HOST-ONLY.  Text of the last error on this context ("" if none). */
 const char *kvattn_last_error(const kvattn_ctx *ctx);
 

@@ -1,7 +1,7 @@
 """MI355X-native per-ubatch attention over a cell-granular F16 KV cache.
 
 The work runs in ``libkvattn.so`` (hand-written HIP for gfx950 behind the C
-ABI of ``include/kvattn.h``); this package is its ctypes binding.  Importing
+ABI of ``include/kvattn.h`` and ``include/kvsched.h``); this package is its ctypes binding.  Importing
 it loads the library and fails loudly when it has not been built -- there is
 no CPU fallback.
 """
@@ -11,7 +11,11 @@ from .kvattn import (  # noqa: F401
     KvattnError, Context, Ubatch, SeqIds, kvattn_params, kvattn_batch, kvattn_ubatch, load, LIB_PATH,
     kvattn_workspace_bytes, kvattn_cache_bytes, kvattn_create, kvattn_destroy, kvattn_split,
     kvattn_store, kvattn_attend, kvattn_n_kv, kvattn_get_mask, kvattn_get_classes, kvattn_get_cells,
-    kvattn_seq_rm, kvattn_seq_pos_max, kvattn_plan_stats, kvattn_last_error,
+    kvattn_seq_rm, kvattn_seq_pos_max, kvattn_plan_stats, kvattn_last_error, kvattn_get_params,
+    kvattn_split_batch, Scheduler, kvattn_sched_params, kvattn_sched_iter, kvattn_sched_create,
+    kvattn_sched_destroy, kvattn_sched_submit, kvattn_sched_step, kvattn_sched_advance,
+    kvattn_sched_request, kvattn_sched_last_error, KVATTN_ADMIT_RESERVE, KVATTN_ADMIT_PAGED,
+    KVATTN_REQ_WAITING, KVATTN_REQ_RUNNING, KVATTN_REQ_DONE,
 )
 
 load()

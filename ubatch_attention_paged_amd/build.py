@@ -1,6 +1,9 @@
 """Build libkvattn.so in-tree with hipcc for gfx950.
 
-    python -m ubatch_attention_paged_amd.build
+    python ubatch_attention_paged_amd/build.py
+
+(run by path: importing the package loads the library, which fails when an
+older build lacks a newer symbol).
 
 Compiles csrc/*.cpp and csrc/*.hip into one shared library next to this
 file.  Packed-FP32 instructions are disabled for the device code.
@@ -18,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvattn.so")
-SOURCES = ["host_core.cpp", "api.cpp", "kernels_commit.hip", "attn_valu.hip", "attn_mfma.hip"]
+SOURCES = ["host_core.cpp", "api.cpp", "sched.cpp", "kernels_commit.hip", "attn_valu.hip", "attn_mfma.hip"]
 ARCH = os.environ.get("KVATTN_OFFLOAD_ARCH", "gfx950")
 
 

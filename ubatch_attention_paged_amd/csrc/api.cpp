@@ -568,6 +568,27 @@ int kvattn_seq_rm(kvattn_ctx* c, int32_t seq_id, int32_t p0, int32_t p1) {
 
 int32_t kvattn_seq_pos_max(const kvattn_ctx* c, int32_t seq_id) { return c ? c->core.seq_pos_max(seq_id) : -1; }
 
+int kvattn_get_params(const kvattn_ctx* c, kvattn_params* out) {
+  if (!c || !out) return KVATTN_EINVAL;
+  const Geometry& g = c->core.geo();
+  *out = kvattn_params{};
+  out->n_layer = g.n_layer;
+  out->n_head = g.n_head;
+  out->n_head_kv = g.n_head_kv;
+  out->head_dim = g.head_dim;
+  out->kv_size = g.kv_size;
+  out->n_stream = g.n_stream;
+  out->n_seq_max = g.n_seq_max;
+  out->n_batch = g.n_batch;
+  out->n_ubatch = g.n_ubatch;
+  out->causal = g.causal;
+  out->kq_scale = g.kq_scale;
+  out->device = c->device;
+  out->attend_layers = g.attend_layers;
+  out->split_mode = g.split_mode;
+  return KVATTN_OK;
+}
+
 int kvattn_plan_stats(const kvattn_ctx* c, int32_t only_outputs, int32_t* n_classes, int32_t* n_items_valu,
                       int32_t* n_items_mfma, int32_t* n_partial_rows, int32_t* n_reduced) {
   if (!c) return KVATTN_EINVAL;

@@ -1,4 +1,5 @@
-"""ctypes binding of libkvattn.so (include/kvattn.h), same names as the C ABI.
+"""ctypes binding of libkvattn.so (include/kvattn.h, include/kvsched.h), same
+names as the C ABI.
 
 Argument marshalling only: every step of the path runs in the library.  The
 ``Context`` class adds torch plumbing -- it allocates the F16 K/V caches and
@@ -21,6 +22,9 @@ KVATTN_SPLIT_AUTO, KVATTN_SPLIT_SIMPLE, KVATTN_SPLIT_EQUAL, KVATTN_SPLIT_SEQ = 0
 SPLIT_MODES = {"auto": KVATTN_SPLIT_AUTO, "simple": KVATTN_SPLIT_SIMPLE, "equal": KVATTN_SPLIT_EQUAL,
                "seq": KVATTN_SPLIT_SEQ}
 KVATTN_EINVAL, KVATTN_ESTATE, KVATTN_ENOMEM, KVATTN_EHIP, KVATTN_ENODEV = -1, -2, -3, -4, -5
+KVATTN_ADMIT_RESERVE, KVATTN_ADMIT_PAGED = 0, 1
+ADMIT_POLICIES = {"reserve": KVATTN_ADMIT_RESERVE, "paged": KVATTN_ADMIT_PAGED}
+KVATTN_REQ_WAITING, KVATTN_REQ_RUNNING, KVATTN_REQ_DONE = 0, 1, 2
 MAX_SEQ = 64
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -55,6 +59,21 @@ class kvattn_ubatch(ctypes.Structure):
                 ("src_idx", _i32p), ("stream", _i32p), ("cells", _i32p)]
 
 
+class kvattn_sched_params(ctypes.Structure):
+    _fields_ = [("token_budget", ctypes.c_int32), ("max_running", ctypes.c_int32),
+                ("policy", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("chunked", ctypes.c_int32), ("max_requests", ctypes.c_int32)]
+
+
+class kvattn_sched_iter(ctypes.Structure):
+    _fields_ = [("batch", kvattn_batch), ("req", _i32p),
+                ("n_retired", ctypes.c_int32), ("retired", _i32p),
+                ("n_preempted", ctypes.c_int32), ("preempted", _i32p),
+                ("n_admitted", ctypes.c_int32), ("admitted", _i32p), ("admitted_seq", _i32p),
+                ("n_running", ctypes.c_int32), ("n_waiting", ctypes.c_int32),
+                ("n_decode", ctypes.c_int32)]
+
+
 class KvattnError(RuntimeError):
     def __init__(self, code, msg):
         super().__init__(f"kvattn error {code}: {msg}")
@@ -83,7 +102,16 @@ SIGNATURES = {
     "kvattn_seq_rm": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
     "kvattn_seq_pos_max": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
     "kvattn_plan_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p]),
+    "kvattn_get_params": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_params)]),
     "kvattn_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
+    "kvattn_sched_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_sched_params),
+                                           ctypes.POINTER(ctypes.c_void_p)]),
+    "kvattn_sched_destroy": (None, [ctypes.c_void_p]),
+    "kvattn_sched_submit": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, _i32p]),
+    "kvattn_sched_step": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_sched_iter)]),
+    "kvattn_sched_advance": (ctypes.c_int, [ctypes.c_void_p]),
+    "kvattn_sched_request": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p]),
+    "kvattn_sched_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
 }
 
 
@@ -211,6 +239,16 @@ def kvattn_split(ctx, n_tokens, pos=None, seq_ids=None, output=None, cap=None, n
         a, p = _arr(output, np.int8)
         keep.append(a)
         b.output = p
+    return _split(lib, ctx, b, keep, cap, n_batch_ids)
+
+
+def kvattn_split_batch(ctx, b: kvattn_batch, cap=None):
+    """kvattn_split of an already marshalled batch (e.g. a scheduler's)."""
+    return _split(load(), ctx, b, None, cap, 0)
+
+
+def _split(lib, ctx, b, keep, cap, n_batch_ids):
+    n_tokens = b.n_tokens
     if cap is None:
         cap = max(1, n_tokens)
     ubs = (kvattn_ubatch * cap)()
@@ -303,6 +341,14 @@ def kvattn_seq_pos_max(ctx, seq_id) -> int:
     return load().kvattn_seq_pos_max(ctx, seq_id)
 
 
+def kvattn_get_params(ctx) -> kvattn_params:
+    p = kvattn_params()
+    rc = load().kvattn_get_params(ctx, ctypes.byref(p))
+    if rc != 0:
+        raise KvattnError(rc, "kvattn_get_params")
+    return p
+
+
 def kvattn_plan_stats(ctx, only_outputs=0):
     vals = [ctypes.c_int32(0) for _ in range(5)]
     load().kvattn_plan_stats(ctx, int(only_outputs), *[ctypes.byref(v) for v in vals])
@@ -382,6 +428,9 @@ class Context:
         from_ids = self.n_batch_clamped() if with_ids else 0
         return kvattn_split(self.ctx, n_tokens, pos, seq_ids, output, n_batch_ids=from_ids)
 
+    def split_batch(self, b: kvattn_batch):
+        return kvattn_split_batch(self.ctx, b)
+
     def n_batch_clamped(self):
         n_ctx = self.kv_size * self.n_stream
         nb = self.params.n_batch if self.params.n_batch > 0 else 2048
@@ -416,3 +465,105 @@ class Context:
 
     def plan_stats(self, only_outputs=False):
         return kvattn_plan_stats(self.ctx, only_outputs)
+
+
+# --- the iteration-level batching loop (include/kvsched.h) ------------------
+
+def kvattn_sched_create(ctx, token_budget=0, max_running=0, policy="paged", block_size=1, chunked=True,
+                        max_requests=4096):
+    p = kvattn_sched_params()
+    p.token_budget, p.max_running = token_budget, max_running
+    p.policy = ADMIT_POLICIES[policy] if isinstance(policy, str) else int(policy)
+    p.block_size, p.chunked, p.max_requests = block_size, int(bool(chunked)), max_requests
+    out = ctypes.c_void_p()
+    rc = load().kvattn_sched_create(ctx, ctypes.byref(p), ctypes.byref(out))
+    if rc != 0:
+        raise KvattnError(rc, "kvattn_sched_create: invalid scheduler parameters")
+    return out
+
+
+def kvattn_sched_destroy(s):
+    load().kvattn_sched_destroy(s)
+
+
+def kvattn_sched_last_error(s) -> str:
+    r = load().kvattn_sched_last_error(s)
+    return r.decode() if r else ""
+
+
+def kvattn_sched_submit(s, n_prompt, n_generate) -> int:
+    rid = ctypes.c_int32(-1)
+    rc = load().kvattn_sched_submit(s, n_prompt, n_generate, ctypes.byref(rid))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_sched_last_error(s))
+    return rid.value
+
+
+def kvattn_sched_step(s, it: kvattn_sched_iter):
+    rc = load().kvattn_sched_step(s, ctypes.byref(it))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_sched_last_error(s))
+
+
+def kvattn_sched_advance(s):
+    rc = load().kvattn_sched_advance(s)
+    if rc != 0:
+        raise KvattnError(rc, kvattn_sched_last_error(s))
+
+
+def kvattn_sched_request(s, req_id):
+    vals = [ctypes.c_int32(0) for _ in range(4)]
+    rc = load().kvattn_sched_request(s, req_id, *[ctypes.byref(v) for v in vals])
+    if rc != 0:
+        raise KvattnError(rc, "unknown request id")
+    return dict(zip(("state", "seq", "n_cached", "n_sampled"), [v.value for v in vals]))
+
+
+class Scheduler:
+    """The native loop over a ``Context``.  ``step()`` returns the raw
+    iteration (``.batch`` feeds ``Context.split_batch``) and ``record()``
+    its host copy as plain lists."""
+
+    def __init__(self, ctx: "Context", token_budget=0, max_running=0, policy="paged", block_size=1,
+                 chunked=True, max_requests=4096):
+        self.context = ctx
+        self.s = kvattn_sched_create(ctx.ctx, token_budget, max_running, policy, block_size, chunked,
+                                     max_requests)
+        self.it = kvattn_sched_iter()
+
+    def close(self):
+        if self.s:
+            kvattn_sched_destroy(self.s)
+            self.s = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def submit(self, n_prompt, n_generate):
+        return kvattn_sched_submit(self.s, n_prompt, n_generate)
+
+    def step(self) -> kvattn_sched_iter:
+        kvattn_sched_step(self.s, self.it)
+        return self.it
+
+    def advance(self):
+        kvattn_sched_advance(self.s)
+
+    def request(self, req_id):
+        return kvattn_sched_request(self.s, req_id)
+
+    def record(self):
+        it = self.it
+        n = it.batch.n_tokens
+        seq = [it.batch.seq_id[i][0] for i in range(n)]
+        return {"retired": _take(it.retired, it.n_retired, np.int32).tolist(),
+                "preempted": _take(it.preempted, it.n_preempted, np.int32).tolist(),
+                "admitted": list(zip(_take(it.admitted, it.n_admitted, np.int32).tolist(),
+                                     _take(it.admitted_seq, it.n_admitted, np.int32).tolist())),
+                "req": _take(it.req, n, np.int32).tolist(), "seq": seq,
+                "pos": _take(it.batch.pos, n, np.int32).tolist(),
+                "output": _take(it.batch.output, n, np.int8).tolist(),
+                "n_running": it.n_running, "n_waiting": it.n_waiting, "n_decode": it.n_decode}
