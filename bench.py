@@ -14,6 +14,11 @@ Two decode workloads are measured in the same run and reported under
 shuffled 65536-cell cache, and 32 sequences sharing a 2048-cell prefix.  A
 decode step appends one token per sequence (positions advance each step).
 
+A mixed prefill + decode workload (8 prompts chunked alongside 56 decoders,
+split_equal) is reported under "mixed", and the iteration-level batching
+loop (the native scheduler admitting, retiring and assembling every
+iteration over a stream of requests) under "serving".
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 
@@ -336,6 +341,104 @@ def bench_mixed(wl, dev, steps, warmup, layer_chunk):
 
 
 # ---------------------------------------------------------------------------
+# iteration-level batching loop (native scheduler) over a request stream
+
+def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk):
+    """The native loop (retire, admit, assemble) drives the context for
+    warm_iters untimed iterations, then timed_iters timed ones.  Every
+    iteration splits the assembled batch and, for each ubatch, stores K/V and
+    runs attention for all slots over all layers.  K/V/Q rows come from a
+    seeded pool resident in HBM (the values do not steer the loop)."""
+    import torch
+    from ubatch_attention_paged_amd import Context, Scheduler, kvattn_store, kvattn_attend
+    L = stream.n_layer
+    ctx = Context(L, stream.n_head, stream.n_head_kv, stream.head_dim, stream.kv_size, stream.n_stream,
+                  stream.n_seq_max, stream.token_budget, stream.n_ubatch, device=dev, attend_layers=layer_chunk,
+                  split_mode=stream.split_mode)
+    sch = Scheduler(ctx, token_budget=stream.token_budget, policy=stream.policy, block_size=stream.block_size,
+                    chunked=stream.chunked, max_requests=stream.n_requests)
+    g = torch.Generator(device=dev)
+    g.manual_seed(stream.seed)
+    nb, HD = stream.token_budget, stream.n_head * stream.head_dim
+    K = torch.randn((L, nb, stream.E), generator=g, device=dev)
+    V = torch.randn((L, nb, stream.E), generator=g, device=dev)
+    Q = torch.randn((L, nb, HD), generator=g, device=dev)
+    outs = torch.empty((L, stream.n_ubatch, HD), dtype=torch.float32, device=dev)
+    cur = torch.cuda.current_stream().cuda_stream
+    attend_ev = []
+
+    def iteration(k, timed):
+        for r in stream.arrivals(k):
+            sch.submit(int(stream.n_prompt[r]), int(stream.n_generate[r]))
+        t0 = time.perf_counter()
+        it = sch.step()
+        t_sched = time.perf_counter() - t0
+        n = it.batch.n_tokens
+        info = (n, it.n_decode, 0, it.n_running, it.n_waiting, it.n_preempted, 0, 0)
+        if n:
+            pos = np.ctypeslib.as_array(it.batch.pos, shape=(n,)).astype(np.int64)
+            req = np.ctypeslib.as_array(it.req, shape=(n,))
+            out = np.ctypeslib.as_array(it.batch.output, shape=(n,))
+            # one sequence id per slot, each sequence's slots contiguous and
+            # ascending: the last slot of a run at position p reads p + 1
+            # cells once for its whole visibility class
+            last = np.nonzero(np.append(req[1:] != req[:-1], True))[0]
+            info = (n, it.n_decode, int(out.sum()), it.n_running, it.n_waiting, it.n_preempted,
+                    int((pos[last] + 1).sum()), int((pos + 1).sum()))
+        if n:
+            st, ubs, _ = ctx.split_batch(it.batch)
+            if st != 0:
+                raise RuntimeError("the loop assembled a batch the cache cannot hold")
+            for ub in ubs:
+                r0 = int(ub.src[0])
+                assert ub.src[-1] - r0 == ub.n_tokens - 1
+                for a in range(0, L, layer_chunk):
+                    b = min(L, a + layer_chunk)
+                    kvattn_store(ctx.ctx, ub, a, row_ptrs(K, a, b, r0), row_ptrs(V, a, b, r0), cur)
+                    if timed:
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record()
+                    kvattn_attend(ctx.ctx, ub, a, row_ptrs(Q, a, b, r0), row_ptrs(outs, a, b, 0), 0, cur)
+                    if timed:
+                        e1.record()
+                        attend_ev.append((e0, e1))
+        sch.advance()
+        return t_sched, info
+
+    log(f"[bench] serving: {warm_iters} warm-up iterations")
+    for k in range(warm_iters):
+        iteration(k, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    recs = [iteration(warm_iters + k, True) for k in range(timed_iters)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    attend_ms = sum(a.elapsed_time(b) for a, b in attend_ev)
+    sched_us = np.array([r[0] for r in recs]) * 1e6
+    info = np.array([r[1] for r in recs], dtype=np.int64)
+    slots, dec, gen = int(info[:, 0].sum()), int(info[:, 1].sum()), int(info[:, 2].sum())
+    row = 2 * stream.n_head_kv * stream.head_dim * 2
+    kv_bytes = float(info[:, 6].sum()) * row * L         # visible cells, each read once per class
+    flops = float(info[:, 7].sum()) * 4.0 * HD * L        # QK^T and PV over visible (query, cell) pairs
+    bound_ms = max(kv_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_F16_PEAK_TFLOPS * 1e12)) * 1e3
+    res = dict(workload=f"{stream.name}: {stream.note()}", iterations=timed_iters,
+               generated_tokens_per_s=round(gen / wall, 1), positions_per_s=round(slots / wall, 1),
+               ms_per_iteration=round(1e3 * wall / timed_iters, 4),
+               attend_ms_per_iteration=round(attend_ms / timed_iters, 4),
+               sched_step_us=dict(mean=round(float(sched_us.mean()), 2),
+                                  p99=round(float(np.percentile(sched_us, 99)), 2)),
+               mean_running=round(float(info[:, 3].mean()), 2), mean_waiting=round(float(info[:, 4].mean()), 1),
+               decode_slot_frac=round(dec / max(1, slots), 4), preemptions=int(info[:, 5].sum()),
+               attend_kv_read_gbs=round(kv_bytes / (attend_ms * 1e-3) / 1e9, 1),
+               attend_tflops=round(flops / (attend_ms * 1e-3) / 1e12, 1),
+               attend_roofline_frac=round(bound_ms / attend_ms, 4))
+    sch.close()
+    ctx.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # oracle on the host cores
 
 def cpu_baseline(wl, budget_s=25.0):
@@ -405,6 +508,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode workloads (for profiling their kernels alone)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode workload")
+    ap.add_argument("--no-serving", action="store_true", help="skip the iteration-level batching loop")
+    ap.add_argument("--serving-iters", type=int, default=200, help="timed iterations of the serving loop")
     ap.add_argument("--decode-workload", choices=["cb_decode", "prefix_decode"], action="append",
                     help="restrict the decode runs to this workload (repeatable)")
     args = ap.parse_args()
@@ -485,6 +590,13 @@ def main():
         log(f"[bench] mixed: {m['tokens_per_s']:,.0f} tok/s; " + "; ".join(
             f"{k}: {v}" for k, v in m.items() if k.endswith("_ubatches")))
         line["mixed"] = m
+    if not args.no_serving:
+        from synthetic.serving import qwen_serving
+        sv = bench_serving(qwen_serving(), dev, 300, args.serving_iters, args.layer_chunk)
+        log(f"[bench] serving: {sv['generated_tokens_per_s']:,.0f} generated tok/s, "
+            f"{sv['positions_per_s']:,.0f} positions/s, {sv['ms_per_iteration']:.3f} ms/iteration, "
+            f"scheduler {sv['sched_step_us']['mean']:.1f} us/iteration")
+        line["serving"] = sv
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(wl)

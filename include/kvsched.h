@@ -34,9 +34,11 @@
  * Sequence ids are the lowest free id in [0, n_seq_max) at admission; the
  * stream of a sequence is seq_id % n_stream, as in kvattn.
  *
- * Every table is sized at kvattn_sched_create; submit, step and advance
- * allocate nothing.  One scheduler drives one context from one thread; the
- * context must not be given other batches or seq_rm calls meanwhile.
+ * The scheduler's tables are sized at kvattn_sched_create; submit, step and
+ * advance allocate nothing of their own (the context's kvattn_seq_rm, which
+ * step calls, keeps its own bookkeeping).  One scheduler drives one context
+ * from one thread; the context must not be given other batches or seq_rm
+ * calls meanwhile.
  * Return codes are kvattn's (KVATTN_OK, KVATTN_EINVAL, KVATTN_ESTATE,
  * KVATTN_ENOMEM); kvattn_sched_last_error() describes the last failure.
  */

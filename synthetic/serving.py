@@ -83,6 +83,13 @@ class RequestStream:
             out[m] = self.rows(int(r), layer, kind, pos[m])
         return out
 
+    def note(self):
+        return (f"{self.n_requests} requests, prompts {self.n_prompt.min()}..{self.n_prompt.max()}, "
+                f"generate {self.n_generate.min()}..{self.n_generate.max()}, {self.n_layer} layers, "
+                f"{self.n_head}/{self.n_head_kv} heads x {self.head_dim}, kv_size {self.kv_size} x "
+                f"{self.n_stream} streams, <= {self.max_running or self.n_seq_max} running, budget "
+                f"{self.token_budget} positions, n_ubatch {self.n_ubatch}, {self.policy}")
+
     def sched_kwargs(self):
         return dict(kv_size=self.kv_size, n_stream=self.n_stream, n_seq_max=self.n_seq_max,
                     token_budget=self.token_budget, max_running=self.max_running, policy=self.policy,

@@ -372,7 +372,8 @@ int HostCore::seq_rm(int32_t seq, int32_t p0, int32_t p1) {
   const int32_t lo = p0 < 0 ? 0 : p0;
   for (int s = 0; s < g_.n_stream; ++s) {
     Stream& S = st_[s];
-    for (int32_t j = 0; j < g_.kv_size; ++j) {
+    const int32_t end = S.umax;           // every cell at or past umax is empty
+    for (int32_t j = 0; j < end; ++j) {
       const int32_t p = S.pos[j];
       if (p < 0 || p < lo || (p1 >= 0 && p >= p1)) continue;
       uint64_t m = S.mask[j];
@@ -391,7 +392,7 @@ int32_t HostCore::seq_pos_max(int32_t seq) const {
   if (seq < 0 || seq >= g_.n_seq_max) return -1;
   int32_t best = -1;
   for (const auto& S : st_)
-    for (int32_t j = 0; j < g_.kv_size; ++j)
+    for (int32_t j = 0; j < S.umax; ++j)
       if (S.pos[j] >= 0 && (S.mask[j] >> seq & 1)) best = std::max(best, S.pos[j]);
   return best;
 }

@@ -5,9 +5,10 @@
 //
 // The pages ask the per-iteration host work to stay well inside one forward
 // pass and to keep memory allocation off that path ("What the loop costs
-// elsewhere"): every table here is sized at create, and one step touches
-// only the running sequences (at most n_seq_max <= 64) and the waiting
-// requests it admits.
+// elsewhere"): every table of the scheduler is sized at create, and one
+// step touches only the running sequences (at most n_seq_max <= 64) and the
+// waiting requests it admits, plus one kvattn_seq_rm per retired or
+// preempted sequence.
 #include <algorithm>
 #include <cstring>
 #include <new>
