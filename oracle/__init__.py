@@ -25,6 +25,10 @@ Modules:
 * ``attention`` -- masked-softmax grouped-query attention in fp64 (the plain
   definition) and an explicit-loop brute force over the token history.
 * ``engine``    -- the decode loop that strings the above together.
+* ``scheduler`` -- the iteration-level batching loop (retire, admit under
+  token and cache budgets, assemble, advance; preemption by recompute).
+* ``seqstate``  -- save / restore of one sequence's cached K/V in the record
+  layout of the .bin dump.
 
 Pinned against the pages' worked numbers, closed forms, brute force, a
 library special case and invariants in ``tests/test_oracle_*.py``.
