@@ -17,7 +17,8 @@ decode step appends one token per sequence (positions advance each step).
 A mixed prefill + decode workload (8 prompts chunked alongside 56 decoders,
 split_equal) is reported under "mixed", and the iteration-level batching
 loop (the native scheduler admitting, retiring and assembling every
-iteration over a stream of requests) under "serving".
+iteration over a stream of requests) under "serving", and save / restore of
+a 2048-position sequence's state under "seq_state".
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -439,6 +440,54 @@ def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk):
 
 
 # ---------------------------------------------------------------------------
+# sequence-state save / restore
+
+def bench_seq_state(dev, n_pos=2048, reps=10):
+    """Save and restore of one n_pos-position sequence of the Qwen3-0.6B
+    shape (28 layers, F16 rows of 2 KiB): each save gathers 2 * 28 * n_pos
+    scattered cache rows into the blob, each restore scatters them back into
+    freshly placed cells (after reading the blob's metadata back)."""
+    import torch
+    from ubatch_attention_paged_amd import Context
+    L, E = 28, 1024
+    order = np.random.default_rng(9).permutation(4096).astype(np.int32)[None, :]
+    ctx = Context(L, 16, 8, 128, 4096, 1, 4, 2048, 512, device=dev, attend_layers=L, cell_order=order)
+    g = torch.Generator(device=dev)
+    g.manual_seed(21)
+    st, ubs, _ = ctx.split(n_pos, list(range(n_pos)), [(0,)] * n_pos, None)
+    assert st == 0
+    for u in ubs:
+        ctx.store(u, 0, [torch.randn((u.n_tokens, E), generator=g, device=dev) for _ in range(L)],
+                  [torch.randn((u.n_tokens, E), generator=g, device=dev) for _ in range(L)])
+    blob = torch.empty(ctx.state_size(0), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        ctx.state_save(0, blob)
+        ctx.state_load(1, blob)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        ctx.state_save(0, blob)
+        e1.record()
+    torch.cuda.synchronize()
+    save_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ctx.state_load(1, blob)
+    torch.cuda.synchronize()
+    load_ms = 1e3 * (time.perf_counter() - t0) / reps
+    payload = 2 * L * n_pos * E * 2
+    moved = 2 * payload                       # each row read once and written once
+    res = dict(workload=f"one {n_pos}-position sequence, 28 layers, 8 KV heads x 128, shuffled cells",
+               blob_bytes=int(blob.numel()), save_ms=round(save_ms, 4),
+               save_gbs=round(moved / (save_ms * 1e-3) / 1e9, 1),
+               save_hbm_frac=round(moved / (save_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+               load_ms_wall=round(load_ms, 4), load_gbs_wall=round(moved / (load_ms * 1e-3) / 1e9, 1))
+    ctx.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # oracle on the host cores
 
 def cpu_baseline(wl, budget_s=25.0):
@@ -509,6 +558,7 @@ def main():
                     help="only the decode workloads (for profiling their kernels alone)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode workload")
     ap.add_argument("--no-serving", action="store_true", help="skip the iteration-level batching loop")
+    ap.add_argument("--no-seq-state", action="store_true", help="skip sequence-state save / restore")
     ap.add_argument("--serving-iters", type=int, default=200, help="timed iterations of the serving loop")
     ap.add_argument("--decode-workload", choices=["cb_decode", "prefix_decode"], action="append",
                     help="restrict the decode runs to this workload (repeatable)")
@@ -597,6 +647,11 @@ def main():
             f"{sv['positions_per_s']:,.0f} positions/s, {sv['ms_per_iteration']:.3f} ms/iteration, "
             f"scheduler {sv['sched_step_us']['mean']:.1f} us/iteration")
         line["serving"] = sv
+    if not args.no_seq_state:
+        ss = bench_seq_state(dev)
+        log(f"[bench] seq state: save {ss['save_ms']:.3f} ms ({ss['save_gbs']:.0f} GB/s), "
+            f"load {ss['load_ms_wall']:.3f} ms wall")
+        line["seq_state"] = ss
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(wl)

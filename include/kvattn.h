@@ -222,6 +222,47 @@ int kvattn_plan_stats(const kvattn_ctx *ctx, int32_t only_outputs, int32_t *n_cl
                       int32_t *n_items_valu, int32_t *n_items_mfma, int32_t *n_partial_rows,
                       int32_t *n_reduced);
 
+/* ---- sequence state: save / restore one sequence's cached K/V ------------
+ *
+ * The serialized form follows the .bin dump of "What does llama.cpp's KV
+ * cache actually look like in memory?" ("Opening the .bin dump"): leading
+ * metadata, then one record per layer for K (layers 0 .. n_layer-1), then
+ * one per layer for V; each record is a 12-byte header followed by the
+ * sequence's rows (n_head_kv * head_dim F16 values each).  The page fixes
+ * only the sizes; the fields are this library's, all little-endian:
+ *   bytes  0..79   "KVSS", u32 version 1, u32 n_layer, u32 n_head_kv,
+ *                  u32 head_dim, u32 n_cells, u32 K type, u32 V type
+ *                  (1 = F16), u64 row bytes, u64 offset of the first record
+ *                  (80 + 4 n_cells), u64 total bytes, 24 zero bytes;
+ *   then n_cells int32 positions, ascending;
+ *   record header: u32 type (1 = F16), u64 row bytes.
+ * Total = 80 + 4 n + 2 n_layer (12 + n row_bytes): 803,596 bytes for 7
+ * cells of the page's 28-layer model, first K record at byte 108.
+ * A sequence's cells are the committed cells whose sequence set holds it
+ * (shared prefix cells included), ordered by position.  The blob holds
+ * positions, not cell indices, so it restores into any free cells. */
+
+/* HOST-ONLY.  Bytes kvattn_seq_state_save will write for seq_id. */
+int kvattn_seq_state_size(const kvattn_ctx *ctx, int32_t seq_id, size_t *bytes);
+
+/* Serialize seq_id into dst: a 4-byte aligned device buffer of cap bytes
+ * (>= kvattn_seq_state_size, else KVATTN_ENOMEM).  *written (may be NULL)
+ * receives the size.  Reads the cache rows on hip_stream, after the stores
+ * enqueued there before; asynchronous. */
+int kvattn_seq_state_save(kvattn_ctx *ctx, int32_t seq_id, void *dst, size_t cap, size_t *written,
+                          void *hip_stream);
+
+/* Restore a blob (4-byte aligned device buffer of `bytes`) as sequence
+ * seq_id of this context: the blob's geometry must match (else
+ * KVATTN_EINVAL, nothing changed); seq_id's cells are replaced by one new
+ * cell per saved position in its stream (seq_id % n_stream), lowest free
+ * rank first -- KVATTN_NO_SLOT, nothing changed, when the free cells plus
+ * those only seq_id holds are too few.  The cells are committed at once
+ * (the device cell mirror follows at the next ubatch commit, as after
+ * kvattn_seq_rm).  Reads the metadata back first (synchronises
+ * hip_stream), then copies the rows into the cells on hip_stream. */
+int kvattn_seq_state_load(kvattn_ctx *ctx, int32_t seq_id, const void *src, size_t bytes, void *hip_stream);
+
 /* HOST-ONLY.  The context's parameters as in effect: n_batch and n_ubatch
  * clamped, kq_scale and attend_layers defaulted, split_mode resolved (never
  * AUTO).  Pointer fields and workspace_bytes are zero. */

@@ -286,3 +286,28 @@ def test_create_accepts_largest_layer_tensor():
     # just below 2 GiB per layer tensor: (2^20 - 64) cells x 1024 numbers x 2 B
     ctx = K.Context(1, 8, 8, 128, kv_size=(1 << 20) - 64, n_seq_max=1)
     assert 0 < ctx.n_kv() <= (1 << 20) - 64
+
+
+def test_seq_state_size_matches_oracle():
+    from oracle import seqstate as S
+    wl = W.prefix_decode(n_seq=4, prefix=20, private=5, n_layer=2, kv_size=128)
+    ctx, eng = host_ctx(wl), oracle_for(wl)
+    for bt in wl.batches:
+        ubs, rubs = compare_split(ctx, eng, bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        commit_all(ctx, eng, ubs, rubs)
+    ctx.seq_rm(2, 22, -1)
+    eng.seq_rm(2, 22, -1)
+    for seq in range(wl.n_seq_max):
+        n = len(S.sequence_cells(eng, seq)[1])
+        assert ctx.state_size(seq) == S.state_bytes(wl.n_layer, wl.n_head_kv, wl.head_dim, n)
+    n0 = 20 + 5 + 1                            # shared prefix, private cells, the decode token
+    assert ctx.state_size(0) == 80 + 4 * n0 + 2 * 2 * (12 + n0 * wl.E * 2)
+    with pytest.raises(K.KvattnError):
+        ctx.state_size(wl.n_seq_max)
+    # save / load need the GPU
+    with pytest.raises(K.KvattnError) as e:
+        K.kvattn_seq_state_save(ctx.ctx, 0, 4096, 1 << 20)
+    assert e.value.code == K.KVATTN_ENODEV
+    with pytest.raises(K.KvattnError) as e:
+        K.kvattn_seq_state_load(ctx.ctx, 0, 4096, 1 << 20)
+    assert e.value.code == K.KVATTN_ENODEV

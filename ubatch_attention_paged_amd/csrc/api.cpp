@@ -95,6 +95,10 @@ struct kvattn_ctx {
   bool pending_fused = false;
   int fused_stage = 0;
   const int32_t* fused_dst_rows = nullptr;
+  // sequence-state restore reads the blob's metadata back through this
+  void* peek = nullptr;
+  size_t peek_cap = 0;
+  char* peek_dev = nullptr;
   char* arena() { return ws + wl.arena; }
 
   int fail(int code, const std::string& msg) {
@@ -128,6 +132,28 @@ int ensure_device(kvattn_ctx* c) {
   HIP_TRY(c, hipMemset(c->ws + c->wl.cmask, 0, sc * 8));
   HIP_TRY(c, hipDeviceSynchronize());
   c->dev_ready = true;
+  return KVATTN_OK;
+}
+
+// The next pinned staging buffer of the ring, at least `bytes` large, once
+// the GPU work that last read it has finished.  Its event must be recorded
+// after the work that reads it now.
+int acquire_stage(kvattn_ctx* c, size_t bytes, int* out) {
+  const int st = c->stage_next;
+  c->stage_next = (st + 1) % kStages;
+  if (c->ev_used[st]) HIP_TRY(c, hipEventSynchronize(c->ev[st]));
+  if (c->stage_cap[st] < bytes) {
+    if (c->stage[st]) HIP_TRY(c, hipHostFree(c->stage[st]));
+    c->stage[st] = nullptr;
+    c->stage_cap[st] = 0;
+    const size_t cap = std::max<size_t>(bytes, 1 << 20);
+    HIP_TRY(c, hipHostMalloc(&c->stage[st], cap, hipHostMallocDefault));
+    c->stage_cap[st] = cap;
+    void* dv = nullptr;
+    HIP_TRY(c, hipHostGetDevicePointer(&dv, c->stage[st], 0));
+    c->stage_dev[st] = static_cast<char*>(dv);
+  }
+  *out = st;
   return KVATTN_OK;
 }
 
@@ -180,19 +206,8 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
     return c->fail(KVATTN_ENOMEM, "ubatch plan exceeds the workspace plan arena");
   }
   // stage
-  const int st = c->stage_next;
-  c->stage_next = (st + 1) % kStages;
-  if (c->ev_used[st]) HIP_TRY(c, hipEventSynchronize(c->ev[st]));
-  if (c->stage_cap[st] < A.total) {
-    if (c->stage[st]) HIP_TRY(c, hipHostFree(c->stage[st]));
-    c->stage[st] = nullptr;
-    const size_t cap = std::max<size_t>(A.total, 1 << 20);
-    HIP_TRY(c, hipHostMalloc(&c->stage[st], cap, hipHostMallocDefault));
-    c->stage_cap[st] = cap;
-    void* dv = nullptr;
-    HIP_TRY(c, hipHostGetDevicePointer(&dv, c->stage[st], 0));
-    c->stage_dev[st] = static_cast<char*>(dv);
-  }
+  int st = 0;
+  if (int rc = acquire_stage(c, A.total, &st)) return rc;
   char* b = static_cast<char*>(c->stage[st]);
   auto copy = [&](size_t at, const void* src, size_t bytes) { if (bytes) std::memcpy(b + at, src, bytes); };
   copy(A.classes, P0.classes.data(), P0.classes.size() * sizeof(ClassInfo));
@@ -338,6 +353,7 @@ void kvattn_destroy(kvattn_ctx* c) {
       if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
       if (c->stage[i]) (void)hipHostFree(c->stage[i]);
     }
+    if (c->peek) (void)hipHostFree(c->peek);
 
   }
   delete c;
@@ -567,6 +583,185 @@ int kvattn_seq_rm(kvattn_ctx* c, int32_t seq_id, int32_t p0, int32_t p1) {
 }
 
 int32_t kvattn_seq_pos_max(const kvattn_ctx* c, int32_t seq_id) { return c ? c->core.seq_pos_max(seq_id) : -1; }
+
+}  // extern "C"
+
+// ---- sequence state ("Opening the .bin dump") ------------------------------
+
+namespace {
+
+constexpr uint32_t kStateMagic = 0x5353564Bu;     // "KVSS" little-endian
+constexpr uint32_t kStateVersion = 1;
+constexpr size_t kStateFixed = 80;
+constexpr size_t kStateRecordHeader = 12;
+
+struct StateGeom {
+  size_t n, row, rec0, stride, total;
+};
+
+StateGeom state_geom(const Geometry& g, size_t n) {
+  StateGeom sg;
+  sg.n = n;
+  sg.row = static_cast<size_t>(g.E()) * 2;
+  sg.rec0 = kStateFixed + 4 * n;
+  sg.stride = kStateRecordHeader + n * sg.row;
+  sg.total = sg.rec0 + 2 * static_cast<size_t>(g.n_layer) * sg.stride;
+  return sg;
+}
+
+int ensure_peek(kvattn_ctx* c, size_t bytes) {
+  if (c->peek_cap >= bytes) return KVATTN_OK;
+  if (c->peek) HIP_TRY(c, hipHostFree(c->peek));
+  c->peek = nullptr;
+  c->peek_cap = 0;
+  const size_t cap = std::max<size_t>(bytes, 1 << 16);
+  HIP_TRY(c, hipHostMalloc(&c->peek, cap, hipHostMallocDefault));
+  c->peek_cap = cap;
+  void* dv = nullptr;
+  HIP_TRY(c, hipHostGetDevicePointer(&dv, c->peek, 0));
+  c->peek_dev = static_cast<char*>(dv);
+  return KVATTN_OK;
+}
+
+template <class T>
+T rd(const char* p, size_t at) {
+  T v;
+  std::memcpy(&v, p + at, sizeof(T));
+  return v;
+}
+
+StateArgs state_args(kvattn_ctx* c, const StateGeom& sg, int32_t il0, int32_t n_il) {
+  StateArgs a{};
+  for (int i = 0; i < n_il; ++i) {
+    a.k[i] = static_cast<_Float16*>(c->K[il0 + i]);
+    a.v[i] = static_cast<_Float16*>(c->V[il0 + i]);
+  }
+  a.n = static_cast<int32_t>(sg.n);
+  a.n_layer = c->core.geo().n_layer;
+  a.il0 = il0;
+  a.n_il = n_il;
+  a.row_words = static_cast<int32_t>(sg.row / 4);
+  a.rec0 = sg.rec0;
+  a.rec_stride = sg.stride;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_seq_state_size(const kvattn_ctx* c, int32_t seq_id, size_t* bytes) {
+  if (!c || !bytes) return KVATTN_EINVAL;
+  std::vector<int32_t> cells, pos;
+  if (c->core.seq_cells(seq_id, cells, pos) < 0) return KVATTN_EINVAL;
+  *bytes = state_geom(c->core.geo(), cells.size()).total;
+  return KVATTN_OK;
+}
+
+int kvattn_seq_state_save(kvattn_ctx* c, int32_t seq_id, void* dst, size_t cap, size_t* written, void* hip_stream) {
+  if (!c) return KVATTN_EINVAL;
+  if (!dst || (reinterpret_cast<uintptr_t>(dst) & 3)) return c->fail(KVATTN_EINVAL, "dst is NULL or not 4-byte aligned");
+  std::vector<int32_t> cells, pos;
+  const int st_id = c->core.seq_cells(seq_id, cells, pos);
+  if (st_id < 0) return c->fail(KVATTN_EINVAL, "sequence id out of range");
+  const Geometry& g = c->core.geo();
+  const StateGeom sg = state_geom(g, cells.size());
+  if (cap < sg.total) return c->fail(KVATTN_ENOMEM, "dst is smaller than kvattn_seq_state_size");
+  int rc;
+  if ((rc = ensure_device(c))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  // staging: leading metadata (what the blob starts with), then the rows
+  // to gather (stream * kv_size + cell)
+  int st = 0;
+  if ((rc = acquire_stage(c, sg.rec0 + 4 * sg.n, &st))) return rc;
+  char* b = static_cast<char*>(c->stage[st]);
+  std::memset(b, 0, kStateFixed);
+  const uint32_t head[8] = {kStateMagic, kStateVersion, static_cast<uint32_t>(g.n_layer),
+                            static_cast<uint32_t>(g.n_head_kv), static_cast<uint32_t>(g.head_dim),
+                            static_cast<uint32_t>(sg.n), kStateTypeF16, kStateTypeF16};
+  std::memcpy(b, head, sizeof(head));
+  const uint64_t sizes[3] = {sg.row, sg.rec0, sg.total};
+  std::memcpy(b + 32, sizes, sizeof(sizes));
+  if (sg.n) std::memcpy(b + kStateFixed, pos.data(), 4 * sg.n);
+  int32_t* rows = reinterpret_cast<int32_t*>(b + sg.rec0);
+  for (size_t i = 0; i < sg.n; ++i) rows[i] = st_id * g.kv_size + cells[i];
+  for (int32_t l0 = 0; l0 < g.n_layer; l0 += kMaxLayersPerLaunch) {
+    const int32_t n_il = std::min<int32_t>(kMaxLayersPerLaunch, g.n_layer - l0);
+    StateArgs a = state_args(c, sg, l0, n_il);
+    a.cells = reinterpret_cast<const int32_t*>(c->stage_dev[st] + sg.rec0);
+    a.blob_w = static_cast<uint32_t*>(dst);
+    a.prefix = reinterpret_cast<const uint32_t*>(c->stage_dev[st]);
+    a.prefix_words = static_cast<int32_t>(sg.rec0 / 4);
+    HIP_TRY(c, launch_state_copy(a, true, s));
+  }
+  HIP_TRY(c, hipEventRecord(c->ev[st], s));
+  c->ev_used[st] = true;
+  if (written) *written = sg.total;
+  return KVATTN_OK;
+}
+
+int kvattn_seq_state_load(kvattn_ctx* c, int32_t seq_id, const void* src, size_t bytes, void* hip_stream) {
+  if (!c) return KVATTN_EINVAL;
+  if (!src || (reinterpret_cast<uintptr_t>(src) & 3)) return c->fail(KVATTN_EINVAL, "src is NULL or not 4-byte aligned");
+  if (seq_id < 0 || seq_id >= c->core.geo().n_seq_max) return c->fail(KVATTN_EINVAL, "sequence id out of range");
+  if (bytes < kStateFixed) return c->fail(KVATTN_EINVAL, "blob shorter than its metadata");
+  int rc;
+  if ((rc = ensure_device(c))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const Geometry& g = c->core.geo();
+  // 1. the fixed metadata
+  if ((rc = ensure_peek(c, kStateFixed))) return rc;
+  HIP_TRY(c, hipMemcpyAsync(c->peek, src, kStateFixed, hipMemcpyDeviceToHost, s));
+  HIP_TRY(c, hipStreamSynchronize(s));
+  const char* pk = static_cast<const char*>(c->peek);
+  const uint32_t n = rd<uint32_t>(pk, 20);
+  if (rd<uint32_t>(pk, 0) != kStateMagic || rd<uint32_t>(pk, 4) != kStateVersion)
+    return c->fail(KVATTN_EINVAL, "not a sequence-state blob");
+  if (rd<uint32_t>(pk, 8) != static_cast<uint32_t>(g.n_layer) || rd<uint32_t>(pk, 12) != static_cast<uint32_t>(g.n_head_kv) ||
+      rd<uint32_t>(pk, 16) != static_cast<uint32_t>(g.head_dim) || rd<uint32_t>(pk, 24) != kStateTypeF16 ||
+      rd<uint32_t>(pk, 28) != kStateTypeF16)
+    return c->fail(KVATTN_EINVAL, "blob geometry or type does not match the context");
+  if (n > static_cast<uint32_t>(g.kv_size)) return c->fail(KVATTN_EINVAL, "more saved cells than a stream holds");
+  const StateGeom sg = state_geom(g, n);
+  if (rd<uint64_t>(pk, 32) != sg.row || rd<uint64_t>(pk, 40) != sg.rec0 || rd<uint64_t>(pk, 48) != sg.total ||
+      bytes < sg.total)
+    return c->fail(KVATTN_EINVAL, "blob sizes are inconsistent");
+  // 2. positions and every record header
+  const int32_t n_rec = 2 * g.n_layer;
+  const size_t peek_bytes = 4 * sg.n + 12 * static_cast<size_t>(n_rec);
+  if ((rc = ensure_peek(c, peek_bytes))) return rc;
+  if (sg.n) HIP_TRY(c, hipMemcpyAsync(c->peek, static_cast<const char*>(src) + kStateFixed, 4 * sg.n,
+                                      hipMemcpyDeviceToHost, s));
+  HIP_TRY(c, launch_state_peek(static_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(c->peek_dev + 4 * sg.n),
+                               n_rec, sg.rec0, sg.stride, s));
+  HIP_TRY(c, hipStreamSynchronize(s));
+  pk = static_cast<const char*>(c->peek);
+  for (int32_t r = 0; r < n_rec; ++r) {
+    const size_t at = 4 * sg.n + 12 * static_cast<size_t>(r);
+    if (rd<uint32_t>(pk, at) != kStateTypeF16 || rd<uint64_t>(pk, at + 4) != sg.row)
+      return c->fail(KVATTN_EINVAL, "a record header does not match");
+  }
+  std::vector<int32_t> pos(sg.n), cells;
+  if (sg.n) std::memcpy(pos.data(), pk, 4 * sg.n);
+  // 3. placement (all-or-nothing), then the rows into the new cells
+  if ((rc = c->core.seq_restore(seq_id, pos.data(), static_cast<int32_t>(sg.n), cells, c->err))) return rc;
+  if (sg.n == 0) return KVATTN_OK;
+  int st = 0;
+  if ((rc = acquire_stage(c, 4 * sg.n, &st))) return rc;
+  int32_t* rows = static_cast<int32_t*>(c->stage[st]);
+  const int32_t sid = seq_id % g.n_stream;
+  for (size_t i = 0; i < sg.n; ++i) rows[i] = sid * g.kv_size + cells[i];
+  for (int32_t l0 = 0; l0 < g.n_layer; l0 += kMaxLayersPerLaunch) {
+    const int32_t n_il = std::min<int32_t>(kMaxLayersPerLaunch, g.n_layer - l0);
+    StateArgs a = state_args(c, sg, l0, n_il);
+    a.cells = reinterpret_cast<const int32_t*>(c->stage_dev[st]);
+    a.blob_r = static_cast<const uint32_t*>(src);
+    HIP_TRY(c, launch_state_copy(a, false, s));
+  }
+  HIP_TRY(c, hipEventRecord(c->ev[st], s));
+  c->ev_used[st] = true;
+  return KVATTN_OK;
+}
 
 int kvattn_get_params(const kvattn_ctx* c, kvattn_params* out) {
   if (!c || !out) return KVATTN_EINVAL;

@@ -388,6 +388,54 @@ int HostCore::seq_rm(int32_t seq, int32_t p0, int32_t p1) {
   return KVATTN_OK;
 }
 
+int HostCore::seq_cells(int32_t seq, std::vector<int32_t>& cells, std::vector<int32_t>& pos) const {
+  cells.clear();
+  pos.clear();
+  if (seq < 0 || seq >= g_.n_seq_max) return -1;
+  const int s = seq % g_.n_stream;
+  const Stream& S = st_[s];
+  std::vector<std::pair<int32_t, int32_t>> v;
+  for (int32_t j = 0; j < S.umax; ++j)
+    if (S.pos[j] >= 0 && (S.mask[j] >> seq & 1)) v.push_back({S.pos[j], j});
+  std::sort(v.begin(), v.end());
+  for (const auto& pc : v) {
+    pos.push_back(pc.first);
+    cells.push_back(pc.second);
+  }
+  return s;
+}
+
+int HostCore::seq_restore(int32_t seq, const int32_t* pos, int32_t n, std::vector<int32_t>& cells,
+                          std::string& err) {
+  if (seq < 0 || seq >= g_.n_seq_max || n < 0) {
+    err = "sequence id out of range";
+    return KVATTN_EINVAL;
+  }
+  for (int32_t i = 0; i < n; ++i)
+    if (pos[i] < 0) {
+      err = "negative position";
+      return KVATTN_EINVAL;
+    }
+  const int s = seq % g_.n_stream;
+  Stream& S = st_[s];
+  const uint64_t bit = 1ULL << seq;
+  int32_t own = 0;
+  for (int32_t j = 0; j < S.umax; ++j)
+    if (S.pos[j] >= 0 && S.mask[j] == bit) ++own;
+  if (S.n_avail + own < n) {
+    err = "no room in the stream for the saved cells";
+    return KVATTN_NO_SLOT;
+  }
+  seq_rm(seq, -1, -1);
+  cells.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    cells[i] = pop_cell(s);
+    set_cell(s, cells[i], pos[i], bit);
+  }
+  latest_ = -1;                       // the device mirror follows at the next commit
+  return KVATTN_OK;
+}
+
 int32_t HostCore::seq_pos_max(int32_t seq) const {
   if (seq < 0 || seq >= g_.n_seq_max) return -1;
   int32_t best = -1;

@@ -78,6 +78,13 @@ class HostCore {
   int build_plan(int k, bool only_outputs, Plan& plan, std::string& err) const;
 
   int seq_rm(int32_t seq, int32_t p0, int32_t p1);
+  // Committed cells holding seq (all in stream seq % n_stream), ordered by
+  // (position, cell).  Returns the stream, or -1 for a bad id.
+  int seq_cells(int32_t seq, std::vector<int32_t>& cells, std::vector<int32_t>& pos) const;
+  // Replace seq's cells by n new ones at positions pos[], lowest free rank
+  // first, committed at once.  KVATTN_NO_SLOT (nothing changed) when the
+  // stream's free cells plus the cells only seq holds are fewer than n.
+  int seq_restore(int32_t seq, const int32_t* pos, int32_t n, std::vector<int32_t>& cells, std::string& err);
   int32_t seq_pos_max(int32_t seq) const;
   int32_t n_kv() const;
   void get_cells(int32_t s, int32_t* pos, uint64_t* mask) const;

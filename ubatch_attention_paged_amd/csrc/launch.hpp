@@ -83,7 +83,30 @@ struct MaskArgs {
   int32_t n_rows, n_kv, kv_size, causal;
 };
 
+// Sequence-state records (kernels_state.hip).  Word offsets: the blob is
+// 4-byte aligned; record r = kind * n_layer + layer starts at byte
+// rec0 + r * rec_stride with a 3-word header, then n rows of row_words.
+constexpr uint32_t kStateTypeF16 = 1;
+struct StateArgs {
+  _Float16* k[kMaxLayersPerLaunch];   // layers il0 .. il0 + n_il - 1
+  _Float16* v[kMaxLayersPerLaunch];
+  const int32_t* cells;               // [n] stream * kv_size + cell, in record row order
+  uint32_t* blob_w;                   // save: destination
+  const uint32_t* blob_r;             // restore: source
+  const uint32_t* prefix;             // save: the leading metadata words
+  int32_t prefix_words;
+  int32_t n;                          // saved cells
+  int32_t n_layer;                    // every layer (record numbering)
+  int32_t il0, n_il;
+  int32_t row_words;
+  uint64_t rec0;                      // bytes before the first record
+  uint64_t rec_stride;                // bytes per record
+};
+
 hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s);
+hipError_t launch_state_copy(const StateArgs& a, bool save, hipStream_t s);
+hipError_t launch_state_peek(const uint32_t* blob, uint32_t* out, int32_t n_rec, uint64_t rec0, uint64_t rec_stride,
+                             hipStream_t s);
 hipError_t launch_commit(const CsrArgs& a, hipStream_t s);
 // a commit small enough for one workgroup (launch_store_commit can carry it)
 bool commit_is_small(const CsrArgs& a);

@@ -103,6 +103,11 @@ SIGNATURES = {
     "kvattn_seq_pos_max": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
     "kvattn_plan_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, _i32p, _i32p, _i32p, _i32p, _i32p]),
     "kvattn_get_params": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_params)]),
+    "kvattn_seq_state_size": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]),
+    "kvattn_seq_state_save": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.POINTER(ctypes.c_size_t), ctypes.c_void_p]),
+    "kvattn_seq_state_load": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                             ctypes.c_void_p]),
     "kvattn_last_error": (ctypes.c_char_p, [ctypes.c_void_p]),
     "kvattn_sched_create": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_sched_params),
                                            ctypes.POINTER(ctypes.c_void_p)]),
@@ -341,6 +346,32 @@ def kvattn_seq_pos_max(ctx, seq_id) -> int:
     return load().kvattn_seq_pos_max(ctx, seq_id)
 
 
+def kvattn_seq_state_size(ctx, seq_id) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().kvattn_seq_state_size(ctx, seq_id, ctypes.byref(n))
+    if rc != 0:
+        raise KvattnError(rc, "kvattn_seq_state_size: sequence id out of range")
+    return n.value
+
+
+def kvattn_seq_state_save(ctx, seq_id, dst_ptr, cap, stream=0) -> int:
+    n = ctypes.c_size_t(0)
+    rc = load().kvattn_seq_state_save(ctx, seq_id, ctypes.c_void_p(dst_ptr), cap, ctypes.byref(n),
+                                      ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+    return n.value
+
+
+def kvattn_seq_state_load(ctx, seq_id, src_ptr, nbytes, stream=0) -> int:
+    """Returns 0, or KVATTN_NO_SLOT when the cells do not fit (nothing
+    changed); invalid blobs raise."""
+    rc = load().kvattn_seq_state_load(ctx, seq_id, ctypes.c_void_p(src_ptr), nbytes, ctypes.c_void_p(stream))
+    if rc < 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+    return rc
+
+
 def kvattn_get_params(ctx) -> kvattn_params:
     p = kvattn_params()
     rc = load().kvattn_get_params(ctx, ctypes.byref(p))
@@ -459,6 +490,24 @@ class Context:
 
     def seq_rm(self, seq_id, p0=-1, p1=-1):
         kvattn_seq_rm(self.ctx, seq_id, p0, p1)
+
+    def state_size(self, seq_id):
+        return kvattn_seq_state_size(self.ctx, seq_id)
+
+    def state_save(self, seq_id, out=None, stream=None):
+        """Serialized state of a sequence as a uint8 device tensor (``out``
+        when given, else a new one of exactly the size)."""
+        import torch
+        n = self.state_size(seq_id)
+        if out is None:
+            out = torch.empty(n, dtype=torch.uint8, device=self.device)
+        kvattn_seq_state_save(self.ctx, seq_id, out.data_ptr(), out.numel(), self._stream(stream))
+        return out[:n]
+
+    def state_load(self, seq_id, blob, stream=None):
+        """Restore a uint8 device tensor as sequence seq_id; returns 0 or
+        KVATTN_NO_SLOT."""
+        return kvattn_seq_state_load(self.ctx, seq_id, blob.data_ptr(), blob.numel(), self._stream(stream))
 
     def n_kv(self):
         return kvattn_n_kv(self.ctx)
