@@ -559,6 +559,8 @@ def main():
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode workload")
     ap.add_argument("--no-serving", action="store_true", help="skip the iteration-level batching loop")
     ap.add_argument("--no-seq-state", action="store_true", help="skip sequence-state save / restore")
+    ap.add_argument("--only", choices=["serving", "seq_state"],
+                    help="run just this leg and print its result (for profiling its kernels alone)")
     ap.add_argument("--serving-iters", type=int, default=200, help="timed iterations of the serving loop")
     ap.add_argument("--decode-workload", choices=["cb_decode", "prefix_decode"], action="append",
                     help="restrict the decode runs to this workload (repeatable)")
@@ -573,6 +575,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.only == "serving":
+        from synthetic.serving import qwen_serving
+        print(json.dumps({"serving": bench_serving(qwen_serving(), dev, 300, args.serving_iters, args.layer_chunk)}),
+              flush=True)
+        return
+    if args.only == "seq_state":
+        print(json.dumps({"seq_state": bench_seq_state(dev)}), flush=True)
+        return
     decode_names = args.decode_workload or ["cb_decode", "prefix_decode"]
     decode_wls = [(name, W.by_name(name)) for name in decode_names]
     if args.decode_only:
