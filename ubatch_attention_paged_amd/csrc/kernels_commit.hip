@@ -13,6 +13,8 @@
 // query's first sequence id and, under causal attention, its position is
 // not later than the query's.  The class lists group cells by sequence set;
 // the attention kernels apply the position test per (query, cell).
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -50,17 +52,15 @@ hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ __launch_bounds__(256) void k_apply_updates(CsrArgs a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= a.n_updates) return;
-  const CellUpdate u = a.updates[i];
-  a.cpos[u.idx] = u.pos;
-  a.cmask[u.idx] = u.mask;
-}
-
-__global__ __launch_bounds__(256) void k_fill_zero(int32_t* p, int64_t n) {
+// Mirror updates, and the per-(class, segment) counts cleared, in one launch.
+__global__ __launch_bounds__(256) void k_apply_updates(CsrArgs a, int64_t n_counts) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0;
+  if (i < a.n_updates) {
+    const CellUpdate u = a.updates[i];
+    a.cpos[u.idx] = u.pos;
+    a.cmask[u.idx] = u.mask;
+  }
+  if (i < n_counts) a.counts[i] = 0;
 }
 
 // Class of each cell j < n_kv of stream blockIdx.y, by binary search of its
@@ -95,21 +95,33 @@ __global__ __launch_bounds__(256) void k_csr_classify(CsrArgs a) {
 }
 
 // Per class: segment counts -> absolute start offsets in the csr arrays.
-__global__ __launch_bounds__(64) void k_csr_scan(CsrArgs a) {
+// Thread t owns a contiguous run of segments: one round of independent loads
+// for its run's total, a workgroup scan of the totals, then its run's
+// offsets.
+constexpr int kScanThreads = 256;
+__global__ __launch_bounds__(kScanThreads) void k_csr_scan(CsrArgs a) {
+  __shared__ int32_t wsum[kScanThreads / 64];
   const int c = blockIdx.x;
-  const int lane = threadIdx.x;
-  int32_t running = a.classes[c].cell_off;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   int32_t* row = a.counts + static_cast<int64_t>(c) * a.n_seg;
-  for (int base = 0; base < a.n_seg; base += 64) {
-    const int k = base + lane;
-    const int v = k < a.n_seg ? row[k] : 0;
-    int incl = v;
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
-    if (k < a.n_seg) row[k] = running + incl - v;
-    running += __shfl(incl, 63);
+  const int per = (a.n_seg + kScanThreads - 1) / kScanThreads;
+  const int k0 = min(a.n_seg, t * per), k1 = min(a.n_seg, k0 + per);
+  int total = 0;
+  for (int k = k0; k < k1; ++k) total += row[k];
+  int incl = total;                                  // inclusive scan over the wavefront
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = a.classes[c].cell_off;
+  for (int j = 0; j < w; ++j) before += wsum[j];
+  int running = before + incl - total;               // exclusive start of this thread's run
+  for (int k = k0; k < k1; ++k) {
+    const int v = row[k];
+    row[k] = running;
+    running += v;
   }
 }
 
@@ -121,20 +133,24 @@ __global__ __launch_bounds__(256) void k_csr_scatter(CsrArgs a) {
   const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
   const int cls = j < a.n_kv ? a.cellcls[idx] : -1;
   const int seg = j >> 6;
+  // rank among the earlier cells of the same class in this segment; the
+  // class offsets are then read once, all lanes at a time
+  int rank = 0;
   uint64_t active = ballot(cls >= 0);
   while (active) {
     const int leader = __builtin_ctzll(active);
     const int c = readlane_i(cls, leader);
     const uint64_t same = ballot(cls == c);
-    if (cls == c) {
-      const int dst = a.counts[static_cast<int64_t>(c) * a.n_seg + seg] + __popcll(same & lanemask_lt());
-      if (dst < a.csr_cap) {
-        a.csr_cell[dst] = j;
-        a.csr_pos[dst] = a.cpos[idx];
-        a.csr_mask[dst] = a.cmask[idx];
-      }
-    }
+    if (cls == c) rank = __popcll(same & lanemask_lt());
     active &= ~same;
+  }
+  if (cls >= 0) {
+    const int dst = a.counts[static_cast<int64_t>(cls) * a.n_seg + seg] + rank;
+    if (dst < a.csr_cap) {
+      a.csr_cell[dst] = j;
+      a.csr_pos[dst] = a.cpos[idx];
+      a.csr_mask[dst] = a.cmask[idx];
+    }
   }
 }
 
@@ -302,14 +318,14 @@ hipError_t launch_store_commit(const StoreArgs& a, int n_il, const CsrArgs& c, h
 }
 
 hipError_t launch_commit(const CsrArgs& a, hipStream_t s) {
-  if (a.n_updates > 0)
-    hipLaunchKernelGGL(k_apply_updates, dim3((a.n_updates + 255) / 256), dim3(256), 0, s, a);
-  if (a.n_classes == 0) return hipGetLastError();
   const int64_t nc = static_cast<int64_t>(a.n_classes) * a.n_seg;
-  hipLaunchKernelGGL(k_fill_zero, dim3(static_cast<unsigned>((nc + 255) / 256)), dim3(256), 0, s, a.counts, nc);
+  const int64_t n_apply = std::max<int64_t>(a.n_updates, nc);
+  if (n_apply > 0)
+    hipLaunchKernelGGL(k_apply_updates, dim3(static_cast<unsigned>((n_apply + 255) / 256)), dim3(256), 0, s, a, nc);
+  if (a.n_classes == 0) return hipGetLastError();
   const dim3 grid((a.n_kv + 255) / 256, a.n_stream);
   hipLaunchKernelGGL(k_csr_classify, grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_csr_scan, dim3(a.n_classes), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(k_csr_scan, dim3(a.n_classes), dim3(kScanThreads), 0, s, a);
   hipLaunchKernelGGL(k_csr_scatter, grid, dim3(256), 0, s, a);
   if (a.max_class_tiles > 0)
     hipLaunchKernelGGL(k_tile_minmax, dim3(a.n_classes, (a.max_class_tiles + 15) / 16), dim3(256), 0, s, a);
