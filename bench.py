@@ -344,7 +344,7 @@ def bench_mixed(wl, dev, steps, warmup, layer_chunk):
 # ---------------------------------------------------------------------------
 # iteration-level batching loop (native scheduler) over a request stream
 
-def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk):
+def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk, swap_bytes=0):
     """The native loop (retire, admit, assemble) drives the context for
     warm_iters untimed iterations, then timed_iters timed ones.  Every
     iteration splits the assembled batch and, for each ubatch, stores K/V and
@@ -357,7 +357,8 @@ def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk):
                   stream.n_seq_max, stream.token_budget, stream.n_ubatch, device=dev, attend_layers=layer_chunk,
                   split_mode=stream.split_mode)
     sch = Scheduler(ctx, token_budget=stream.token_budget, policy=stream.policy, block_size=stream.block_size,
-                    chunked=stream.chunked, max_requests=stream.n_requests)
+                    chunked=stream.chunked, max_requests=stream.n_requests, preempt=stream.preempt,
+                    swap_bytes=swap_bytes)
     g = torch.Generator(device=dev)
     g.manual_seed(stream.seed)
     nb, HD = stream.token_budget, stream.n_head * stream.head_dim
@@ -375,7 +376,7 @@ def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk):
         it = sch.step()
         t_sched = time.perf_counter() - t0
         n = it.batch.n_tokens
-        info = (n, it.n_decode, 0, it.n_running, it.n_waiting, it.n_preempted, 0, 0)
+        info = (n, it.n_decode, 0, it.n_running, it.n_waiting, it.n_preempted, 0, 0, it.n_swapped_out)
         if n:
             pos = np.ctypeslib.as_array(it.batch.pos, shape=(n,)).astype(np.int64)
             req = np.ctypeslib.as_array(it.req, shape=(n,))
@@ -385,7 +386,7 @@ def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk):
             # cells once for its whole visibility class
             last = np.nonzero(np.append(req[1:] != req[:-1], True))[0]
             info = (n, it.n_decode, int(out.sum()), it.n_running, it.n_waiting, it.n_preempted,
-                    int((pos[last] + 1).sum()), int((pos + 1).sum()))
+                    int((pos[last] + 1).sum()), int((pos + 1).sum()), it.n_swapped_out)
         if n:
             st, ubs, _ = ctx.split_batch(it.batch)
             if st != 0:
@@ -431,6 +432,7 @@ def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk):
                                   p99=round(float(np.percentile(sched_us, 99)), 2)),
                mean_running=round(float(info[:, 3].mean()), 2), mean_waiting=round(float(info[:, 4].mean()), 1),
                decode_slot_frac=round(dec / max(1, slots), 4), preemptions=int(info[:, 5].sum()),
+               swapped_out=int(info[:, 8].sum()), positions_per_generated=round(slots / max(1, gen), 3),
                attend_kv_read_gbs=round(kv_bytes / (attend_ms * 1e-3) / 1e9, 1),
                attend_tflops=round(flops / (attend_ms * 1e-3) / 1e12, 1),
                attend_roofline_frac=round(bound_ms / attend_ms, 4))
@@ -657,6 +659,18 @@ def main():
             f"{sv['positions_per_s']:,.0f} positions/s, {sv['ms_per_iteration']:.3f} ms/iteration, "
             f"scheduler {sv['sched_step_us']['mean']:.1f} us/iteration")
         line["serving"] = sv
+        # the same stream over a cache too small for it: preemption by
+        # recomputation against preemption by swapping ("Where it breaks")
+        pr = {}
+        for mode in ("recompute", "swap"):
+            r = bench_serving(qwen_serving(kv_size=40960, preempt=mode), dev, 300, args.serving_iters,
+                              args.layer_chunk, swap_bytes=2 << 30)
+            pr[mode] = {k: r[k] for k in ("generated_tokens_per_s", "positions_per_s", "ms_per_iteration",
+                                          "preemptions", "swapped_out", "positions_per_generated",
+                                          "mean_running", "sched_step_us")}
+        log(f"[bench] serving under cache pressure (40960 cells): recompute "
+            f"{pr['recompute']['generated_tokens_per_s']:,.0f} tok/s, swap {pr['swap']['generated_tokens_per_s']:,.0f} tok/s")
+        line["serving_pressure"] = dict(workload="qwen_serving over a 40960-cell cache, 2 GiB swap arena", **pr)
     if not args.no_seq_state:
         ss = bench_seq_state(dev)
         log(f"[bench] seq state: save {ss['save_ms']:.3f} ms ({ss['save_gbs']:.0f} GB/s), "

@@ -11,14 +11,21 @@
  *   2. under the paged policy, a stream whose free cells cannot cover one new
  *      cell for each sequence with a single pending position gives memory
  *      back: its most recently admitted sequence is preempted -- cells
- *      released, progress discarded, sampled tokens kept, back to the front
- *      of the waiting queue to be recomputed ("Where it breaks", cache
- *      exhaustion);
+ *      released, sampled tokens kept, back to the front of the waiting
+ *      queue ("Where it breaks", cache exhaustion: swapping or
+ *      recomputation).  KVATTN_PREEMPT_RECOMPUTE discards its progress, so
+ *      it prefills prompt plus sampled tokens again.  KVATTN_PREEMPT_SWAP
+ *      first saves its cells (kvattn_seq_state_save) into the swap arena, at
+ *      the lowest offset where the blob fits (extents rounded up to 256
+ *      bytes), and on re-admission restores them under its new sequence id
+ *      before the batch is placed, so it resumes where it stopped; a victim
+ *      whose blob does not fit is recomputed instead;
  *   3. waiting requests are admitted first come, first served while the
  *      token budget and the cache budget both allow ("The budget that
  *      actually binds"): the worst-case block reservation of the page's
  *      sketch (KVATTN_ADMIT_RESERVE) or, with a paged cache, the cells the
- *      new sequence's pending positions occupy (KVATTN_ADMIT_PAGED);
+ *      new sequence's pending positions occupy, plus its restored cells
+ *      when it was swapped out (KVATTN_ADMIT_PAGED);
  *   4. the batch is assembled: every running sequence with one pending
  *      position (a decoding sequence) contributes it; the remaining budget
  *      goes to pending prompt positions in admission order, split across
@@ -62,6 +69,11 @@ enum {
 
 enum { KVATTN_REQ_WAITING = 0, KVATTN_REQ_RUNNING = 1, KVATTN_REQ_DONE = 2 };
 
+enum {
+  KVATTN_PREEMPT_RECOMPUTE = 0,   /* a preempted sequence prefills prompt + sampled tokens again */
+  KVATTN_PREEMPT_SWAP = 1         /* its cells are saved to the swap arena and restored */
+};
+
 typedef struct kvattn_sched_params {
   int32_t token_budget;     /* positions per iteration; <= 0: the context's (clamped) n_batch.
                                max_running <= token_budget <= n_batch */
@@ -72,6 +84,12 @@ typedef struct kvattn_sched_params {
   int32_t chunked;          /* nonzero: pending prompt positions may be split across iterations;
                                zero: a sequence runs all its pending positions or waits */
   int32_t max_requests;     /* capacity of the request table (requests ever submitted) */
+  int32_t preempt;          /* KVATTN_PREEMPT_*; only the paged policy preempts */
+  void *swap_space;         /* SWAP on a device context: device buffer of swap_bytes, 256-byte
+                               aligned, owned by the caller; holds the saved states */
+  size_t swap_bytes;
+  void *hip_stream;         /* SWAP: the stream the batches run on; saves and restores are enqueued
+                               there (a hipStream_t, NULL = the null stream) */
 } kvattn_sched_params;
 
 /* One iteration as assembled by kvattn_sched_step.  Every array is host
@@ -86,6 +104,10 @@ typedef struct kvattn_sched_iter {
   int32_t n_admitted;           /* requests admitted, in admission order, with their sequence id */
   const int32_t *admitted;
   const int32_t *admitted_seq;
+  int32_t n_swapped_out;        /* preempted requests whose cells went to the swap arena */
+  const int32_t *swapped_out;
+  int32_t n_swapped_in;         /* admitted requests whose cells were restored from it */
+  const int32_t *swapped_in;
   int32_t n_running;            /* after admission */
   int32_t n_waiting;
   int32_t n_decode;             /* slots from sequences with a single pending position */
@@ -106,9 +128,12 @@ void kvattn_sched_destroy(kvattn_sched *s);
  * KVATTN_ENOMEM when max_requests have been submitted. */
 int kvattn_sched_submit(kvattn_sched *s, int32_t n_prompt, int32_t n_generate, int32_t *req_id);
 
-/* HOST-ONLY.  Steps 1-4 above: retire, relieve cache pressure, admit,
- * assemble into *it.  Calls kvattn_seq_rm on the context for every retired
- * or preempted sequence.  KVATTN_ESTATE when the previous iteration was not
+/* HOST-ONLY on a host-only context.  Steps 1-4 above: retire, relieve cache
+ * pressure, admit, assemble into *it.  Calls kvattn_seq_rm on the context
+ * for every retired or preempted sequence; with KVATTN_PREEMPT_SWAP on a
+ * device context it also enqueues the saves and restores on hip_stream
+ * (nothing synchronises; on a host-only context only the placement of
+ * restored cells happens).  KVATTN_ESTATE when the previous iteration was not
  * advanced.  An empty batch (n_tokens 0) with n_running and n_waiting 0
  * means the loop is idle. */
 int kvattn_sched_step(kvattn_sched *s, kvattn_sched_iter *it);

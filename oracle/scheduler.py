@@ -52,6 +52,14 @@ Readings where P4 leaves a step open (each is a choice, stated once):
   prompt plus sampled tokens.  A newcomer is admitted when its pending
   positions fit in the free cells left after that need.
 * ``"reserve"``: ``kv_size // block_size`` blocks per stream; never preempts.
+* Preemption by swapping (``preempt="swap"``, the other option P4 names):
+  the victim's cells are saved first (the sequence-state blob of P3 "Opening
+  the .bin dump", ``blob_bytes``) into a swap arena of ``swap_bytes``, at the
+  lowest offset where it fits (first fit, extents rounded up to 256 bytes);
+  the victim keeps its cached positions and, when re-admitted, its cells
+  are restored into its new sequence id before the batch is placed.  Its
+  admission then needs its cached plus pending positions in free cells.  A
+  victim whose blob does not fit the arena is recomputed instead.
 * A request that can never finish alone (more than ``kv_size`` positions, or
   more blocks than a stream has; without chunking a prompt, or under
   ``"paged"`` a recomputation, longer than the budget) is rejected at
@@ -70,6 +78,15 @@ class SchedError(ValueError):
     """A request or parameter the loop cannot serve."""
 
 
+def blob_bytes(n_layer, row_bytes, n_cells):
+    """Size of a saved sequence state: leading metadata (80 bytes + 4 per
+    cell), then 2 * n_layer records of a 12-byte header and the rows."""
+    return 80 + 4 * n_cells + 2 * n_layer * (12 + n_cells * row_bytes)
+
+
+SWAP_ALIGN = 256
+
+
 @dataclass
 class Request:
     id: int
@@ -80,6 +97,8 @@ class Request:
     generated: int = 0     # tokens sampled so far
     state: int = WAITING
     blocks: int = 0        # "reserve": blocks held
+    swap: tuple = None     # (offset, bytes) of its saved state while swapped out
+    blob: bytes = None
 
     @property
     def known(self):       # prompt plus sampled tokens
@@ -107,8 +126,9 @@ class OracleScheduler:
     """
 
     def __init__(self, kv_size, n_stream, n_seq_max, token_budget, max_running=0,
-                 policy="paged", block_size=1, chunked=True, release=None):
-        if policy not in ("paged", "reserve"):
+                 policy="paged", block_size=1, chunked=True, release=None,
+                 preempt="recompute", swap_bytes=0, n_layer=1, row_bytes=0, swap_out=None, swap_in=None):
+        if policy not in ("paged", "reserve") or preempt not in ("recompute", "swap"):
             raise SchedError("policy")
         max_running = n_seq_max if max_running <= 0 else max_running
         if not (0 < max_running <= n_seq_max) or token_budget < max_running or block_size < 1:
@@ -117,6 +137,10 @@ class OracleScheduler:
         self.budget, self.max_running = token_budget, max_running
         self.policy, self.block_size, self.chunked = policy, block_size, bool(chunked)
         self.release = release
+        self.preempt, self.swap_bytes = preempt, int(swap_bytes)
+        self.n_layer, self.row_bytes = n_layer, row_bytes
+        self.swap_out, self.swap_in = swap_out, swap_in   # callables: seq -> blob, (seq, blob) -> None
+        self.swapped = []          # (offset, bytes, request id) of the arena's live extents, by offset
         self.requests = []
         self.waiting = deque()
         self.running = []
@@ -172,6 +196,35 @@ class OracleScheduler:
             return min(want, self._left)
         return want if want <= self._left else 0
 
+    # -- swap arena (first fit) ---------------------------------------------
+    def _swap_place(self, need):
+        at = 0
+        for off, size, _ in self.swapped:
+            if off - at >= need:
+                return at
+            at = off + size
+        return at if self.swap_bytes - at >= need else None
+
+    def _swap_out(self, r):
+        """Save r's state into the arena; False when it does not fit."""
+        if self.preempt != "swap" or r.n_ctx == 0:
+            return False
+        need = -(-blob_bytes(self.n_layer, self.row_bytes, r.n_ctx) // SWAP_ALIGN) * SWAP_ALIGN
+        at = self._swap_place(need)
+        if at is None:
+            return False
+        r.blob = self.swap_out(r.seq) if self.swap_out is not None else None
+        r.swap = (at, need)
+        self.swapped.append((at, need, r.id))
+        self.swapped.sort()
+        return True
+
+    def _swap_in(self, r):
+        if self.swap_in is not None:
+            self.swap_in(r.seq, r.blob)
+        self.swapped.remove((r.swap[0], r.swap[1], r.id))
+        r.swap, r.blob = None, None
+
     # -- one iteration -------------------------------------------------------
     def step(self):
         """Retire, relieve cache pressure, admit, assemble.  Returns the
@@ -179,7 +232,7 @@ class OracleScheduler:
         batch as parallel lists (request, seq id, position, output flag)."""
         if self.assembled:
             raise SchedError("advance() the previous batch first")
-        retired, preempted, admitted = [], [], []
+        retired, preempted, admitted, swapped_out, swapped_in = [], [], [], [], []
 
         for r in [r for r in self.running if r.finished]:
             self._drop(r)
@@ -190,8 +243,11 @@ class OracleScheduler:
             for s in range(self.n_stream):
                 while self._free_cells(s) < self._need(s):
                     victim = [r for r in self.running if self.stream_of(r.seq) == s][-1]
+                    if self._swap_out(victim):
+                        swapped_out.append(victim.id)
+                    else:
+                        victim.n_ctx = 0
                     self._drop(victim)
-                    victim.n_ctx = 0
                     victim.state = WAITING
                     self.waiting.appendleft(victim)
                     preempted.append(victim.id)
@@ -218,7 +274,7 @@ class OracleScheduler:
                 need = _ceil_div(r.n_prompt + r.n_generate, self.block_size)
                 if need > self.free_blocks[s]:
                     break
-            elif r.pending > self._free_cells(s) - self._need(s):
+            elif r.n_ctx + r.pending > self._free_cells(s) - self._need(s):
                 break
             self.waiting.popleft()
             r.seq, r.state = seq, RUNNING
@@ -226,6 +282,9 @@ class OracleScheduler:
             if self.policy == "reserve":
                 r.blocks = need
                 self.free_blocks[s] -= need
+            if r.swap is not None:
+                self._swap_in(r)
+                swapped_in.append(r.id)
             self.running.append(r)
             admitted.append((r.id, seq))
             self.chunk[r.id] = c
@@ -241,6 +300,7 @@ class OracleScheduler:
                 out.append(1 if p == r.known - 1 else 0)
         self.assembled = True
         return {"retired": retired, "preempted": preempted, "admitted": admitted,
+                "swapped_out": swapped_out, "swapped_in": swapped_in,
                 "req": req, "seq": seq, "pos": pos, "output": out,
                 "n_running": len(self.running), "n_waiting": len(self.waiting)}
 

@@ -45,6 +45,8 @@ class RequestStream:
     chunked: bool = True
     max_running: int = 0
     split_mode: str = "auto"
+    preempt: str = "recompute"
+    swap_bytes: int = 0
     _rows: dict = field(default_factory=dict, repr=False)
 
     @property
@@ -93,13 +95,15 @@ class RequestStream:
     def sched_kwargs(self):
         return dict(kv_size=self.kv_size, n_stream=self.n_stream, n_seq_max=self.n_seq_max,
                     token_budget=self.token_budget, max_running=self.max_running, policy=self.policy,
-                    block_size=self.block_size, chunked=self.chunked)
+                    block_size=self.block_size, chunked=self.chunked, preempt=self.preempt,
+                    swap_bytes=self.swap_bytes, n_layer=self.n_layer, row_bytes=self.E * 2)
 
 
 def request_stream(n_req=24, rate=1.0, burst=4, prompt_range=(4, 40), gen_range=(1, 12),
                    n_layer=2, n_head=4, n_head_kv=2, head_dim=64, kv_size=256, n_stream=1,
                    n_seq_max=8, token_budget=64, n_ubatch=32, policy="paged", block_size=1,
-                   chunked=True, max_running=0, split_mode="auto", seed=2001, name="stream"):
+                   chunked=True, max_running=0, split_mode="auto", preempt="recompute", swap_bytes=0,
+                   seed=2001, name="stream"):
     rng = np.random.default_rng(np.random.SeedSequence([seed, PURPOSE_REQUESTS]))
     arrive = [0] * min(burst, n_req)
     it = 0
@@ -111,12 +115,12 @@ def request_stream(n_req=24, rate=1.0, burst=4, prompt_range=(4, 40), gen_range=
     return RequestStream(name, n_layer, n_head, n_head_kv, head_dim, kv_size, n_stream, n_seq_max,
                          token_budget, n_ubatch, seed, np.asarray(arrive, np.int32),
                          n_prompt.astype(np.int32), n_generate.astype(np.int32), policy, block_size,
-                         bool(chunked), max_running, split_mode)
+                         bool(chunked), max_running, split_mode, preempt, int(swap_bytes))
 
 
 def qwen_serving(n_req=400, rate=2.0, burst=64, prompt_range=(128, 1024), gen_range=(64, 512),
                  n_layer=28, kv_size=131072, n_stream=1, n_seq_max=64, token_budget=2048, n_ubatch=512,
-                 policy="paged", seed=2002):
+                 policy="paged", preempt="recompute", seed=2002):
     """Qwen3-0.6B-shaped serving stream: up to 64 concurrent sequences, a
     2048-position budget per iteration, prompts of 128..1024 positions and
     64..512 generated tokens, one unified cache of 131072 cells."""
@@ -124,5 +128,5 @@ def qwen_serving(n_req=400, rate=2.0, burst=64, prompt_range=(128, 1024), gen_ra
                           gen_range=gen_range, n_layer=n_layer, n_head=QWEN3_06B["n_head"],
                           n_head_kv=QWEN3_06B["n_head_kv"], head_dim=QWEN3_06B["head_dim"],
                           kv_size=kv_size, n_stream=n_stream, n_seq_max=n_seq_max,
-                          token_budget=token_budget, n_ubatch=n_ubatch, policy=policy, seed=seed,
-                          name="qwen_serving")
+                          token_budget=token_budget, n_ubatch=n_ubatch, policy=policy, preempt=preempt,
+                          seed=seed, name="qwen_serving")

@@ -7,14 +7,16 @@ flagged ones).  In lockstep the oracle loop drives the oracle engine on the
 same rows.  Checked per iteration: the two loops' records bit for bit, the
 cells of every ubatch, and every attention output within |g - r| <= 2e-3 +
 5e-3 |r|.  Rows are keyed by (request, position), so a recomputation after
-preemption writes what the first pass wrote.
+preemption writes what the first pass wrote.  Under preemption by swapping
+the oracle loop saves and restores through the oracle's own sequence-state
+functions.
 """
 
 import numpy as np
 import pytest
 import torch
 
-from oracle import OracleEngine
+from oracle import OracleEngine, seqstate
 from oracle.scheduler import OracleScheduler
 from synthetic.serving import request_stream, QWEN3_06B
 from synthetic.workloads import KIND_K, KIND_V, KIND_Q
@@ -23,7 +25,8 @@ from helpers import assert_parity
 
 pytestmark = pytest.mark.gpu
 
-KEYS = ("retired", "preempted", "admitted", "req", "seq", "pos", "output", "n_running", "n_waiting")
+KEYS = ("retired", "preempted", "admitted", "swapped_out", "swapped_in", "req", "seq", "pos", "output",
+        "n_running", "n_waiting")
 
 
 def serve_parity(stream, max_iters=400):
@@ -36,13 +39,17 @@ def serve_parity(stream, max_iters=400):
                     stream.n_stream, stream.n_seq_max, nb, stream.n_ubatch, device="cuda:0",
                     attend_layers=len(layers), split_mode=stream.split_mode)
     sch = K.Scheduler(ctx, token_budget=nb, max_running=stream.max_running, policy=stream.policy,
-                      block_size=stream.block_size, chunked=stream.chunked, max_requests=stream.n_requests)
+                      block_size=stream.block_size, chunked=stream.chunked, max_requests=stream.n_requests,
+                      preempt=stream.preempt, swap_bytes=stream.swap_bytes)
     eng = OracleEngine(stream.n_layer, stream.n_head, stream.n_head_kv, stream.head_dim, stream.kv_size,
                        stream.n_stream, stream.n_seq_max, nb, stream.n_ubatch, layers=layers,
                        split_mode=stream.split_mode)
-    ref = OracleScheduler(release=lambda q: eng.seq_rm(q), **stream.sched_kwargs())
+    hooks = {}
+    if stream.preempt == "swap":
+        hooks = dict(swap_out=lambda q: seqstate.save(eng, q), swap_in=lambda q, b: seqstate.load(eng, q, b))
+    ref = OracleScheduler(release=lambda q: eng.seq_rm(q), **stream.sched_kwargs(), **hooks)
     HD = stream.n_head * stream.head_dim
-    stats = dict(iters=0, rows=0, preempted=0, mfma_items=0, valu_items=0, max_abs=0.0)
+    stats = dict(iters=0, rows=0, preempted=0, swapped=0, mfma_items=0, valu_items=0, max_abs=0.0)
     it = 0
     while it < max_iters:
         for r in stream.arrivals(it):
@@ -53,6 +60,7 @@ def serve_parity(stream, max_iters=400):
         for key in KEYS:
             assert got[key] == exp[key], (it, key)
         stats["preempted"] += len(exp["preempted"])
+        stats["swapped"] += len(exp["swapped_out"])
         n = len(exp["pos"])
         if n:
             rows = {(l, k): stream.batch_rows(exp["req"], exp["pos"], l, k)
@@ -113,3 +121,22 @@ def test_serving_streams_split_equal_reserve():
     s = serve_parity(st)
     print(s)
     assert s["preempted"] == 0 and s["rows"] > 200
+
+
+def test_serving_swap_preemption():
+    """Preempted sequences go to the swap arena and come back: their
+    restored rows (other cells, other sequence ids) must attend exactly like
+    the oracle's, which restores through the oracle's own save / load."""
+    st = request_stream(n_req=28, rate=1.5, kv_size=96, token_budget=64, n_ubatch=32, preempt="swap",
+                        swap_bytes=1 << 22, seed=2504)
+    s = serve_parity(st)
+    print(s)
+    assert s["swapped"] > 0 and s["rows"] > 300
+
+
+def test_serving_swap_arena_too_small_recomputes():
+    st = request_stream(n_req=28, rate=2.0, kv_size=64, n_stream=4, n_seq_max=8, token_budget=64, n_ubatch=32,
+                        preempt="swap", swap_bytes=32768, seed=2510)
+    s = serve_parity(st)
+    print(s)
+    assert 0 < s["swapped"] < s["preempted"]

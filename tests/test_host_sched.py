@@ -16,7 +16,7 @@ which is pinned by hand-worked traces in test_oracle_scheduler.py:
 import numpy as np
 import pytest
 
-from oracle import OracleEngine
+from oracle import OracleEngine, seqstate
 from oracle.scheduler import OracleScheduler, SchedError
 from synthetic.serving import request_stream
 
@@ -24,7 +24,8 @@ from test_oracle_scheduler import CASES, STREAMS
 
 K = pytest.importorskip("ubatch_attention_paged_amd")
 
-KEYS = ("retired", "preempted", "admitted", "req", "seq", "pos", "output", "n_running", "n_waiting")
+KEYS = ("retired", "preempted", "admitted", "swapped_out", "swapped_in", "req", "seq", "pos", "output",
+        "n_running", "n_waiting")
 
 
 def host_ctx(kv_size, n_stream, n_seq_max, n_batch, n_ubatch=0, split_mode="auto"):
@@ -48,9 +49,12 @@ def test_native_hand_worked_trace(name):
     case = CASES[name]
     p = case["params"]
     budget = int(p["budget"])
-    ctx = host_ctx(int(p["kv_size"]), int(p["n_stream"]), int(p["n_seq_max"]), budget)
+    # the swap cases size their blobs for 1 layer of 64-byte rows: 1 KV head of 32
+    ctx = K.Context(int(p.get("n_layer", 1)), 2, 1, int(p.get("row_bytes", 32)) // 2, kv_size=int(p["kv_size"]),
+                    n_stream=int(p["n_stream"]), n_seq_max=int(p["n_seq_max"]), n_batch=budget, n_ubatch=budget)
     sch = K.Scheduler(ctx, token_budget=budget, max_running=int(p["max_running"]), policy=p["policy"],
-                      block_size=int(p["block_size"]), chunked=p["chunked"] == "1", max_requests=16)
+                      block_size=int(p["block_size"]), chunked=p["chunked"] == "1", max_requests=16,
+                      preempt=p.get("preempt", "recompute"), swap_bytes=int(p.get("swap_bytes", 0)))
     for pr, g in case["reqs"]:
         sch.submit(pr, g)
     for exp in case["its"]:
@@ -79,10 +83,17 @@ def drive_both(stream, max_iters=5000):
     ctx = host_ctx(stream.kv_size, stream.n_stream, stream.n_seq_max, n_batch, stream.n_ubatch, stream.split_mode)
     eng = OracleEngine(1, 2, 1, 16, stream.kv_size, stream.n_stream, stream.n_seq_max, n_batch, stream.n_ubatch,
                        layers=[], split_mode=stream.split_mode)
-    ref = OracleScheduler(release=lambda q: eng.seq_rm(q), **stream.sched_kwargs())
+    hooks = {}
+    if stream.preempt == "swap":
+        eng = OracleEngine(1, 2, 1, 16, stream.kv_size, stream.n_stream, stream.n_seq_max, n_batch, stream.n_ubatch,
+                           split_mode=stream.split_mode)
+        hooks = dict(swap_out=lambda q: seqstate.save(eng, q), swap_in=lambda q, b: seqstate.load(eng, q, b))
+    kw = stream.sched_kwargs()
+    kw.update(n_layer=1, row_bytes=32)          # the host contexts here: 1 layer, 1 KV head of 16
+    ref = OracleScheduler(release=lambda q: eng.seq_rm(q), **kw, **hooks)
     sch = K.Scheduler(ctx, token_budget=stream.token_budget, max_running=stream.max_running,
                       policy=stream.policy, block_size=stream.block_size, chunked=stream.chunked,
-                      max_requests=stream.n_requests)
+                      max_requests=stream.n_requests, preempt=stream.preempt, swap_bytes=stream.swap_bytes)
     n_pre, it = 0, 0
     while it < max_iters:
         for r in stream.arrivals(it):

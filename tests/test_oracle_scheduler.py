@@ -19,8 +19,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import OracleEngine
-from oracle.scheduler import OracleScheduler, SchedError
+from oracle import OracleEngine, seqstate
+from oracle.scheduler import OracleScheduler, SchedError, blob_bytes
 from synthetic.serving import request_stream
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "sched_traces.txt")
@@ -67,7 +67,9 @@ CASES = parse_traces()
 def sched_from(p, release=None):
     return OracleScheduler(int(p["kv_size"]), int(p["n_stream"]), int(p["n_seq_max"]), int(p["budget"]),
                            max_running=int(p["max_running"]), policy=p["policy"],
-                           block_size=int(p["block_size"]), chunked=p["chunked"] == "1", release=release)
+                           block_size=int(p["block_size"]), chunked=p["chunked"] == "1", release=release,
+                           preempt=p.get("preempt", "recompute"), swap_bytes=int(p.get("swap_bytes", 0)),
+                           n_layer=int(p.get("n_layer", 1)), row_bytes=int(p.get("row_bytes", 0)))
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
@@ -87,6 +89,7 @@ def test_hand_worked_trace(name):
 def test_golden_file_covers_every_mechanism():
     its = [it for c in CASES.values() for it in c["its"]]
     assert any(it["preempted"] for it in its)
+    assert {c["params"].get("preempt", "recompute") for c in CASES.values()} == {"recompute", "swap"}
     assert {c["params"]["policy"] for c in CASES.values()} == {"paged", "reserve"}
     assert {c["params"]["chunked"] for c in CASES.values()} == {"0", "1"}
     assert any(int(c["params"]["n_stream"]) > 1 for c in CASES.values())
@@ -115,6 +118,33 @@ def test_closed_form_when_everything_fits():
     assert k == max(G) + 1
 
 
+def test_swap_records_and_arena():
+    case = CASES["paged_swap_decoder"]
+    s = sched_from(case["params"])
+    for pr, g in case["reqs"]:
+        s.submit(pr, g)
+    outs, ins = {}, {}
+    for exp in case["its"]:
+        rec = s.step()
+        outs[exp["k"]], ins[exp["k"]] = rec["swapped_out"], rec["swapped_in"]
+        if exp["k"] == 3:
+            assert s.swapped == [(0, 768, 1)] and s.requests[1].n_ctx == 4
+        s.advance()
+    assert outs[3] == [1] and ins[5] == [1] and s.swapped == []
+    assert all(not v for k, v in outs.items() if k != 3) and all(not v for k, v in ins.items() if k != 5)
+    fb = sched_from(CASES["paged_swap_fallback"]["params"])
+    assert fb._swap_place(768) is None and fb._swap_place(512) == 0
+
+
+def test_swap_arena_first_fit():
+    s = OracleScheduler(kv_size=64, n_stream=1, n_seq_max=4, token_budget=8, preempt="swap", swap_bytes=4096)
+    s.swapped = [(0, 512, 0), (1024, 256, 1), (2048, 1024, 2)]
+    assert s._swap_place(512) == 512          # the first gap that fits
+    assert s._swap_place(768) == 1280
+    assert s._swap_place(1024) == 3072        # the tail
+    assert s._swap_place(1025) is None
+
+
 def test_submission_rejections():
     s = OracleScheduler(kv_size=16, n_stream=1, n_seq_max=4, token_budget=8, chunked=False)
     with pytest.raises(SchedError):
@@ -137,12 +167,15 @@ def test_submission_rejections():
 def drive(stream, with_engine=True, max_iters=10000):
     """Run the loop over a request stream; returns the iteration records and
     checks the invariants after every iteration."""
-    eng = None
+    eng, hooks = None, {}
     if with_engine:
+        swap = stream.preempt == "swap"
         eng = OracleEngine(stream.n_layer, stream.n_head, stream.n_head_kv, stream.head_dim, stream.kv_size,
                            stream.n_stream, stream.n_seq_max, stream.token_budget, stream.n_ubatch,
-                           layers=[], split_mode=stream.split_mode)
-    s = OracleScheduler(release=(lambda q: eng.seq_rm(q)) if eng else None, **stream.sched_kwargs())
+                           layers=None if swap else [], split_mode=stream.split_mode)
+        if swap:
+            hooks = dict(swap_out=lambda q: seqstate.save(eng, q), swap_in=lambda q, b: seqstate.load(eng, q, b))
+    s = OracleScheduler(release=(lambda q: eng.seq_rm(q)) if eng else None, **stream.sched_kwargs(), **hooks)
     outputs = {r: [] for r in range(stream.n_requests)}
     recs, it = [], 0
     while it < max_iters:
@@ -192,6 +225,8 @@ STREAMS = {
     "paged_unchunked": dict(kv_size=128, chunked=False, token_budget=64),
     "reserve_blocks": dict(kv_size=128, policy="reserve", block_size=16),
     "reserve_streams": dict(kv_size=96, n_stream=2, policy="reserve", block_size=8, rate=2.0),
+    "swap_tight": dict(kv_size=96, rate=1.5, preempt="swap", swap_bytes=1 << 20),
+    "swap_small_arena": dict(kv_size=64, n_stream=4, rate=2.0, preempt="swap", swap_bytes=32768),
 }
 
 
@@ -202,7 +237,12 @@ def test_invariants_on_request_streams(name):
     n_pre = sum(len(r["preempted"]) for r in recs)
     if st.policy == "reserve":
         assert n_pre == 0
-    if name in ("paged_tight", "paged_tight_streams"):
+    if name in ("paged_tight", "paged_tight_streams", "swap_tight", "swap_small_arena"):
         assert n_pre > 0           # the case exists to exercise preemption
+    n_swap = sum(len(r["swapped_out"]) for r in recs)
+    if name.startswith("swap"):
+        assert n_swap > 0 and n_swap == sum(len(r["swapped_in"]) for r in recs)
+    if name == "swap_small_arena":
+        assert n_swap < n_pre      # some victims did not fit the arena and were recomputed
     # every running sequence with one pending position is served each iteration
     assert all(len(r["pos"]) > 0 or r["n_running"] == 0 for r in recs)

@@ -11,6 +11,7 @@
 #include "host_core.hpp"
 #include "kvattn.h"
 #include "launch.hpp"
+#include "state_internal.hpp"
 
 using namespace kvattn;
 
@@ -646,7 +647,45 @@ StateArgs state_args(kvattn_ctx* c, const StateGeom& sg, int32_t il0, int32_t n_
   return a;
 }
 
+// Placement of n cells at pos[] for seq (all-or-nothing), then the rows of
+// the blob's records into them on stream s (device contexts only).
+int restore_rows(kvattn_ctx* c, int32_t seq, const void* src, const int32_t* pos, int32_t n, hipStream_t s) {
+  const Geometry& g = c->core.geo();
+  std::vector<int32_t> cells;
+  int rc;
+  if ((rc = c->core.seq_restore(seq, pos, n, cells, c->err))) return rc;
+  if (n == 0 || !c->has_dev) return KVATTN_OK;
+  const StateGeom sg = state_geom(g, static_cast<size_t>(n));
+  int st = 0;
+  if ((rc = acquire_stage(c, 4 * sg.n, &st))) return rc;
+  int32_t* rows = static_cast<int32_t*>(c->stage[st]);
+  const int32_t sid = seq % g.n_stream;
+  for (size_t i = 0; i < sg.n; ++i) rows[i] = sid * g.kv_size + cells[i];
+  for (int32_t l0 = 0; l0 < g.n_layer; l0 += kMaxLayersPerLaunch) {
+    const int32_t n_il = std::min<int32_t>(kMaxLayersPerLaunch, g.n_layer - l0);
+    StateArgs a = state_args(c, sg, l0, n_il);
+    a.cells = reinterpret_cast<const int32_t*>(c->stage_dev[st]);
+    a.blob_r = static_cast<const uint32_t*>(src);
+    HIP_TRY(c, launch_state_copy(a, false, s));
+  }
+  HIP_TRY(c, hipEventRecord(c->ev[st], s));
+  c->ev_used[st] = true;
+  return KVATTN_OK;
+}
+
 }  // namespace
+
+bool kvattn::ctx_has_device(const kvattn_ctx* c) { return c && c->has_dev; }
+
+int kvattn::state_restore_known(kvattn_ctx* c, int32_t seq, const void* src, const int32_t* pos, int32_t n,
+                        void* hip_stream) {
+  if (!c || n < 0 || (n > 0 && !pos)) return KVATTN_EINVAL;
+  if (c->has_dev) {
+    if (!src || (reinterpret_cast<uintptr_t>(src) & 3)) return c->fail(KVATTN_EINVAL, "src is NULL or not 4-byte aligned");
+    if (int rc = ensure_device(c)) return rc;
+  }
+  return restore_rows(c, seq, src, pos, n, static_cast<hipStream_t>(hip_stream));
+}
 
 extern "C" {
 
@@ -741,26 +780,10 @@ int kvattn_seq_state_load(kvattn_ctx* c, int32_t seq_id, const void* src, size_t
     if (rd<uint32_t>(pk, at) != kStateTypeF16 || rd<uint64_t>(pk, at + 4) != sg.row)
       return c->fail(KVATTN_EINVAL, "a record header does not match");
   }
-  std::vector<int32_t> pos(sg.n), cells;
+  std::vector<int32_t> pos(sg.n);
   if (sg.n) std::memcpy(pos.data(), pk, 4 * sg.n);
   // 3. placement (all-or-nothing), then the rows into the new cells
-  if ((rc = c->core.seq_restore(seq_id, pos.data(), static_cast<int32_t>(sg.n), cells, c->err))) return rc;
-  if (sg.n == 0) return KVATTN_OK;
-  int st = 0;
-  if ((rc = acquire_stage(c, 4 * sg.n, &st))) return rc;
-  int32_t* rows = static_cast<int32_t*>(c->stage[st]);
-  const int32_t sid = seq_id % g.n_stream;
-  for (size_t i = 0; i < sg.n; ++i) rows[i] = sid * g.kv_size + cells[i];
-  for (int32_t l0 = 0; l0 < g.n_layer; l0 += kMaxLayersPerLaunch) {
-    const int32_t n_il = std::min<int32_t>(kMaxLayersPerLaunch, g.n_layer - l0);
-    StateArgs a = state_args(c, sg, l0, n_il);
-    a.cells = reinterpret_cast<const int32_t*>(c->stage_dev[st]);
-    a.blob_r = static_cast<const uint32_t*>(src);
-    HIP_TRY(c, launch_state_copy(a, false, s));
-  }
-  HIP_TRY(c, hipEventRecord(c->ev[st], s));
-  c->ev_used[st] = true;
-  return KVATTN_OK;
+  return restore_rows(c, seq_id, src, pos.data(), static_cast<int32_t>(sg.n), s);
 }
 
 int kvattn_get_params(const kvattn_ctx* c, kvattn_params* out) {

@@ -17,6 +17,7 @@
 
 #include "kvattn.h"
 #include "kvsched.h"
+#include "state_internal.hpp"
 
 namespace {
 
@@ -27,12 +28,21 @@ struct Req {
   int32_t sampled = 0;      // tokens sampled
   int32_t blocks = 0;       // RESERVE: blocks held
   int32_t state = KVATTN_REQ_WAITING;
+  int64_t swap_off = -1;    // SWAP: extent of its saved state while swapped out
+  int64_t swap_len = 0;
   int32_t known() const { return n_prompt + sampled; }
   int32_t pending() const { return known() - n_ctx; }
   bool finished() const { return sampled >= n_generate; }
 };
 
 int32_t ceil_div(int32_t a, int32_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kSwapAlign = 256;
+
+struct Extent {
+  int64_t off, len;
+  int32_t req;
+};
 
 }  // namespace
 
@@ -50,12 +60,20 @@ struct kvattn_sched {
   std::vector<int32_t> seq_owner;        // request running under each sequence id, -1 free
   std::vector<int32_t> free_blocks;      // RESERVE, per stream
   std::vector<int32_t> held, need;       // PAGED, per stream: cells held or promised; single-pending count
+  int32_t preempt = KVATTN_PREEMPT_RECOMPUTE;
+  char* swap_space = nullptr;
+  int64_t swap_bytes = 0;
+  void* stream = nullptr;
+  bool device = false;
+  int32_t n_layer = 0, row_bytes = 0;
+  std::vector<Extent> swapped;           // live extents of the swap arena, by offset
+  std::vector<int32_t> iota;             // positions 0, 1, 2, ... of a restored sequence
 
   // the assembled iteration
   std::vector<int32_t> b_pos, b_nsid, b_req, seq_val;
   std::vector<const int32_t*> b_seq;
   std::vector<int8_t> b_out;
-  std::vector<int32_t> retired, preempted, admitted, admitted_seq;
+  std::vector<int32_t> retired, preempted, admitted, admitted_seq, swapped_out, swapped_in;
   bool assembled = false;
 
   int fail(int code, const char* msg) {
@@ -109,6 +127,56 @@ struct kvattn_sched {
     return KVATTN_OK;
   }
 
+  // Lowest offset of the swap arena with `len` free bytes (first fit), -1 if none.
+  int64_t swap_place(int64_t len) const {
+    int64_t at = 0;
+    for (const Extent& e : swapped) {
+      if (e.off - at >= len) return at;
+      at = e.off + e.len;
+    }
+    return swap_bytes - at >= len ? at : -1;
+  }
+
+  // Save a victim's cells into the arena before they are released; false
+  // (recompute instead) when its blob does not fit.
+  int swap_out(Req& r, int32_t id, bool* saved) {
+    *saved = false;
+    if (preempt != KVATTN_PREEMPT_SWAP || r.n_ctx == 0) return KVATTN_OK;
+    size_t bytes = 0;
+    if (kvattn_seq_state_size(ctx, r.seq, &bytes) != KVATTN_OK) return fail(KVATTN_EINVAL, "kvattn_seq_state_size failed");
+    const int64_t n = r.n_ctx;
+    if (static_cast<int64_t>(bytes) != 80 + 4 * n + 2 * static_cast<int64_t>(n_layer) * (12 + n * row_bytes))
+      return fail(KVATTN_ESTATE, "the context's cells of a running sequence differ from its cached positions");
+    const int64_t len = (static_cast<int64_t>(bytes) + kSwapAlign - 1) / kSwapAlign * kSwapAlign;
+    const int64_t off = swap_place(len);
+    if (off < 0) return KVATTN_OK;
+    if (device) {
+      const int rc = kvattn_seq_state_save(ctx, r.seq, swap_space + off, static_cast<size_t>(len), nullptr, stream);
+      if (rc != KVATTN_OK) return fail(rc, "kvattn_seq_state_save failed");
+    }
+    auto it = std::lower_bound(swapped.begin(), swapped.end(), off,
+                               [](const Extent& e, int64_t o) { return e.off < o; });
+    swapped.insert(it, Extent{off, len, id});
+    r.swap_off = off;
+    r.swap_len = len;
+    *saved = true;
+    return KVATTN_OK;
+  }
+
+  int swap_in(Req& r) {
+    const int rc = kvattn::state_restore_known(ctx, r.seq, device ? swap_space + r.swap_off : nullptr, iota.data(),
+                                               r.n_ctx, stream);
+    if (rc != KVATTN_OK) return fail(rc, "restoring a swapped-out sequence failed");
+    for (size_t i = 0; i < swapped.size(); ++i)
+      if (swapped[i].off == r.swap_off) {
+        swapped.erase(swapped.begin() + static_cast<std::ptrdiff_t>(i));
+        break;
+      }
+    r.swap_off = -1;
+    r.swap_len = 0;
+    return KVATTN_OK;
+  }
+
   // Positions a sequence with `want` pending gets from `left`.
   int32_t take(int32_t want, int32_t left) const {
     if (chunked) return std::min(want, left);
@@ -129,6 +197,11 @@ int kvattn_sched_create(kvattn_ctx* ctx, const kvattn_sched_params* p, kvattn_sc
   if (p->policy != KVATTN_ADMIT_RESERVE && p->policy != KVATTN_ADMIT_PAGED) return KVATTN_EINVAL;
   if (p->policy == KVATTN_ADMIT_RESERVE && (p->block_size < 1 || p->block_size > cp.kv_size)) return KVATTN_EINVAL;
   if (p->max_requests < 1) return KVATTN_EINVAL;
+  if (p->preempt != KVATTN_PREEMPT_RECOMPUTE && p->preempt != KVATTN_PREEMPT_SWAP) return KVATTN_EINVAL;
+  const bool device = kvattn::ctx_has_device(ctx);
+  if (p->preempt == KVATTN_PREEMPT_SWAP && device && p->swap_bytes > 0 &&
+      (!p->swap_space || (reinterpret_cast<uintptr_t>(p->swap_space) & (kSwapAlign - 1))))
+    return KVATTN_EINVAL;
 
   kvattn_sched* s = new (std::nothrow) kvattn_sched();
   if (!s) return KVATTN_ENOMEM;
@@ -142,6 +215,18 @@ int kvattn_sched_create(kvattn_ctx* ctx, const kvattn_sched_params* p, kvattn_sc
     s->policy = p->policy;
     s->block_size = p->policy == KVATTN_ADMIT_RESERVE ? p->block_size : 1;
     s->chunked = p->chunked ? 1 : 0;
+    s->preempt = p->preempt;
+    s->swap_space = static_cast<char*>(p->swap_space);
+    s->swap_bytes = p->preempt == KVATTN_PREEMPT_SWAP ? static_cast<int64_t>(p->swap_bytes) : 0;
+    s->stream = p->hip_stream;
+    s->device = device;
+    s->n_layer = cp.n_layer;
+    s->row_bytes = cp.n_head_kv * cp.head_dim * 2;
+    s->swapped.reserve(p->max_requests);
+    s->iota.resize(cp.kv_size);
+    for (int32_t q = 0; q < cp.kv_size; ++q) s->iota[q] = q;
+    s->swapped_out.reserve(cp.n_seq_max);
+    s->swapped_in.reserve(cp.n_seq_max);
     s->reqs.reserve(p->max_requests);
     s->wq.assign(p->max_requests, -1);
     s->run.reserve(cp.n_seq_max);
@@ -201,6 +286,8 @@ int kvattn_sched_step(kvattn_sched* s, kvattn_sched_iter* it) {
   s->preempted.clear();
   s->admitted.clear();
   s->admitted_seq.clear();
+  s->swapped_out.clear();
+  s->swapped_in.clear();
 
   // 1. retire finished sequences
   for (int32_t i = 0; i < static_cast<int32_t>(s->run.size());) {
@@ -225,8 +312,11 @@ int kvattn_sched_step(kvattn_sched* s, kvattn_sched_iter* it) {
         Req& r = s->reqs[id];
         s->held[st] -= kvattn_sched::claim(r);
         s->need[st] -= r.pending() == 1 ? 1 : 0;
+        bool saved = false;
+        if (int rc = s->swap_out(r, id, &saved)) return rc;
+        if (saved) s->swapped_out.push_back(id);
         if (int rc = s->drop(idx)) return rc;
-        r.n_ctx = 0;
+        if (!saved) r.n_ctx = 0;
         r.state = KVATTN_REQ_WAITING;
         s->w_push_front(id);
         s->preempted.push_back(id);
@@ -264,7 +354,7 @@ int kvattn_sched_step(kvattn_sched* s, kvattn_sched_iter* it) {
     if (s->policy == KVATTN_ADMIT_RESERVE) {
       blocks = ceil_div(r.n_prompt + r.n_generate, s->block_size);
       if (blocks > s->free_blocks[st]) break;
-    } else if (r.pending() > s->kv_size - s->held[st] - s->need[st]) {
+    } else if (r.n_ctx + r.pending() > s->kv_size - s->held[st] - s->need[st]) {
       break;
     }
     s->w_pop_front();
@@ -274,10 +364,13 @@ int kvattn_sched_step(kvattn_sched* s, kvattn_sched_iter* it) {
     if (s->policy == KVATTN_ADMIT_RESERVE) {
       r.blocks = blocks;
       s->free_blocks[st] -= blocks;
-    } else if (r.pending() == 1) {
-      s->need[st] += 1;
     } else {
-      s->held[st] += r.pending();
+      s->held[st] += kvattn_sched::claim(r);
+      s->need[st] += r.pending() == 1 ? 1 : 0;
+    }
+    if (r.swap_off >= 0) {
+      if (int rc = s->swap_in(r)) return rc;
+      s->swapped_in.push_back(id);
     }
     s->chunk[s->run.size()] = c;
     s->run.push_back(id);
@@ -315,6 +408,10 @@ int kvattn_sched_step(kvattn_sched* s, kvattn_sched_iter* it) {
   it->n_admitted = static_cast<int32_t>(s->admitted.size());
   it->admitted = s->admitted.data();
   it->admitted_seq = s->admitted_seq.data();
+  it->n_swapped_out = static_cast<int32_t>(s->swapped_out.size());
+  it->swapped_out = s->swapped_out.data();
+  it->n_swapped_in = static_cast<int32_t>(s->swapped_in.size());
+  it->swapped_in = s->swapped_in.data();
   it->n_running = static_cast<int32_t>(s->run.size());
   it->n_waiting = s->w_count;
   it->n_decode = n_decode;

@@ -25,6 +25,8 @@ KVATTN_EINVAL, KVATTN_ESTATE, KVATTN_ENOMEM, KVATTN_EHIP, KVATTN_ENODEV = -1, -2
 KVATTN_ADMIT_RESERVE, KVATTN_ADMIT_PAGED = 0, 1
 ADMIT_POLICIES = {"reserve": KVATTN_ADMIT_RESERVE, "paged": KVATTN_ADMIT_PAGED}
 KVATTN_REQ_WAITING, KVATTN_REQ_RUNNING, KVATTN_REQ_DONE = 0, 1, 2
+KVATTN_PREEMPT_RECOMPUTE, KVATTN_PREEMPT_SWAP = 0, 1
+PREEMPT_MODES = {"recompute": KVATTN_PREEMPT_RECOMPUTE, "swap": KVATTN_PREEMPT_SWAP}
 MAX_SEQ = 64
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -62,7 +64,9 @@ class kvattn_ubatch(ctypes.Structure):
 class kvattn_sched_params(ctypes.Structure):
     _fields_ = [("token_budget", ctypes.c_int32), ("max_running", ctypes.c_int32),
                 ("policy", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("chunked", ctypes.c_int32), ("max_requests", ctypes.c_int32)]
+                ("chunked", ctypes.c_int32), ("max_requests", ctypes.c_int32),
+                ("preempt", ctypes.c_int32), ("swap_space", ctypes.c_void_p),
+                ("swap_bytes", ctypes.c_size_t), ("hip_stream", ctypes.c_void_p)]
 
 
 class kvattn_sched_iter(ctypes.Structure):
@@ -70,6 +74,8 @@ class kvattn_sched_iter(ctypes.Structure):
                 ("n_retired", ctypes.c_int32), ("retired", _i32p),
                 ("n_preempted", ctypes.c_int32), ("preempted", _i32p),
                 ("n_admitted", ctypes.c_int32), ("admitted", _i32p), ("admitted_seq", _i32p),
+                ("n_swapped_out", ctypes.c_int32), ("swapped_out", _i32p),
+                ("n_swapped_in", ctypes.c_int32), ("swapped_in", _i32p),
                 ("n_running", ctypes.c_int32), ("n_waiting", ctypes.c_int32),
                 ("n_decode", ctypes.c_int32)]
 
@@ -519,11 +525,13 @@ class Context:
 # --- the iteration-level batching loop (include/kvsched.h) ------------------
 
 def kvattn_sched_create(ctx, token_budget=0, max_running=0, policy="paged", block_size=1, chunked=True,
-                        max_requests=4096):
+                        max_requests=4096, preempt="recompute", swap_space=0, swap_bytes=0, stream=0):
     p = kvattn_sched_params()
     p.token_budget, p.max_running = token_budget, max_running
     p.policy = ADMIT_POLICIES[policy] if isinstance(policy, str) else int(policy)
     p.block_size, p.chunked, p.max_requests = block_size, int(bool(chunked)), max_requests
+    p.preempt = PREEMPT_MODES[preempt] if isinstance(preempt, str) else int(preempt)
+    p.swap_space, p.swap_bytes, p.hip_stream = swap_space or None, swap_bytes, stream or None
     out = ctypes.c_void_p()
     rc = load().kvattn_sched_create(ctx, ctypes.byref(p), ctypes.byref(out))
     if rc != 0:
@@ -574,10 +582,19 @@ class Scheduler:
     its host copy as plain lists."""
 
     def __init__(self, ctx: "Context", token_budget=0, max_running=0, policy="paged", block_size=1,
-                 chunked=True, max_requests=4096):
+                 chunked=True, max_requests=4096, preempt="recompute", swap_bytes=0, stream=None):
+        """With preempt="swap" on a device context the swap arena is a uint8
+        device tensor of swap_bytes allocated here; saves and restores run
+        on ``stream`` (torch's current stream by default)."""
         self.context = ctx
+        self.swap = None
+        ptr = 0
+        if preempt == "swap" and swap_bytes and ctx.device is not None:
+            import torch
+            self.swap = torch.empty(swap_bytes, dtype=torch.uint8, device=ctx.device)
+            ptr = self.swap.data_ptr()
         self.s = kvattn_sched_create(ctx.ctx, token_budget, max_running, policy, block_size, chunked,
-                                     max_requests)
+                                     max_requests, preempt, ptr, swap_bytes, ctx._stream(stream))
         self.it = kvattn_sched_iter()
 
     def close(self):
@@ -612,6 +629,8 @@ class Scheduler:
                 "preempted": _take(it.preempted, it.n_preempted, np.int32).tolist(),
                 "admitted": list(zip(_take(it.admitted, it.n_admitted, np.int32).tolist(),
                                      _take(it.admitted_seq, it.n_admitted, np.int32).tolist())),
+                "swapped_out": _take(it.swapped_out, it.n_swapped_out, np.int32).tolist(),
+                "swapped_in": _take(it.swapped_in, it.n_swapped_in, np.int32).tolist(),
                 "req": _take(it.req, n, np.int32).tolist(), "seq": seq,
                 "pos": _take(it.batch.pos, n, np.int32).tolist(),
                 "output": _take(it.batch.output, n, np.int8).tolist(),
