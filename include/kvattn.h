@@ -70,7 +70,10 @@ typedef struct kvattn_params {
   int32_t head_dim;       /* 16, 32, 64 or 128 */
   int32_t kv_size;        /* cells PER STREAM (tensor dimension 1); one layer's tensor,
                              n_stream * kv_size * n_head_kv * head_dim * 2 bytes, < 2 GiB */
-  int32_t n_stream;       /* 1 = unified cache; a slot's stream is seq_id[0] % n_stream */
+  int32_t n_stream;       /* 1 = unified cache; a slot's stream is seq_id[0] % n_stream, its cell
+                             holds the ids that live there (stream of id q: q % n_stream); a slot
+                             whose ids span streams is also stored once in each other stream it
+                             touches ("Unified versus non-unified": separate copies) */
   int32_t n_seq_max;      /* sequence ids must lie in [0, n_seq_max); <= KVATTN_MAX_SEQ */
   int32_t n_batch;        /* <= 0: 2048; clamped to kv_size*n_stream when causal */
   int32_t n_ubatch;       /* 0: n_batch; then clamped to n_batch */
@@ -132,6 +135,11 @@ typedef struct kvattn_ubatch {
   const int32_t *src_idx;           /* [n_tokens] row of each slot in the submitted batch */
   const int32_t *stream;            /* [n_tokens] */
   const int32_t *cells;             /* [n_tokens] reserved cell within the stream */
+  int32_t n_copies;                 /* separate copies (several streams only): extra cells of slots
+                                       whose ids span streams, one per other stream they touch */
+  const int32_t *copy_src;          /* [n_copies] slot (ubatch index) whose row the copy holds */
+  const int32_t *copy_stream;       /* [n_copies] */
+  const int32_t *copy_cell;         /* [n_copies] */
 } kvattn_ubatch;
 
 /* Device workspace the caller must provide: cell metadata mirror, the

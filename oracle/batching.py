@@ -51,9 +51,9 @@ def fill_batch(n_tokens, pos, seq_id, output, next_pos, n_seq_max, n_stream):
     * ``output is None``  -> only the last slot is flagged.
 
     A slot's sequence ids form a set (duplicates collapse).  Rejected: an id
-    outside [0, n_seq_max), an empty id list, a negative position, and -- with
-    several streams -- a slot whose ids live in different streams (stream =
-    seq % n_stream, a reading of P3 "Unified versus non-unified").
+    outside [0, n_seq_max), an empty id list, a negative position.  (With
+    several streams a slot whose ids live in different streams is stored once
+    per stream: see ``OracleEngine.split``.)
 
     Returns (pos list, list of sorted seq-id tuples, output list).
     """
@@ -70,8 +70,6 @@ def fill_batch(n_tokens, pos, seq_id, output, next_pos, n_seq_max, n_stream):
             for s in ids:
                 if s < 0 or s >= n_seq_max:
                     raise SplitError(f"slot {i}: seq id {s} out of range")
-            if n_stream > 1 and len({s % n_stream for s in ids}) != 1:
-                raise SplitError(f"slot {i}: seq ids span several streams")
             sids.append(tuple(ids))
     if pos is None:
         counter = dict(next_pos)

@@ -31,6 +31,7 @@ class OracleUbatch:
     n_seqs: int
     streams: list
     cells: list
+    copies: list = field(default_factory=list)   # (slot index, stream, cell): separate copies
     committed: bool = False
     n_kv: int = 0
     mask: np.ndarray = field(default=None, repr=False)
@@ -67,6 +68,7 @@ class OracleEngine:
         for ub in self._pending:
             if not ub.committed:
                 self.cells.release(ub.streams, ub.cells)
+                self.cells.release([c[1] for c in ub.copies], [c[2] for c in ub.copies])
         self._pending = []
         if n_tokens > self.n_batch:
             raise SplitError("n_tokens > n_batch")       # P1: GGML_ASSERT on n_batch
@@ -77,18 +79,33 @@ class OracleEngine:
         p, sids, out = fill_batch(n_tokens, pos, seq_id, output, next_pos,
                                   self.n_seq_max, self.n_stream)
         parts = split_batch([set(x) for x in sids], self.n_ubatch, self.n_stream, self.split_mode)
-        streams = [sids[i][0] % self.n_stream for (slots, _, _) in parts for i in slots]
-        cells = self.cells.reserve(streams)
+        # a slot's cell is in the stream of its first id (seq % n_stream);
+        # P3 "Unified versus non-unified": with several streams a common
+        # prefix needs separate copies -- a slot whose ids span streams also
+        # gets a cell in each other stream it touches (ascending), holding
+        # the ids that live there.  Cells are taken per stream in slot order.
+        want = []                               # (stream, slot, primary?) in placement order
+        for (slots, _, _) in parts:
+            for i in slots:
+                s0 = sids[i][0] % self.n_stream
+                want.append((s0, i, True))
+                for s2 in sorted({q % self.n_stream for q in sids[i]} - {s0}):
+                    want.append((s2, i, False))
+        cells = self.cells.reserve([w[0] for w in want])
         if cells is None:
             return 1, [], None
-        ubs, k = [], 0
+        placed = {}
+        for (st, i, prim), c in zip(want, cells):
+            placed.setdefault(i, []).append((st, c, prim))
+        ubs = []
         for (slots, nst, ns) in parts:
-            n = len(slots)
+            prim = [next((st, c) for st, c, pr in placed[i] if pr) for i in slots]
+            copies = [(k, st, c) for k, i in enumerate(slots) for st, c, pr in placed[i] if not pr]
             ubs.append(OracleUbatch(src=list(slots), pos=[p[i] for i in slots],
                                     seq_ids=[sids[i] for i in slots],
                                     output=[out[i] for i in slots], n_seq_tokens=nst,
-                                    n_seqs=ns, streams=streams[k:k + n], cells=cells[k:k + n]))
-            k += n
+                                    n_seqs=ns, streams=[x[0] for x in prim], cells=[x[1] for x in prim],
+                                    copies=copies))
         self._pending = ubs
         return 0, ubs, output_ids(out, self.n_batch)
 
@@ -97,7 +114,11 @@ class OracleEngine:
         """The ubatch's cells become visible, then its mask is built over
         the table as it now stands (later ubatches are not yet committed).
         ``build_mask=False`` only records placement (for placement checks)."""
-        self.cells.commit(ub.streams, ub.cells, ub.pos, ub.seq_ids)
+        here = lambda ids, st: tuple(q for q in ids if q % self.n_stream == st)   # the ids a cell of st holds
+        self.cells.commit(ub.streams, ub.cells, ub.pos,
+                          [here(ids, st) for ids, st in zip(ub.seq_ids, ub.streams)])
+        self.cells.commit([c[1] for c in ub.copies], [c[2] for c in ub.copies], [ub.pos[c[0]] for c in ub.copies],
+                          [here(ub.seq_ids[c[0]], c[1]) for c in ub.copies])
         ub.committed = True
         ub.n_kv = self.cells.n_kv()
         if build_mask:
@@ -109,6 +130,9 @@ class OracleEngine:
         rounded to F16."""
         k16, v16 = f16_round(k_rows), f16_round(v_rows)
         for r, (s, j) in enumerate(zip(ub.streams, ub.cells)):
+            self.K[layer][s, j] = k16[r]
+            self.V[layer][s, j] = v16[r]
+        for r, s, j in ub.copies:
             self.K[layer][s, j] = k16[r]
             self.V[layer][s, j] = v16[r]
 

@@ -191,11 +191,12 @@ def mixed(n_prompt_seq=8, n_decoders=56, prompt_range=(128, 1024), ctx_range=(25
                     note=f"prompts {plen.tolist()}, {n_decoders} decoders")
 
 
-def prefix_decode(n_seq=32, prefix=2048, private=256, n_layer=28, kv_size=16384, seed=1005):
+def prefix_decode(n_seq=32, prefix=2048, private=256, n_layer=28, kv_size=16384, n_stream=1, seed=1005):
     """Prefix sharing: one prefix of ``prefix`` tokens stored once for all
     n_seq sequences (slots with n_seq ids; "Batch、Ubatch 与解码主循环" Part E),
     then ``private`` tokens per sequence, then one measured decode token per
-    sequence."""
+    sequence.  With several streams (kv_size cells each) the prefix slots'
+    ids span the streams, so the prefix is stored once per stream."""
     everyone = tuple(range(n_seq))
     batches = _prompt_batches(everyone, 0, prefix, 2048, measured=False, out_last=False)
     pos, seqs = [], []
@@ -206,7 +207,7 @@ def prefix_decode(n_seq=32, prefix=2048, private=256, n_layer=28, kv_size=16384,
         batches.append(_batch(pos[a:b], seqs[a:b], [0] * (b - a), False))
     batches.append(_batch([prefix + private] * n_seq, [(i,) for i in range(n_seq)],
                           [1] * n_seq, True))
-    return Workload("prefix_decode", n_layer, 16, 8, 128, kv_size=kv_size, n_stream=1,
+    return Workload("prefix_decode", n_layer, 16, 8, 128, kv_size=kv_size, n_stream=n_stream,
                     n_seq_max=n_seq, seed=seed, batches=batches,
                     note=f"{n_seq} sequences share {prefix} cells, {private} private each")
 

@@ -363,3 +363,22 @@ def test_split_mode_parity(name, mode):
     _, got = gpu_run(wl, layers, on_ubatch=check)
     for key in ref:
         assert_parity(got[key], ref[key], tag=f"{mode} {name} {key}")
+
+
+def test_prefix_separate_copies_across_streams():
+    """A prefix shared by 8 sequences in a 4-stream cache is stored once per
+    stream (separate copies written by the store kernel); every sequence's
+    decode token attends like the oracle's and like the same workload over
+    one unified stream."""
+    wl4 = W.prefix_decode(n_seq=8, prefix=200, private=30, n_layer=2, kv_size=512, n_stream=4)
+    wl1 = W.prefix_decode(n_seq=8, prefix=200, private=30, n_layer=2, kv_size=2048, n_stream=1)
+    layers = [0, 1]
+    _, ref, _, _ = oracle_run(wl4, layers)
+    ctx4, got4 = gpu_run(wl4, layers)
+    ctx1, got1 = gpu_run(wl1, layers)
+    for key in ref:
+        assert_parity(got4[key], ref[key], tag=f"4 streams {key}")
+        assert_parity(got4[key], got1[key], tag=f"4 streams vs unified {key}")
+    for s in range(4):
+        pos, mask = ctx4.cells(s)
+        assert int((pos >= 0).sum()) == 200 + 2 * 31       # the prefix copy, 2 sequences x (30 + 1)

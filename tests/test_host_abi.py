@@ -69,6 +69,7 @@ def compare_split(ctx, eng, n, pos, seqs, out):
         assert (u.n_seq_tokens, u.n_seqs) == (r.n_seq_tokens, r.n_seqs)
         assert u.stream.tolist() == r.streams
         assert u.cells.tolist() == r.cells
+        assert u.copies == [tuple(c) for c in r.copies]
         assert u.n_tokens == u.n_seq_tokens * u.n_seqs
         assert u.seq_id_unq.tolist() == sorted({s for ss in r.seq_ids for s in ss})
     assert np.array_equal(ids, rids)
@@ -102,10 +103,14 @@ WORKLOADS = [
     lambda: shrink(W.mixed(n_prompt_seq=4, n_decoders=12, prompt_range=(20, 90), ctx_range=(10, 60),
                            n_layer=1, n_stream=4, kv_size=512, n_batch=128, n_ubatch=32)),
     lambda: shrink(W.prefix_decode(n_seq=8, prefix=300, private=40, n_layer=1, kv_size=1024)),
+    lambda: shrink(W.prefix_decode(n_seq=8, prefix=300, private=40, n_layer=1, kv_size=512, n_stream=4)),
 ]
 
 
-@pytest.mark.parametrize("make", WORKLOADS, ids=["tiny", "prefill", "cb_decode", "mixed", "prefix"])
+WL_IDS = ["tiny", "prefill", "cb_decode", "mixed", "prefix", "prefix_streams"]
+
+
+@pytest.mark.parametrize("make", WORKLOADS, ids=WL_IDS)
 def test_host_split_placement_matches_oracle(make):
     wl = make()
     ctx, eng = host_ctx(wl), oracle_for(wl)
@@ -116,7 +121,7 @@ def test_host_split_placement_matches_oracle(make):
 
 
 @pytest.mark.parametrize("mode", ["simple", "equal", "seq"])
-@pytest.mark.parametrize("make", WORKLOADS, ids=["tiny", "prefill", "cb_decode", "mixed", "prefix"])
+@pytest.mark.parametrize("make", WORKLOADS, ids=WL_IDS)
 def test_host_split_modes_match_oracle(make, mode):
     """Each split strategy requested explicitly, on every workload shape."""
     import dataclasses
@@ -232,10 +237,11 @@ def test_error_codes():
     with pytest.raises(K.KvattnError) as e:
         ctx.attend(ubs3[0], 0, [], [])
     assert e.value.code == K.KVATTN_ENODEV
-    # streams: a slot whose ids live in two streams
+    # streams: a slot whose ids live in two streams is stored in both
     c2 = K.Context(1, 2, 1, 16, kv_size=8, n_stream=2, n_seq_max=4)
-    with pytest.raises(K.KvattnError):
-        c2.split(1, [0], [[0, 1]])
+    st, ubs, _ = c2.split(2, [0, 1], [[1, 0, 2], [3]])
+    assert st == 0 and ubs[0].copies == [(0, 0, 0)] and ubs[0].stream.tolist() == [1, 1]
+    assert ubs[0].cells.tolist() == [0, 1]
     # bad parameters
     with pytest.raises(K.KvattnError):
         K.Context(1, 3, 2, 16, kv_size=8)                 # n_head not a multiple

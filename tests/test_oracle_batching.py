@@ -151,8 +151,48 @@ def test_fill_batch_autofill_and_errors():
         B.fill_batch(1, [-1], [[0]], None, {}, 4, 1)       # negative position
     with pytest.raises(SplitError):
         B.fill_batch(1, [0], [[]], None, {}, 4, 1)         # no id
-    with pytest.raises(SplitError):
-        B.fill_batch(1, [0], [[0, 1]], None, {}, 4, 2)     # ids in two streams
+    p, s, o = B.fill_batch(1, [0], [[1, 0]], None, {}, 4, 2)   # ids in two streams: accepted
+    assert s == [(1, 0)]
+
+
+def test_separate_copies_of_a_prefix_across_streams():
+    """P3 "Unified versus non-unified": with one stream per sequence a common
+    prefix needs separate copies.  A 6-slot prefix shared by sequences 0..3
+    takes 6 cells of the unified cache and 6 cells in each of 4 streams, each
+    copy holding only the id of its stream; every sequence's decode query
+    then attends exactly as over the unified cache."""
+    rng = np.random.default_rng(21)
+    P, n_seq, layers = 6, 4, [0]
+    k = rng.standard_normal((P, 2 * 16))
+    v = rng.standard_normal((P, 2 * 16))
+    q = rng.standard_normal((n_seq, 4 * 16))
+    kd = rng.standard_normal((n_seq, 2 * 16))
+    vd = rng.standard_normal((n_seq, 2 * 16))
+    outs = {}
+    for n_stream, kv in ((1, 64), (4, 16)):
+        eng = OracleEngine(1, 4, 2, 16, kv_size=kv, n_stream=n_stream, n_seq_max=n_seq, n_batch=64, n_ubatch=64,
+                           layers=layers)
+        st, ubs, _ = eng.split(P, list(range(P)), [tuple(range(n_seq))] * P, [0] * P)
+        assert st == 0 and len(ubs) == 1
+        ub = ubs[0]
+        eng.commit(ub, build_mask=False)
+        eng.store(ub, 0, k, v)
+        assert len(ub.copies) == P * (n_stream - 1)
+        used = [int((eng.cells.pos[s] >= 0).sum()) for s in range(n_stream)]
+        assert used == [P] * n_stream
+        for s in range(n_stream):
+            held = eng.cells.member[s][eng.cells.pos[s] >= 0]
+            want = [q_ for q_ in range(n_seq) if q_ % n_stream == s]
+            assert all(sorted(np.nonzero(h)[0].tolist()) == want for h in held)
+        st, ubs, _ = eng.split(n_seq, [P] * n_seq, [(i,) for i in range(n_seq)], [1] * n_seq)
+        ub = ubs[0] if len(ubs) == 1 else None
+        res = np.zeros((n_seq, 4 * 16))
+        for u in ubs:
+            eng.commit(u, build_mask=True)
+            eng.store(u, 0, kd[u.src], vd[u.src])
+            res[u.src] = eng.attend(u, 0, q[u.src])
+        outs[n_stream] = res
+    assert np.allclose(outs[1], outs[4], rtol=0, atol=1e-12)
 
 
 def test_engine_rejects_batch_larger_than_n_batch():

@@ -178,9 +178,16 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
     c->plan[1] = Plan();
   }
   const Plan& P0 = c->plan[0];
-  std::vector<int32_t> dst(u.cells.size());
-  for (size_t i = 0; i < u.cells.size(); ++i)
+  // destination rows of the store: the slots' cells, then the separate
+  // copies; after them the source slot of each copy
+  const size_t n_slot = u.cells.size(), n_copy = u.copy_cell.size();
+  std::vector<int32_t> dst(n_slot + 2 * n_copy);
+  for (size_t i = 0; i < n_slot; ++i)
     dst[i] = static_cast<int32_t>(static_cast<int64_t>(u.stream[i]) * g.kv_size + u.cells[i]);
+  for (size_t i = 0; i < n_copy; ++i) {
+    dst[n_slot + i] = static_cast<int32_t>(static_cast<int64_t>(u.copy_stream[i]) * g.kv_size + u.copy_cell[i]);
+    dst[n_slot + n_copy + i] = u.copy_src[i];
+  }
 
   // arena layout
   ArenaLayout& A = c->al;
@@ -393,6 +400,10 @@ int kvattn_split(kvattn_ctx* c, const kvattn_batch* b, kvattn_ubatch* ubs, int32
     o.src_idx = u.src.data();
     o.stream = u.stream.data();
     o.cells = u.cells.data();
+    o.n_copies = static_cast<int32_t>(u.copy_cell.size());
+    o.copy_src = u.copy_src.data();
+    o.copy_stream = u.copy_stream.data();
+    o.copy_cell = u.copy_cell.data();
   }
   *n_ubs = static_cast<int32_t>(v.size());
   return KVATTN_OK;
@@ -436,7 +447,8 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
   const Geometry& g = c->core.geo();
   StoreArgs a{};
   a.dst_rows = reinterpret_cast<const int32_t*>(c->arena() + c->al.dst_rows);
-  a.n_rows = static_cast<int32_t>(u.cells.size());
+  a.n_src = static_cast<int32_t>(u.cells.size());
+  a.n_rows = a.n_src + static_cast<int32_t>(u.copy_cell.size());
   a.E = g.E();
   for (int32_t l0 = 0; l0 < n_il; l0 += kMaxLayersPerLaunch) {
     const int n = std::min<int32_t>(kMaxLayersPerLaunch, n_il - l0);

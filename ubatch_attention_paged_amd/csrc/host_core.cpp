@@ -118,8 +118,10 @@ void HostCore::push_cell(int s, int32_t cell) {
 
 void HostCore::release_uncommitted() {
   for (auto& u : ubs_)
-    if (!u.committed)
+    if (!u.committed) {
       for (size_t i = 0; i < u.cells.size(); ++i) push_cell(u.stream[i], u.cells[i]);
+      for (size_t i = 0; i < u.copy_cell.size(); ++i) push_cell(u.copy_stream[i], u.copy_cell[i]);
+    }
 }
 
 int HostCore::find(int32_t id) const {
@@ -162,10 +164,6 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
         const int32_t s = b.seq_id[i][t];
         if (s < 0 || s >= g_.n_seq_max) {
           err = "slot " + std::to_string(i) + ": sequence id " + std::to_string(s) + " outside [0, n_seq_max)";
-          return KVATTN_EINVAL;
-        }
-        if (g_.n_stream > 1 && s % g_.n_stream != b.seq_id[i][0] % g_.n_stream) {
-          err = "slot " + std::to_string(i) + ": sequence ids in different streams";
           return KVATTN_EINVAL;
         }
         m |= 1ULL << s;
@@ -285,8 +283,16 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
   // -- placement: every slot of every ubatch, all-or-nothing ("Batch、Ubatch
   // 与解码主循环", Part C: prepare reserves slots for all ubatches; Part F:
   // return 1 when the cache is full)
+  // A slot's cell lives in the stream of its first id; with several streams
+  // ("What does llama.cpp's KV cache ...", "Unified versus non-unified":
+  // common prefixes need separate copies) a slot whose ids span streams also
+  // gets one cell in each other stream, holding the ids that live there.
+  std::vector<uint64_t> smask(g_.n_stream, 0);       // ids of each stream
+  for (int32_t q = 0; q < g_.n_seq_max; ++q) smask[q % g_.n_stream] |= 1ULL << q;
   std::vector<int32_t> need(g_.n_stream, 0);
-  for (int32_t i = 0; i < n; ++i) ++need[seq0(i) % g_.n_stream];
+  for (int32_t i = 0; i < n; ++i)
+    for (int s = 0; s < g_.n_stream; ++s)
+      if (setmask[i] & smask[s]) ++need[s];
   for (int s = 0; s < g_.n_stream; ++s)
     if (need[s] > st_[s].n_avail) {
       err = "no free cells: stream " + std::to_string(s) + " needs " + std::to_string(need[s]) +
@@ -305,11 +311,18 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
       u.pos.push_back(pos[i]);
       u.n_seq_id.push_back(beg[i + 1] - beg[i]);
       u.seq_ptr.push_back(&seq_flat_[beg[i]]);
-      u.setmask.push_back(setmask[i]);
+      u.setmask.push_back(setmask[i] & smask[s]);
       u.output.push_back(out[i]);
       u.n_outputs += out[i];
       u.stream.push_back(s);
       u.cells.push_back(pop_cell(s));
+      for (int s2 = 0; s2 < g_.n_stream; ++s2) {
+        if (s2 == s || !(setmask[i] & smask[s2])) continue;
+        u.copy_src.push_back(static_cast<int32_t>(u.src.size()) - 1);
+        u.copy_stream.push_back(s2);
+        u.copy_cell.push_back(pop_cell(s2));
+        u.copy_mask.push_back(setmask[i] & smask[s2]);
+      }
       unq |= setmask[i];
     }
     for (uint64_t m = unq; m; m &= m - 1) u.seq_unq.push_back(lowest_bit(m));
@@ -349,6 +362,8 @@ int HostCore::commit(int k, std::vector<CellUpdate>* upd, std::string& err) {
     return KVATTN_ESTATE;
   }
   for (size_t i = 0; i < u.cells.size(); ++i) set_cell(u.stream[i], u.cells[i], u.pos[i], u.setmask[i]);
+  for (size_t i = 0; i < u.copy_cell.size(); ++i)
+    set_cell(u.copy_stream[i], u.copy_cell[i], u.pos[u.copy_src[i]], u.copy_mask[i]);
   u.committed = true;
   latest_ = k;
   if (upd) {

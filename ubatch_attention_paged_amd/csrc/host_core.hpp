@@ -33,7 +33,11 @@ struct UbatchRec {
   int32_t id = 0;
   int32_t n_seq_tokens = 0, n_seqs = 0;
   std::vector<int32_t> src, pos, n_seq_id, stream, cells, seq_unq;
-  std::vector<uint64_t> setmask;
+  std::vector<uint64_t> setmask;      // ids of the slot that live in its own stream (its cell's set)
+  // separate copies: a slot whose ids span several streams also gets a cell
+  // in each other stream, holding the ids that live there
+  std::vector<int32_t> copy_src, copy_stream, copy_cell;   // copy_src = slot index in this ubatch
+  std::vector<uint64_t> copy_mask;
   std::vector<const int32_t*> seq_ptr;
   std::vector<int8_t> output;
   int32_t n_outputs = 0;

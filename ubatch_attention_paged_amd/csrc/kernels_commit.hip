@@ -30,7 +30,8 @@ KVATTN_DEV void store_rows(const StoreArgs& a) {
   if (t >= static_cast<int64_t>(a.n_rows) * vec_per_row) return;
   const int r = static_cast<int>(t / vec_per_row);
   const int c = static_cast<int>(t % vec_per_row);
-  const float* src = (which ? a.v_cur[il] : a.k_cur[il]) + static_cast<int64_t>(r) * a.E + c * 8;
+  const int sr = r < a.n_src ? r : a.dst_rows[a.n_rows + r - a.n_src];   // a copy stores its slot's row
+  const float* src = (which ? a.v_cur[il] : a.k_cur[il]) + static_cast<int64_t>(sr) * a.E + c * 8;
   _Float16* dst = (which ? a.v[il] : a.k[il]) + static_cast<int64_t>(a.dst_rows[r]) * a.E + c * 8;
   const float4 x0 = *reinterpret_cast<const float4*>(src);
   const float4 x1 = *reinterpret_cast<const float4*>(src + 4);

@@ -15,8 +15,10 @@ struct StoreArgs {
   const float* v_cur[kMaxLayersPerLaunch];
   _Float16* k[kMaxLayersPerLaunch];
   _Float16* v[kMaxLayersPerLaunch];
-  const int32_t* dst_rows;    // [n_rows] stream * kv_size + cell
+  const int32_t* dst_rows;    // [n_rows] stream * kv_size + cell, then [n_rows - n_src] source slots:
+                              // rows >= n_src are separate copies of slot dst_rows[n_rows + r - n_src]
   int32_t n_rows;
+  int32_t n_src;              // slots of the ubatch (rows of k_cur / v_cur)
   int32_t E;
 };
 

@@ -58,7 +58,9 @@ class kvattn_ubatch(ctypes.Structure):
                 ("n_seqs_unq", ctypes.c_int32), ("n_outputs", ctypes.c_int32),
                 ("pos", _i32p), ("n_seq_id", _i32p), ("seq_id", ctypes.POINTER(_i32p)),
                 ("seq_id_unq", _i32p), ("output", ctypes.POINTER(ctypes.c_int8)),
-                ("src_idx", _i32p), ("stream", _i32p), ("cells", _i32p)]
+                ("src_idx", _i32p), ("stream", _i32p), ("cells", _i32p),
+                ("n_copies", ctypes.c_int32), ("copy_src", _i32p), ("copy_stream", _i32p),
+                ("copy_cell", _i32p)]
 
 
 class kvattn_sched_params(ctypes.Structure):
@@ -195,6 +197,9 @@ class Ubatch:
         self.cells = _take(raw.cells, n, np.int32)
         self.output = _take(raw.output, n, np.int8)
         self.seq_id_unq = _take(raw.seq_id_unq, raw.n_seqs_unq, np.int32)
+        self.copies = list(zip(_take(raw.copy_src, raw.n_copies, np.int32).tolist(),
+                               _take(raw.copy_stream, raw.n_copies, np.int32).tolist(),
+                               _take(raw.copy_cell, raw.n_copies, np.int32).tolist()))
         self._seq_ids = None
 
     @property
