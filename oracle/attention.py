@@ -60,12 +60,13 @@ def masked_attention(q, k_cache, v_cache, streams, mask, n_head, n_head_kv, scal
     return out
 
 
-def brute_force_attention(queries, history, n_head, n_head_kv, head_dim, causal=True, scale=None):
+def brute_force_attention(queries, history, n_head, n_head_kv, head_dim, causal=True, scale=None, swa=0):
     """Per-sequence attention by explicit loops over the token history.
 
     Independent of cells, placement, n_kv and the mask: a query (pos, first
     seq id s, q) sees every stored token whose sequence set contains s and,
-    when causal, whose position is not later than its own.
+    when causal, whose position is not later than its own; with a sliding
+    window of swa > 0 positions, only tokens fewer than swa positions back.
 
     queries  list of (pos, seq0, q[n_head*head_dim])
     history  list of (pos, seq_set, k_f16[n_head_kv*head_dim], v_f16[...])
@@ -77,7 +78,7 @@ def brute_force_attention(queries, history, n_head, n_head_kv, head_dim, causal=
     rows = []
     for (qp, s0, q) in queries:
         seen = [(float_row(k), float_row(v)) for (p, ss, k, v) in history
-                if s0 in ss and (not causal or p <= qp)]
+                if s0 in ss and (not causal or p <= qp) and (swa <= 0 or qp - p < swa)]
         o = [0.0] * (n_head * head_dim)
         for h in range(n_head):
             g = h // group

@@ -45,11 +45,12 @@ class OracleEngine:
     """Cell table + per-layer F16 caches (only the layers in ``layers``)."""
 
     def __init__(self, n_layer, n_head, n_head_kv, head_dim, kv_size, n_stream=1,
-                 n_seq_max=1, n_batch=0, n_ubatch=512, causal=True, kq_scale=None,
+                 n_seq_max=1, n_batch=0, n_ubatch=512, causal=True, kq_scale=None, swa=0,
                  cell_order=None, layers=None, split_mode="auto"):
         self.n_layer, self.n_head, self.n_head_kv, self.head_dim = n_layer, n_head, n_head_kv, head_dim
         self.kv_size, self.n_stream, self.n_seq_max = kv_size, n_stream, n_seq_max
         self.causal = bool(causal)
+        self.swa = int(swa)                   # sliding window in positions, 0 = none
         self.kq_scale = kq_scale
         self.split_mode = split_mode          # "auto", "simple", "equal" or "seq"
         self.n_batch, self.n_ubatch = clamp_params(kv_size * n_stream, n_batch, n_ubatch, causal)
@@ -122,7 +123,7 @@ class OracleEngine:
         ub.committed = True
         ub.n_kv = self.cells.n_kv()
         if build_mask:
-            ub.mask = self.cells.mask(ub.streams, ub.pos, [s[0] for s in ub.seq_ids], self.causal)
+            ub.mask = self.cells.mask(ub.streams, ub.pos, [s[0] for s in ub.seq_ids], self.causal, self.swa)
         return ub.mask
 
     def store(self, ub: OracleUbatch, layer: int, k_rows, v_rows):

@@ -160,21 +160,29 @@ class CellTable:
         return result
 
     # -- the KQ mask -----------------------------------------------------
-    def visible_row(self, s, q_pos, q_seq0, nkv, causal=True) -> np.ndarray:
+    def visible_row(self, s, q_pos, q_seq0, nkv, causal=True, swa=0) -> np.ndarray:
         """P1 "The mask is doing the work": skip empty cells, cells of other
-        sequences and, under causal attention, cells from the future.  The
-        query's sequence is its FIRST listed id.  Cells j < nkv of stream s."""
+        sequences, under causal attention cells from the future, and for
+        models with sliding-window attention cells outside the window.  The
+        query's sequence is its FIRST listed id.  Cells j < nkv of stream s.
+
+        The window rule is elided on the page (``is_masked_swa(...)``).
+        Reading: with a window of ``swa`` > 0 positions a cell is outside it
+        when ``q_pos - pos >= swa``, i.e. a query sees the last ``swa``
+        positions up to its own; ``swa == 0`` means no window."""
         pos = self.pos[s, :nkv]
         vis = (pos >= 0) & self.member[s, :nkv, q_seq0]
         if causal:
             vis &= pos <= q_pos
+        if swa > 0:
+            vis &= q_pos - pos < swa
         return vis
 
-    def mask(self, streams, q_pos, q_seq0, causal=True) -> np.ndarray:
+    def mask(self, streams, q_pos, q_seq0, causal=True, swa=0) -> np.ndarray:
         """F16 KQ mask [n_tokens][n_kv]: 0 where visible, -inf elsewhere,
         row-major without padding (encoding is a reading)."""
         nkv = self.n_kv()
         m = np.full((len(q_pos), nkv), MASK_HIDDEN, dtype=np.float16)
         for i in range(len(q_pos)):
-            m[i, self.visible_row(streams[i], q_pos[i], q_seq0[i], nkv, causal)] = MASK_VISIBLE
+            m[i, self.visible_row(streams[i], q_pos[i], q_seq0[i], nkv, causal, swa)] = MASK_VISIBLE
         return m

@@ -57,6 +57,7 @@ class Workload:
     causal: bool = True
     cell_order: Optional[np.ndarray] = field(default=None, repr=False)
     split_mode: str = "auto"          # "auto", "simple", "equal" or "seq"
+    swa: int = 0                      # sliding window in positions, 0 = none
     note: str = ""
 
     @property

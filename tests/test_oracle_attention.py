@@ -30,7 +30,7 @@ def run_oracle(wl, cell_order="auto", n_ubatch=None, layers=None):
     eng = OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size,
                        wl.n_stream, wl.n_seq_max, wl.n_batch,
                        wl.n_ubatch if n_ubatch is None else n_ubatch, wl.causal,
-                       cell_order=order, layers=layers)
+                       cell_order=order, layers=layers, swa=wl.swa)
     layers = eng.layers
     outs = {}
     for b, bt in enumerate(wl.batches):
@@ -67,7 +67,7 @@ def brute(wl, layer=0):
             q = wl.tensor(b, layer, W.KIND_Q)
             queries = [(int(bt.pos[i]), bt.seq_ids[i][0], q[i]) for i in range(bt.n_tokens)]
             outs[(b, layer)] = np.array(brute_force_attention(
-                queries, hist, wl.n_head, wl.n_head_kv, wl.head_dim, wl.causal))
+                queries, hist, wl.n_head, wl.n_head_kv, wl.head_dim, wl.causal, swa=wl.swa))
     return outs
 
 
@@ -324,3 +324,70 @@ def test_noncausal_multi_sequence_matches_brute_force():
     ref = brute(wl)
     for key in ref:
         np.testing.assert_allclose(got[key], ref[key], rtol=1e-12, atol=1e-12)
+
+
+# -- sliding window ("llama.cpp and the ubatch", "The mask is doing the work":
+# the window rule is elided; reading: a key is outside the window when the
+# query's position minus the key's is at least the window)
+
+def _swa(wl, w):
+    import dataclasses
+    wl = dataclasses.replace(wl, swa=w)
+    for bt in wl.batches:
+        bt.measured = True
+    return wl
+
+
+@pytest.mark.parametrize("w", [1, 3, 6])
+def test_swa_matches_brute_force(w):
+    for wl in (W.tiny(), W.prefix_decode(n_seq=3, prefix=5, private=4, n_layer=1, kv_size=64)):
+        wl = _swa(wl, w)
+        wl.n_head, wl.n_head_kv, wl.head_dim = (2, 1, 16) if wl.name == "tiny" else (4, 2, 8)
+        got, _ = run_oracle(wl)
+        ref = brute(wl)
+        for key in ref:
+            np.testing.assert_allclose(got[key], ref[key], rtol=1e-12, atol=1e-12)
+
+
+def test_swa_wider_than_the_history_is_causal():
+    wl = W.tiny()
+    base, _ = run_oracle(_swa(wl, 0))
+    wide, _ = run_oracle(_swa(W.tiny(), 15))          # positions 0..14: every key within 15
+    narrow, _ = run_oracle(_swa(W.tiny(), 14))
+    for key in base:
+        np.testing.assert_array_equal(wide[key], base[key])
+    assert any(not np.array_equal(narrow[key], base[key]) for key in base)
+
+
+def test_swa_window_of_one_returns_the_own_value():
+    wl = _swa(W.tiny(), 1)
+    got, _ = run_oracle(wl)
+    for b, bt in enumerate(wl.batches):
+        v = f16_round(wl.tensor(b, 0, W.KIND_V)).astype(np.float64)
+        G, d = wl.n_head // wl.n_head_kv, wl.head_dim              # head h reads KV head h // G
+        want = np.concatenate([v[:, (h // G) * d:(h // G + 1) * d] for h in range(wl.n_head)], axis=1)
+        np.testing.assert_allclose(got[(b, 0)], want, rtol=0, atol=1e-12)
+
+
+def test_swa_needle_at_the_window_edge():
+    """A dominant key one position inside the window takes over the output;
+    the same key one position further back changes nothing."""
+    H, Hk, d, w = 2, 1, 16, 4
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal(H * d)
+    base_k = rng.standard_normal((10, Hk * d)) * 0.1
+    base_v = rng.standard_normal((10, Hk * d))
+    def run(needle_pos):
+        eng = OracleEngine(1, H, Hk, d, kv_size=64, swa=w)
+        k, v = base_k.copy(), base_v.copy()
+        if needle_pos is not None:
+            k[needle_pos] = 50.0 * q[:d] / np.linalg.norm(q[:d])
+            v[needle_pos] = 7.0
+        st, ubs, _ = eng.split(10, list(range(10)), [(0,)] * 10, [1] * 10)
+        eng.commit(ubs[0])
+        eng.store(ubs[0], 0, k, v)
+        return eng.attend(ubs[0], 0, np.tile(q, (10, 1)))[9]
+    plain = run(None)
+    assert np.allclose(run(9 - w), plain, atol=1e-12)          # just outside: no effect
+    inside = run(9 - w + 1)
+    assert np.allclose(inside[:d], 7.0, atol=1e-3)                # just inside: takes over
