@@ -15,9 +15,10 @@
  *   3. each ubatch writes its K/V rows, rounded to F16, into per-layer
  *      tensors of shape [n_stream][kv_size][n_head_kv * head_dim] ("What
  *      does llama.cpp's KV cache ...", "The tensor's three dimensions");
- *   4. the KQ mask hides empty cells, cells of other sequences and future
- *      positions, the query masking with its first sequence id ("llama.cpp
- *      and the ubatch", "The mask is doing the work");
+ *   4. the KQ mask hides empty cells, cells of other sequences, future
+ *      positions and, with a sliding window, positions outside it, the query
+ *      masking with its first sequence id ("llama.cpp and the ubatch", "The
+ *      mask is doing the work");
  *   5. masked-softmax grouped-query attention runs over the visible cells.
  *
  * Conventions for every entry point:
@@ -91,6 +92,10 @@ typedef struct kvattn_params {
   int32_t attend_layers;  /* scheduling hint, no effect on results: layers per kvattn_attend
                              call the caller will use (0 = 1); sizes the work items */
   int32_t split_mode;     /* KVATTN_SPLIT_*: how kvattn_split cuts a batch into ubatches */
+  int32_t swa_window;     /* sliding window in positions, 0 = none: a query at position p sees no
+                             cell with position <= p - swa_window ("llama.cpp and the ubatch",
+                             "The mask is doing the work", whose window rule is elided; this is
+                             the reading taken) */
 } kvattn_params;
 
 /* Batch -> ubatch split strategies ("Batch、Ubatch 与解码主循环", Part C).

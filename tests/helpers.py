@@ -29,7 +29,7 @@ def oracle_run(wl, layers, measured_only=True, keep_masks=False, n_ubatch=None):
     order for measured batches; masks[(b, u)] when keep_masks."""
     eng = OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
                        wl.n_seq_max, wl.n_batch, wl.n_ubatch if n_ubatch is None else n_ubatch, wl.causal,
-                       cell_order=wl.cell_order, layers=layers, split_mode=wl.split_mode)
+                       cell_order=wl.cell_order, layers=layers, split_mode=wl.split_mode, swa=wl.swa)
     res, masks, ubmeta = {}, {}, {}
     for b, bt in enumerate(wl.batches):
         st, ubs, _ = eng.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
@@ -57,7 +57,7 @@ def make_ctx(wl, device="cuda:0", n_ubatch=None, attend_layers=0):
     return Context(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream, wl.n_seq_max,
                    wl.n_batch, wl.n_ubatch if n_ubatch is None else n_ubatch, wl.causal,
                    cell_order=wl.cell_order, device=device, attend_layers=attend_layers,
-                   split_mode=wl.split_mode)
+                   split_mode=wl.split_mode, swa_window=wl.swa)
 
 
 def gpu_run(wl, layers, layer_chunk=None, only_outputs=False, on_ubatch=None, ctx=None, n_ubatch=None,

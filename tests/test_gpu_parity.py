@@ -382,3 +382,27 @@ def test_prefix_separate_copies_across_streams():
     for s in range(4):
         pos, mask = ctx4.cells(s)
         assert int((pos >= 0).sum()) == 200 + 2 * 31       # the prefix copy, 2 sequences x (30 + 1)
+
+
+@pytest.mark.parametrize("name,w", [("tiny", 3), ("prefill", 100), ("prefill", 300), ("cb_decode", 50),
+                                    ("mixed", 64), ("prefix", 200), ("prefix", 1)])
+def test_sliding_window_parity(name, w):
+    """A sliding window of w positions (reading of the elided window rule: a
+    cell is hidden when the query's position minus its position is >= w) in
+    the dense diagnostic mask (bit for bit), the matrix-core kernel (masked
+    and skipped tiles) and the vector-ALU kernel."""
+    import dataclasses
+    wl = dataclasses.replace(small(name), swa=w)
+    layers = list(range(wl.n_layer))
+    print(f"[gpu] sliding window {w} on {name}", flush=True)
+    eng, ref, masks, meta = oracle_run(wl, layers, keep_masks=True)
+    ub_index = {b: 0 for b in range(len(wl.batches))}
+
+    def check(ctx, b, ub):
+        m = ctx.mask(ub).cpu().numpy().view(np.uint16)
+        assert np.array_equal(m, masks[(b, ub_index[b])].view(np.uint16))
+        ub_index[b] += 1
+
+    _, got = gpu_run(wl, layers, on_ubatch=check)
+    for key in ref:
+        assert_parity(got[key], ref[key], tag=f"window {w} {name} {key}")

@@ -277,7 +277,7 @@ def test_workspace_and_cache_bytes():
 
 
 @pytest.mark.parametrize("kw", [dict(head_dim=48), dict(n_head=3, n_head_kv=2), dict(n_head=32, n_head_kv=2),
-                                dict(n_seq_max=65), dict(kv_size=0), dict(split_mode=4), dict(split_mode=-1),
+                                dict(n_seq_max=65), dict(kv_size=0), dict(split_mode=4), dict(split_mode=-1), dict(swa_window=-1),
                                 # one layer's K tensor at 2 GiB: 2^20 cells x 8 heads x 128 x 2 B
                                 dict(kv_size=1 << 20, n_head=8, n_head_kv=8, head_dim=128)])
 def test_create_rejects_bad_geometry(kw):

@@ -507,6 +507,7 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   a.n_head = g.n_head;
   a.n_head_kv = g.n_head_kv;
   a.causal = g.causal;
+  a.swa = g.swa;
   a.scale_log2e = g.kq_scale * 1.4426950408889634f;
   a.layer_bytes = static_cast<uint32_t>(static_cast<size_t>(g.n_stream) * g.kv_size * g.E() * 2);
   const int64_t per = std::max<int64_t>(1, P.n_partial_rows);
@@ -555,6 +556,7 @@ int kvattn_get_mask(kvattn_ctx* c, const kvattn_ubatch* ub, void* d_mask, size_t
   a.n_kv = P.n_kv;
   a.kv_size = c->core.geo().kv_size;
   a.causal = c->core.geo().causal;
+  a.swa = c->core.geo().swa;
   HIP_TRY(c, launch_mask(a, static_cast<hipStream_t>(hip_stream)));
   return KVATTN_OK;
 }
@@ -816,6 +818,7 @@ int kvattn_get_params(const kvattn_ctx* c, kvattn_params* out) {
   out->device = c->device;
   out->attend_layers = g.attend_layers;
   out->split_mode = g.split_mode;
+  out->swa_window = g.swa;
   return KVATTN_OK;
 }
 

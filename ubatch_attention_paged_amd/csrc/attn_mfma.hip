@@ -40,7 +40,9 @@ KVATTN_DEV float dot2_sum(half2v h, float acc) {
 
 constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag the true max
 
-template <int D, int G>
+// SWA: the sliding-window variant (a.swa > 0); the other compiles without any
+// of its tests
+template <int D, int G, bool SWA>
 __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(AttnArgs a) {
   constexpr int RB = kMfmaRowBlocks;              // 32-row blocks per wavefront
   constexpr int QT = kMfmaRowsPerItem / G;        // queries per item
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
 
   // this lane's query rows: row block b of wavefront w is rows
   // 32 * (w * RB + b) .. +31, the lane owning row lane % 32 of it
-  int t_r[RB], h_r[RB], pos_lim[RB], qseq[RB];
+  int t_r[RB], h_r[RB], pos_lim[RB], pos_lo[RB], qseq[RB];
   bool qvalid[RB];
   SlotInfo si[RB];
   bool any_row = false;
@@ -91,6 +93,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     si[b] = a.slots[a.qlist[it.q_off + (qvalid[b] ? t_r[b] : 0)]];
     h_r[b] = kvh * G + hg;
     pos_lim[b] = a.causal ? si[b].pos : INT32_MAX - 1;   // largest visible cell position
+    pos_lo[b] = SWA ? si[b].pos - a.swa + 1 : INT32_MIN;   // smallest, with a sliding window
     qseq[b] = si[b].seq0;
     any_row |= qvalid[b];
   }
@@ -122,7 +125,9 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     }
   }
 
-  // tiles of this item; trailing tiles in the future of every query are dropped
+  // tiles of this item; trailing tiles in the future of every query are
+  // dropped, and with a sliding window leading tiles behind every query's
+  // window (tiles are walked from t0)
   const int tb = ci.tile_base + (it.c0 - ci.cell_off) / KT;
   int ntile = (it.c1 - it.c0 + KT - 1) / KT;
   if (a.causal) {
@@ -130,6 +135,14 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     for (int k = lane; k < ntile; k += 64)
       if (a.tile_min[tb + k] <= it.qpos_max) last = k;
     ntile = wave_max_i(last) + 1;
+  }
+  const int win_lo = SWA ? it.qpos_min - a.swa + 1 : INT32_MIN;   // no query sees below this
+  int t0 = 0;
+  if constexpr (SWA) {
+    int first = ntile;
+    for (int k = lane; k < ntile; k += 64)
+      if (a.tile_max[tb + k] >= win_lo) first = min(first, k);
+    t0 = wave_min_i(first);
   }
 
   floatx16 oacc[RB][DP / 32];
@@ -172,19 +185,19 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
       mk = in ? a.csr_mask[idx] : 0ULL;
     }
   };
-  if (ntile > 0) {
+  if (ntile > t0) {
     int cfirst[NP];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) cfirst[p] = loader ? cell_at(0, row0 + p * ROW_STEP) : -1;
-    issue(0, cfirst);
+    for (int p = 0; p < NP; ++p) cfirst[p] = loader ? cell_at(t0, row0 + p * ROW_STEP) : -1;
+    issue(t0, cfirst);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) cnext[p] = (loader && ntile > 1) ? cell_at(1, row0 + p * ROW_STEP) : -1;
+    for (int p = 0; p < NP; ++p) cnext[p] = (loader && ntile > t0 + 1) ? cell_at(t0 + 1, row0 + p * ROW_STEP) : -1;
   }
 
   const int s16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
-  for (int i = 0; i < ntile; ++i) {
-    const int buf = i & 1;
+  for (int i = t0; i < ntile; ++i) {
+    const int buf = SWA ? (i - t0) & 1 : i & 1;
     // stage tile i
     if (loader) {
 #pragma unroll
@@ -210,7 +223,9 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     const int nk = min(KT, it.c1 - (it.c0 + i * KT));
     const int tmin = a.tile_min[tb + i], tmax = a.tile_max[tb + i];
     if (a.causal && tmin > it.qpos_max) continue;
-    const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min);
+    if (SWA && tmax < win_lo) continue;
+    const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min) &&
+                      (!SWA || tmin >= it.qpos_max - a.swa + 1);
 
     // The tile is two 32-cell blocks, each with its own online-softmax step
     // per row block.  Every K or V fragment read from LDS feeds the RB row
@@ -243,8 +258,9 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb * 32 + acc_row(e, lane);
-          const bool vis =
-              (kpos_s[buf][key] <= pos_lim[b]) & static_cast<bool>((kmask_s[buf][key] >> qseq[b]) & 1ULL);
+          const int kp = kpos_s[buf][key];
+          bool vis = (kp <= pos_lim[b]) & static_cast<bool>((kmask_s[buf][key] >> qseq[b]) & 1ULL);
+          if constexpr (SWA) vis &= kp >= pos_lo[b];
           sb[e] = vis ? sb[e] : -INFINITY;
         }
       }
@@ -358,7 +374,10 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
 
 template <int D, int G>
 static void mfma_launch(const AttnArgs& a, int n_il, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn_mfma<D, G>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256), 0, s, a);
+  if (a.swa > 0)
+    hipLaunchKernelGGL((k_attn_mfma<D, G, true>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_attn_mfma<D, G, false>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256), 0, s, a);
 }
 
 template <int D>

@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
       const half8* vp = reinterpret_cast<const half8*>(Vl + off);
       kr[u][0] = kp[0]; kr[u][1] = kp[1];
       vr[u][0] = vp[0]; vr[u][1] = vp[1];
-      vis[u] = c + u < it.c1 && (!a.causal || lp[u] <= si.pos) && ((lm[u] >> si.seq0) & 1ULL);
+      vis[u] = c + u < it.c1 && (!a.causal || lp[u] <= si.pos) && ((lm[u] >> si.seq0) & 1ULL) &&
+               (a.swa == 0 || si.pos - lp[u] < a.swa);
     }
   };
   auto compute = [&](const half8 (&kr)[U][2], const half8 (&vr)[U][2], const bool (&vis)[U]) {

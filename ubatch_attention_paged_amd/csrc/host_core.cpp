@@ -63,6 +63,11 @@ int make_geometry(const kvattn_params& p, Geometry& g, std::string& err) {
   g.n_ubatch = std::min(g.n_batch, p.n_ubatch == 0 ? nb_in : p.n_ubatch);
   g.kq_scale = p.kq_scale != 0.f ? p.kq_scale : 1.0f / std::sqrt(static_cast<float>(p.head_dim));
   g.attend_layers = std::max(1, std::min(p.attend_layers, p.n_layer));
+  if (p.swa_window < 0) {
+    err = "swa_window must be >= 0";
+    return KVATTN_EINVAL;
+  }
+  g.swa = p.swa_window;
   if (p.split_mode < KVATTN_SPLIT_AUTO || p.split_mode > KVATTN_SPLIT_SEQ) {
     err = "split_mode must be one of KVATTN_SPLIT_AUTO, _SIMPLE, _EQUAL, _SEQ";
     return KVATTN_EINVAL;

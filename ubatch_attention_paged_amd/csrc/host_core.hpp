@@ -21,6 +21,7 @@ struct Geometry {
   float kq_scale = 0.f;
   int32_t attend_layers = 1;            // layers per attend call (work-item sizing hint)
   int32_t split_mode = 0;               // KVATTN_SPLIT_SIMPLE / _EQUAL / _SEQ (AUTO resolved)
+  int32_t swa = 0;                      // sliding window in positions, 0 = none
   int32_t E() const { return n_head_kv * head_dim; }
   int32_t G() const { return n_head / n_head_kv; }
 };

@@ -341,7 +341,8 @@ __global__ __launch_bounds__(256) void k_mask_dense(MaskArgs a) {
   const SlotInfo q = a.slots[i];
   const int64_t idx = static_cast<int64_t>(q.stream) * a.kv_size + j;
   const int32_t p = a.cpos[idx];
-  const bool vis = p >= 0 && ((a.cmask[idx] >> q.seq0) & 1ULL) && (!a.causal || p <= q.pos);
+  const bool vis = p >= 0 && ((a.cmask[idx] >> q.seq0) & 1ULL) && (!a.causal || p <= q.pos) &&
+                   (a.swa == 0 || q.pos - p < a.swa);
   a.mask[static_cast<int64_t>(i) * a.n_kv + j] = vis ? 0x0000 : 0xFC00;
 }
 

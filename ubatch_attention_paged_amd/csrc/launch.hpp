@@ -73,6 +73,7 @@ struct AttnArgs {
   int32_t n_head;
   int32_t n_head_kv;
   int32_t causal;
+  int32_t swa;                // sliding window in positions, 0 = none
   float scale_log2e;          // kq_scale * log2(e)
   uint32_t layer_bytes;       // bytes of one layer's K (= V) tensor, < 2 GiB
 };
@@ -82,7 +83,7 @@ struct MaskArgs {
   const uint64_t* cmask;
   const SlotInfo* slots;      // ubatch order
   uint16_t* mask;             // [n_rows][n_kv]
-  int32_t n_rows, n_kv, kv_size, causal;
+  int32_t n_rows, n_kv, kv_size, causal, swa;
 };
 
 // Sequence-state records (kernels_state.hip).  Word offsets: the blob is

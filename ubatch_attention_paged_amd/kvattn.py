@@ -44,7 +44,7 @@ class kvattn_params(ctypes.Structure):
                 ("k_layers", _vpp), ("v_layers", _vpp),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("device", ctypes.c_int32), ("attend_layers", ctypes.c_int32),
-                ("split_mode", ctypes.c_int32)]
+                ("split_mode", ctypes.c_int32), ("swa_window", ctypes.c_int32)]
 
 
 class kvattn_batch(ctypes.Structure):
@@ -411,7 +411,7 @@ class Context:
 
     def __init__(self, n_layer, n_head, n_head_kv, head_dim, kv_size, n_stream=1, n_seq_max=1,
                  n_batch=0, n_ubatch=512, causal=True, kq_scale=0.0, cell_order=None, device=None,
-                 attend_layers=0, split_mode=0):
+                 attend_layers=0, split_mode=0, swa_window=0):
         self.n_layer, self.n_head, self.n_head_kv, self.head_dim = n_layer, n_head, n_head_kv, head_dim
         self.kv_size, self.n_stream, self.n_seq_max = kv_size, n_stream, n_seq_max
         self.E = n_head_kv * head_dim
@@ -421,6 +421,7 @@ class Context:
         p.n_batch, p.n_ubatch, p.causal, p.kq_scale = n_batch, n_ubatch, int(bool(causal)), kq_scale
         p.attend_layers = attend_layers
         p.split_mode = SPLIT_MODES[split_mode] if isinstance(split_mode, str) else int(split_mode)
+        p.swa_window = swa_window
         self._order = None
         if cell_order is not None:
             self._order, p.cell_order = _arr(np.asarray(cell_order).reshape(-1), np.int32)
