@@ -103,6 +103,34 @@ def test_end_to_end_parity(name):
     ctx.close()
 
 
+HEAD_SHAPES = [(16, 1), (16, 4), (32, 2), (32, 8), (64, 1), (64, 8), (128, 1), (128, 4)]
+
+
+@pytest.mark.parametrize("d,g", HEAD_SHAPES)
+def test_mfma_head_shapes(d, g):
+    """Every head size and query-head group the matrix-core kernel is built
+    for.  Its LDS tile layout differs per head size (row length, segment
+    swizzle, and below 32 the zero V columns the transpose reads cover), so
+    each runs prompt ubatches long enough for matrix-core work items, with
+    ragged tails, against the oracle."""
+    wl = W.mixed(n_prompt_seq=2, n_decoders=4, prompt_range=(70, 200), ctx_range=(10, 90), n_layer=1,
+                 n_stream=1, kv_size=1024, n_batch=256, n_ubatch=128)
+    wl.n_head, wl.n_head_kv, wl.head_dim = 2 * g, 2, d
+    layers = [0]
+    print(f"[gpu] head shape d={d} g={g}: {wl.note}", flush=True)
+    _, ref, _, _ = oracle_run(wl, layers, keep_masks=False)
+    items = {"mfma": 0}
+
+    def count(ctx, b, ub):
+        items["mfma"] += ctx.plan_stats()["n_items_mfma"]
+
+    ctx, got = gpu_run(wl, layers, on_ubatch=count)
+    for key in ref:
+        assert_parity(got[key], ref[key], tag=f"d={d} g={g} batch {key[0]}")
+    assert items["mfma"] > 0
+    ctx.close()
+
+
 @pytest.mark.parametrize("name", ["prefill", "cb_decode", "mixed", "prefix32"])
 def test_class_lists_bit_exact(name):
     wl = small(name)

@@ -5,9 +5,13 @@
 // rows.  The item's cells are walked in 64-cell tiles:
 //
 //  * K and V rows of a tile (that head's 2*D bytes of each cell row) are
-//    gathered through the cell list with 16 B loads into registers one tile
-//    ahead, then stored row-major into a double-buffered LDS ring; the cell
-//    indices themselves are fetched two tiles ahead.  One barrier per tile.
+//    gathered through the cell list by buffer loads that write LDS directly
+//    (16 B per lane, 1 KB per wavefront instruction), one tile ahead, into a
+//    double-buffered ring; the cell indices are fetched two tiles ahead.  The
+//    rows sit unpadded in LDS: each lane picks which 16 B segment of its row
+//    it fetches so that the segment order inside a row is XOR-swizzled by the
+//    row index, which keeps the fragment reads free of bank conflicts.  One
+//    barrier per tile.
 //  * Wavefront w computes S^T[64 cells][its 32 rows] = K Q^T with
 //    v_mfma_f32_32x32x16_f16 (A = K rows from LDS, B = its queries, held in
 //    registers as F16 and pre-scaled by scale*log2(e)).
@@ -49,15 +53,24 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   static_assert(kMfmaRowsPerItem == 128 * RB, "4 wavefronts x RB x 32 rows");
   constexpr int KT = kTileCells;                  // cells per tile (64)
   constexpr int DP = D < 32 ? 32 : D;             // O^T rows, padded to a 32-row block
-  constexpr int KSK = D + 8;                      // K row stride (halfs): rows shift 4 banks (16 B reads)
-  constexpr int KSV = D + 16;                     // V row stride: rows shift 8 banks (8 B transpose reads)
-  constexpr int SEGS = D / 8;                     // 16 B segments per row
-  constexpr int RPP = 256 / SEGS;                 // rows one pass of 256 threads loads
-  constexpr int ROW_STEP = RPP >= KT ? KT : RPP;
-  constexpr int NP = KT / ROW_STEP;               // passes per tile
-  static_assert(KSV >= DP, "V rows must hold the padded columns");
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KT * KSK];
-  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KT * KSV];
+  // LDS tiles: K rows of D halfs, V rows of DP halfs (columns D.. of a V
+  // row are zeros), both unpadded.  One wavefront instruction of the
+  // LDS-direct load fills 1 KB = 64 segments of 16 B.
+  constexpr int SK = D / 8;                       // 16 B segments per K row
+  constexpr int SV = DP / 8;                      // per V row; segments >= SK are zero padding
+  constexpr int RK = 64 / SK, RV = 64 / SV;       // rows per instruction
+  constexpr int NK = KT / RK, NV = KT / RV;       // instructions per tile
+  constexpr int JK = (NK + 3) / 4, JV = (NV + 3) / 4;   // per wavefront
+  constexpr bool SAME_ROWS = SK == SV;            // K and V instructions cover the same rows
+  // Swizzles.  K: 16 B fragment reads by 32 consecutive rows at one segment
+  // -> the segment index is XORed with (row / rows-per-128-B) so any 8
+  // consecutive rows hit 8 different 16 B bank groups.  V: the transpose
+  // reads take 32 B (two segments) of 4 consecutive rows -> the pair index
+  // is XORed, keeping the two segments of a pair adjacent.
+  constexpr int RBK = SK >= 8 ? 1 : 8 / SK, MK = (SK < 8 ? SK : 8) - 1;
+  constexpr int RBV = SV >= 8 ? 1 : 8 / SV, MV = (SV / 2 < 4 ? SV / 2 : 4) - 1;
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KT * D];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KT * DP];
   __shared__ int32_t kpos_s[2][KT];
   __shared__ uint64_t kmask_s[2][KT];
 
@@ -73,8 +86,8 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   const bool pure = ci.pure;
   // K / V rows are gathered with range-checked buffer loads: 32-bit byte
   // offsets, and an empty slot reads zeros from an out-of-range offset
-  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(a.k[il], a.layer_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(a.v[il], a.layer_bytes);
+  const u32x4 krw = buffer_rsrc_words(a.k[il], a.layer_bytes);
+  const u32x4 vrw = buffer_rsrc_words(a.v[il], a.layer_bytes);
   const uint32_t row_bytes = static_cast<uint32_t>(E) * 2;
   const uint32_t sbase_bytes = static_cast<uint32_t>(ci.stream) * static_cast<uint32_t>(a.kv_size) * row_bytes;
 
@@ -118,12 +131,6 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
       qb[b][ks][7] = static_cast<_Float16>(x1.w * a.scale_log2e);
     }
   }
-  if (D < DP) {   // columns D .. DP-1 of every V row are read as O^T rows >= D: keep them zero
-    for (int i = tid; i < 2 * KT * (DP - D); i += 256) {
-      const int bb = i / (KT * (DP - D)), rem = i % (KT * (DP - D));
-      Vs[bb][(rem / (DP - D)) * KSV + D + rem % (DP - D)] = static_cast<_Float16>(0.f);
-    }
-  }
 
   // tiles of this item; trailing tiles in the future of every query are
   // dropped, and with a sliding window leading tiles behind every query's
@@ -157,71 +164,103 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
       for (int i = 0; i < 16; ++i) oacc[b][db][i] = 0.f;
   }
 
-  // loader geometry: thread -> (row0 + p * ROW_STEP, 16 B segment seg)
-  const int seg = tid % SEGS;
-  const int row0 = tid / SEGS;
-  const bool loader = row0 < ROW_STEP;
-  u32x4 kreg[NP], vreg[NP];
-  int cnext[NP];
-  int pk = INT32_MAX;
-  uint64_t mk = 0;
-  auto cell_at = [&](int tile, int row) {
-    const int idx = it.c0 + tile * KT + row;
-    return idx < it.c1 ? a.csr_cell[idx] : -1;
-  };
-  const uint32_t col_bytes = static_cast<uint32_t>(kvh * D + seg * 8) * 2;
-  auto issue = [&](int tile, const int* cells) {
+  // loader geometry: instruction j of wavefront wv fills LDS kilobyte
+  // t = wv + 4 j of the tile; lane -> row t * R + lane / S, stored segment
+  // lane % S, which holds the row's segment (lane % S) ^ swizzle(row)
+  const int wv = __builtin_amdgcn_readfirstlane(w);
+  int rowk[JK], rowv[JV];
+  uint32_t colk[JK], colv[JV];     // byte column in the cache row; kOobOffset = zero padding
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const uint32_t off =
-          cells[p] >= 0 ? sbase_bytes + static_cast<uint32_t>(cells[p]) * row_bytes + col_bytes : kOobOffset;
-      kreg[p] = buffer_load16(krs, off);
-      vreg[p] = buffer_load16(vrs, off);
+  for (int j = 0; j < JK; ++j) {
+    rowk[j] = (wv + 4 * j) * RK + lane / SK;
+    const int sg = (lane % SK) ^ ((rowk[j] / RBK) & MK);
+    colk[j] = static_cast<uint32_t>(kvh * D + sg * 8) * 2;
+  }
+#pragma unroll
+  for (int j = 0; j < JV; ++j) {
+    rowv[j] = (wv + 4 * j) * RV + lane / SV;
+    const int sg = (lane % SV) ^ (2 * ((rowv[j] / RBV) & MV));
+    colv[j] = sg < SK ? static_cast<uint32_t>(kvh * D + sg * 8) * 2 : kOobOffset;
+  }
+  // Everything a tile needs from memory is requested one tile (cell
+  // indices: two tiles) ahead and first read after the vmcnt(0) that opens
+  // that tile, so no wait inside a tile's compute covers the loads in flight
+  // (vmcnt retires in order: any wait would also wait for the next tile).
+  constexpr int JC = SAME_ROWS ? JK : JK + JV;     // cell indices a lane needs per tile
+  int cnext[JC];                                   // raw list entries; validity is decided at use
+  int pk = INT32_MAX, nmin = 0, nmax = 0;
+  uint64_t mk = 0;
+  auto has_k = [&](int j) { return NK % 4 == 0 || wv + 4 * j < NK; };   // wave-uniform
+  auto has_v = [&](int j) { return NV % 4 == 0 || wv + 4 * j < NV; };
+  // the list entry is read at a clamped index (no branch, no wait)
+  auto cells_of = [&](int tile, int* cells) {
+    const int base = it.c0 + tile * KT;
+#pragma unroll
+    for (int j = 0; j < JK; ++j) cells[j] = has_k(j) ? a.csr_cell[min(base + rowk[j], it.c1 - 1)] : 0;
+    if constexpr (!SAME_ROWS) {
+#pragma unroll
+      for (int j = 0; j < JV; ++j) cells[JK + j] = has_v(j) ? a.csr_cell[min(base + rowv[j], it.c1 - 1)] : 0;
     }
+  };
+  auto issue = [&](int tile, int bsel, const int* cells) {
+    const int lim = it.c1 - (it.c0 + tile * KT);     // rows of this tile inside the list
+#pragma unroll
+    for (int j = 0; j < JK; ++j)
+      if (has_k(j)) {
+        const uint32_t off =
+            rowk[j] < lim ? sbase_bytes + static_cast<uint32_t>(cells[j]) * row_bytes + colk[j] : kOobOffset;
+        buffer_load16_lds(krw, lds_addr(&Ks[bsel][(wv + 4 * j) * 512]), off);
+      }
+#pragma unroll
+    for (int j = 0; j < JV; ++j)
+      if (has_v(j)) {
+        const int cl = SAME_ROWS ? cells[j] : cells[JK + j];
+        const uint32_t off = rowv[j] < lim && colv[j] != kOobOffset
+                                 ? sbase_bytes + static_cast<uint32_t>(cl) * row_bytes + colv[j]
+                                 : kOobOffset;
+        buffer_load16_lds(vrw, lds_addr(&Vs[bsel][(wv + 4 * j) * 512]), off);
+      }
     if (tid < KT) {
       const int idx = it.c0 + tile * KT + tid;
       const bool in = idx < it.c1;
       pk = in ? a.csr_pos[idx] : INT32_MAX;
       mk = in ? a.csr_mask[idx] : 0ULL;
     }
+    nmin = a.tile_min[tb + tile];
+    nmax = a.tile_max[tb + tile];
   };
   if (ntile > t0) {
-    int cfirst[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) cfirst[p] = loader ? cell_at(t0, row0 + p * ROW_STEP) : -1;
-    issue(t0, cfirst);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) cnext[p] = (loader && ntile > t0 + 1) ? cell_at(t0 + 1, row0 + p * ROW_STEP) : -1;
+    int cfirst[JC];
+    cells_of(t0, cfirst);
+    issue(t0, 0, cfirst);
+    if (ntile > t0 + 1) cells_of(t0 + 1, cnext);
   }
 
   const int s16 = lane & 15;
   const int dsub = 16 * ((lane >> 4) & 1);
+  // read-side swizzles: row bits below the 32-row block (K) or 4-row group (V)
+  const int kswz = ((lane & 31) / RBK) & MK;
+  const int vswz = 2 * (((s16 >> 2) / RBV) & MV);
   for (int i = t0; i < ntile; ++i) {
     const int buf = SWA ? (i - t0) & 1 : i & 1;
-    // stage tile i
-    if (loader) {
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int rr = row0 + p * ROW_STEP;
-        *reinterpret_cast<u32x4*>(&Ks[buf][rr * KSK + seg * 8]) = kreg[p];
-        *reinterpret_cast<u32x4*>(&Vs[buf][rr * KSV + seg * 8]) = vreg[p];
-      }
-    }
+    // stage tile i: its rows arrived by the LDS-direct loads this thread
+    // issued (vmcnt), positions and masks go through registers
     if (tid < KT) {
       kpos_s[buf][tid] = pk;
       kmask_s[buf][tid] = mk;
     }
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
-    // tile i+1 loads and tile i+2 cell indices fly while tile i computes
+    const int tmin = __builtin_amdgcn_readfirstlane(nmin), tmax = __builtin_amdgcn_readfirstlane(nmax);
+    // tile i+1 loads and tile i+2 cell indices fly while tile i computes;
+    // buffer buf ^ 1 was last read in tile i-1, which every wave has left
     if (i + 1 < ntile) {
-      issue(i + 1, cnext);
-#pragma unroll
-      for (int p = 0; p < NP; ++p) cnext[p] = (loader && i + 2 < ntile) ? cell_at(i + 2, row0 + p * ROW_STEP) : -1;
+      issue(i + 1, buf ^ 1, cnext);
+      if (i + 2 < ntile) cells_of(i + 2, cnext);
     }
     if (!wave_rows) continue;
 
     const int nk = min(KT, it.c1 - (it.c0 + i * KT));
-    const int tmin = a.tile_min[tb + i], tmax = a.tile_max[tb + i];
     if (a.causal && tmin > it.qpos_max) continue;
     if (SWA && tmax < win_lo) continue;
     const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min) &&
@@ -243,8 +282,8 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
         for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const half8 ka =
-            *reinterpret_cast<const half8*>(&Ks[buf][(kb * 32 + (lane & 31)) * KSK + 16 * ks + 8 * half_id]);
+        const half8 ka = *reinterpret_cast<const half8*>(
+            &Ks[buf][(kb * 32 + (lane & 31)) * D + 8 * ((2 * ks + half_id) ^ kswz)]);
 #pragma unroll
         for (int b = 0; b < RB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qb[b][ks], acc[b], 0, 0, 0);
       }
@@ -297,16 +336,19 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     };
     // O^T += V^T P^T: source lane s of each 16-lane group points at cell row
     // key0 + s/4, column dsub + 4*(s%4); lane gets cells key0..key0+3 of
-    // column db*32 + lane%32 (and key0+8.. for the upper four k-values)
+    // column db*32 + lane%32 (and key0+8.. for the upper four k-values).
+    // That column sits in segment (dsub + 32 db) / 8 + (s%4) / 2 of the row,
+    // stored at that index XOR the row's pair swizzle.
     auto pv_block = [&](int kb, const half8 (&pb)[RB][2]) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int key0 = kb * 32 + 16 * st + 4 * half_id;
-        const _Float16* vb = &Vs[buf][(key0 + (s16 >> 2)) * KSV + 4 * (s16 & 3) + dsub];
+        const _Float16* vb = &Vs[buf][(key0 + (s16 >> 2)) * DP + 4 * (s16 & 1)];
 #pragma unroll
         for (int db = 0; db < DP / 32; ++db) {
-          const half4 lo = lds_read_tr16(vb + db * 32);
-          const half4 hi = lds_read_tr16(vb + db * 32 + 8 * KSV);
+          const int sg = (((dsub + 32 * db) >> 3) + ((s16 & 3) >> 1)) ^ vswz;
+          const half4 lo = lds_read_tr16(vb + 8 * sg);
+          const half4 hi = lds_read_tr16(vb + 8 * sg + 8 * DP);
           const half8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int b = 0; b < RB; ++b)

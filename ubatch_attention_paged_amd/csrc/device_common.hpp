@@ -52,6 +52,33 @@ KVATTN_DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
 }
 
+// 16 B per lane from a raw buffer straight into LDS: lane l's bytes land at
+// LDS byte address lds + 16 * l (wavefront-uniform, passed through M0); an
+// out-of-range offset writes zeros.  Issued as inline asm on purpose: the
+// compiler then inserts no waits for it (it would otherwise drain every
+// such load before any later LDS read, whatever the address), so the caller
+// owns the ordering -- an s_waitcnt vmcnt(0) before the barrier that hands
+// the data to other waves.  rsrc: the four descriptor words of
+// buffer_rsrc_words.
+KVATTN_DEV u32x4 buffer_rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  u32x4 r;
+  r[0] = static_cast<uint32_t>(a);
+  r[1] = static_cast<uint32_t>(a >> 32) & 0xffffu;   // stride 0
+  r[2] = bytes;
+  r[3] = 0x00020000u;
+  return r;
+}
+KVATTN_DEV uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
+}
+KVATTN_DEV void buffer_load16_lds(u32x4 rsrc, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(off), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Accumulator register r of lane l in a 32x32 MFMA block holds row
 // 8*(r/4) + 4*(l/32) + r%4, column l%32.
 KVATTN_DEV int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
