@@ -42,7 +42,24 @@ KVATTN_DEV float dot2_sum(half2v h, float acc) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, h), __builtin_bit_cast(fp16x2, one), acc, false);
 }
 
+// x[l] and x[l ^ 32] side by side in every lane through the VALU lane-half
+// swap (no LDS round trip, no wait on LDS reads in flight); lanes l and
+// l ^ 32 receive the same pair
+KVATTN_DEV float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+KVATTN_DEV float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 constexpr float kRescaleSlack = 8.f;   // log2 units the running max may lag the true max
+
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
 
 // SWA: the sliding-window variant (a.swa > 0); the other compiles without any
 // of its tests
@@ -153,6 +170,9 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   }
 
   floatx16 oacc[RB][DP / 32];
+  // l_run: this lane's share of each row's sum (its 16 cells of every
+  // 32-cell block); lanes l and l ^ 32 always hold the same running maximum,
+  // so the two shares are rescaled alike and added once at the end
   float m_run[RB], l_run[RB];
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
@@ -241,13 +261,19 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   // read-side swizzles: row bits below the 32-row block (K) or 4-row group (V)
   const int kswz = ((lane & 31) / RBK) & MK;
   const int vswz = 2 * (((s16 >> 2) / RBV) & MV);
+  // The tile loop exists twice: for a pure class (one sequence set that
+  // every row belongs to) visibility is the position test alone, otherwise
+  // each cell's set membership is tested too.  Purity is per work item, so
+  // the branch is taken once, outside the loop.
+  auto tile_loop = [&](auto pure_tag) {
+  constexpr bool PURE = decltype(pure_tag)::value;
   for (int i = t0; i < ntile; ++i) {
     const int buf = SWA ? (i - t0) & 1 : i & 1;
     // stage tile i: its rows arrived by the LDS-direct loads this thread
     // issued (vmcnt), positions and masks go through registers
     if (tid < KT) {
       kpos_s[buf][tid] = pk;
-      kmask_s[buf][tid] = mk;
+      if constexpr (!PURE) kmask_s[buf][tid] = mk;
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
@@ -263,7 +289,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     const int nk = min(KT, it.c1 - (it.c0 + i * KT));
     if (a.causal && tmin > it.qpos_max) continue;
     if (SWA && tmax < win_lo) continue;
-    const bool full = nk == KT && pure && (!a.causal || tmax <= it.qpos_min) &&
+    const bool full = nk == KT && PURE && (!a.causal || tmax <= it.qpos_min) &&
                       (!SWA || tmin >= it.qpos_max - a.swa + 1);
 
     // The tile is two 32-cell blocks, each with its own online-softmax step
@@ -272,9 +298,6 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     // is issued beside the exponentials of block 0, PV(0) beside the mask
     // and maximum of block 1.  PV(0) is accumulated before block 1's step may
     // rescale O: its weights are relative to the maximum in force before.
-    float rs[RB];      // this lane's share of each row's sum over this tile
-#pragma unroll
-    for (int b = 0; b < RB; ++b) rs[b] = 0.f;
     auto s_block = [&](int kb, floatx16 (&acc)[RB]) {
 #pragma unroll
       for (int b = 0; b < RB; ++b)
@@ -293,12 +316,13 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
     auto max_block = [&](int b, int kb, floatx16& sb) {
       if (!full) {
         // branch-free: cells past the list end hold position INT32_MAX and an
-        // empty sequence set, so both tests remove them
+        // empty sequence set, so either test removes them
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb * 32 + acc_row(e, lane);
           const int kp = kpos_s[buf][key];
-          bool vis = (kp <= pos_lim[b]) & static_cast<bool>((kmask_s[buf][key] >> qseq[b]) & 1ULL);
+          bool vis = kp <= pos_lim[b];
+          if constexpr (!PURE) vis &= static_cast<bool>((kmask_s[buf][key] >> qseq[b]) & 1ULL);
           if constexpr (SWA) vis &= kp >= pos_lo[b];
           sb[e] = vis ? sb[e] : -INFINITY;
         }
@@ -307,13 +331,12 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sb[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_halves(mx);
       const bool grow = mx > m_run[b] + kRescaleSlack;     // false while the row sees nothing
       if (ballot(grow)) {
         const float m_new = grow ? mx : m_run[b];
         const float alpha = m_run[b] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[b] - m_new);
         l_run[b] *= alpha;
-        rs[b] *= alpha;
 #pragma unroll
         for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
@@ -329,7 +352,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
         half2v ph;
         ph[0] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sb[e] - m_use));
         ph[1] = static_cast<_Float16>(__builtin_amdgcn_exp2f(sb[e + 1] - m_use));
-        rs[b] = dot2_sum(ph, rs[b]);     // the row sum sees the F16 weights the PV product sees
+        l_run[b] = dot2_sum(ph, l_run[b]);     // the row sum sees the F16 weights the PV product sees
         pb[e >> 3][e & 7] = ph[0];
         pb[e >> 3][(e & 7) + 1] = ph[1];
       }
@@ -371,13 +394,15 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
 #pragma unroll
     for (int b = 0; b < RB; ++b) weights(b, s1[b], mu[b], p1[b]);
     pv_block(1, p1);
-#pragma unroll
-    for (int b = 0; b < RB; ++b) {
-      rs[b] += __shfl_xor(rs[b], 32);
-      l_run[b] += rs[b];
-    }
   }
+  };
+  if (pure)
+    tile_loop(BoolTag<true>{});
+  else
+    tile_loop(BoolTag<false>{});
 
+#pragma unroll
+  for (int b = 0; b < RB; ++b) l_run[b] = sum_halves(l_run[b]);
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     if (!qvalid[b]) continue;
