@@ -75,7 +75,7 @@ KVATTN_DEV uint32_t lds_addr(const void* p) {
 KVATTN_DEV void buffer_load16_lds(u32x4 rsrc, uint32_t lds, uint32_t off) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds), "v"(off), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(rsrc)
                : "memory", "m0");
 }
 
