@@ -79,13 +79,16 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   constexpr int NK = KT / RK, NV = KT / RV;       // instructions per tile
   constexpr int JK = (NK + 3) / 4, JV = (NV + 3) / 4;   // per wavefront
   constexpr bool SAME_ROWS = SK == SV;            // K and V instructions cover the same rows
-  // Swizzles.  K: 16 B fragment reads by 32 consecutive rows at one segment
-  // -> the segment index is XORed with (row / rows-per-128-B) so any 8
-  // consecutive rows hit 8 different 16 B bank groups.  V: the transpose
-  // reads take 32 B (two segments) of 4 consecutive rows -> the pair index
-  // is XORed, keeping the two segments of a pair adjacent.
-  constexpr int RBK = SK >= 8 ? 1 : 8 / SK, MK = (SK < 8 ? SK : 8) - 1;
-  constexpr int RBV = SV >= 8 ? 1 : 8 / SV, MV = (SV / 2 < 4 ? SV / 2 : 4) - 1;
+  // Swizzles, for LDS serving 256 B (64 banks of 4 B) per cycle.  K: a
+  // 16 B fragment read serves 16 lanes per cycle, 16 consecutive rows at one
+  // segment -> the segment index is XORed with (row / rows-per-256-B), so the
+  // 16 rows land in 16 different 16 B bank groups.  V: a transpose read
+  // serves 32 lanes per cycle, 4 consecutive rows x two adjacent 32 B pairs
+  // -> the segment index is XORed with a multiple of 4 (pairs stay whole)
+  // chosen so the 8 (row, pair) reads fill the 8 32 B slots of 256 B; with
+  // two pairs per row the row stride alone does that.
+  constexpr int RBK = 16 / SK, MK = SK - 1;
+  constexpr int VSH = SV >= 16 ? 0 : SV == 8 ? 1 : 2;
   __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KT * D];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KT * DP];
   __shared__ int32_t kpos_s[2][KT];
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
 #pragma unroll
   for (int j = 0; j < JV; ++j) {
     rowv[j] = (wv + 4 * j) * RV + lane / SV;
-    const int sg = (lane % SV) ^ (2 * ((rowv[j] / RBV) & MV));
+    const int sg = (lane % SV) ^ (((rowv[j] & 3) >> VSH) << 2);
     colv[j] = sg < SK ? static_cast<uint32_t>(kvh * D + sg * 8) * 2 : kOobOffset;
   }
   // Everything a tile needs from memory is requested one tile (cell
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   const int dsub = 16 * ((lane >> 4) & 1);
   // read-side swizzles: row bits below the 32-row block (K) or 4-row group (V)
   const int kswz = ((lane & 31) / RBK) & MK;
-  const int vswz = 2 * (((s16 >> 2) / RBV) & MV);
+  const int vswz = (((s16 >> 2) & 3) >> VSH) << 2;
   // The tile loop exists twice: for a pure class (one sequence set that
   // every row belongs to) visibility is the position test alone, otherwise
   // each cell's set membership is tested too.  Purity is per work item, so
