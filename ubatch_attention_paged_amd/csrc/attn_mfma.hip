@@ -25,10 +25,14 @@
 //  * The running maximum is only moved (and O rescaled) when a row's tile
 //    maximum exceeds it by more than 2^8, so most tiles skip the rescale; the
 //    F16 weights then stay below 256.  Row sums use v_dot2 on the same F16
-//    weights the PV product consumes.
+//    weights the PV product consumes; each lane keeps its own share and the
+//    two halves of a row are added once at the end.  The row maximum crosses
+//    lane halves through v_permlane32_swap, not LDS.
 //  * Tiles entirely in the future of every query of the item are never
 //    loaded and tiles entirely visible skip the per-element mask, both from
-//    per-tile position ranges built at commit.
+//    per-tile position ranges built at commit.  The tile loop is instanced
+//    per class purity: a class with one sequence set that every row belongs
+//    to needs the position test only.
 #include "device_common.hpp"
 #include "launch.hpp"
 
