@@ -72,11 +72,19 @@ KVATTN_DEV u32x4 buffer_rsrc_words(const void* p, uint32_t bytes) {
 KVATTN_DEV uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)(p)));
 }
+// M0 is a register the compiler reserves, so the asm saves and restores it
+// itself instead of declaring it clobbered.
 KVATTN_DEV void buffer_load16_lds(u32x4 rsrc, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(rsrc)
-               : "memory", "m0");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(rsrc)
+      : "memory");
 }
 
 // Accumulator register r of lane l in a 32x32 MFMA block holds row
