@@ -528,20 +528,50 @@ def cpu_baseline(wl, budget_s=25.0):
                        f"{wl.n_layer / done_layers:.1f}")
 
 
+def kernel_source_digest(source):
+    """sha256 over a kernel source file and, recursively, the local headers
+    it includes (csrc/ or include/), in name order: a change to any of them
+    changes the compiled kernel."""
+    import hashlib
+    import re
+    dirs = [os.path.join(ROOT, "ubatch_attention_paged_amd", "csrc"), os.path.join(ROOT, "include")]
+
+    def find(name):
+        for d in dirs:
+            f = os.path.join(d, name)
+            if os.path.exists(f):
+                return f
+        return None
+
+    seen, todo = {}, [source]
+    while todo:
+        name = todo.pop()
+        if name in seen:
+            continue
+        f = find(name)
+        if f is None:
+            continue
+        seen[name] = open(f, "rb").read()
+        todo.extend(re.findall(r'#include "([^"]+)"', seen[name].decode("utf-8", "replace")))
+    h = hashlib.sha256()
+    for name in sorted(seen):
+        h.update(name.encode())
+        h.update(seen[name])
+    return h.hexdigest()
+
+
 def committed_traffic(kernel, source):
     """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE /
     WRITE_SIZE summary, scaled by the copy-kernel calibration recorded there;
-    None when no summary exists or the kernel source changed since it was
-    taken (the summary stores the source's sha256)."""
-    import hashlib
+    None when no summary exists or the kernel's sources changed since it was
+    taken (the summary stores kernel_source_digest of them)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
-    src = os.path.join(ROOT, "ubatch_attention_paged_amd", "csrc", source)
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = kernel_source_digest(source)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_digest") != digest:
         return None
     return round(rec["bytes_per_launch"])
 
