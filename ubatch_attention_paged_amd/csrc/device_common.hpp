@@ -40,17 +40,7 @@ KVATTN_DEV half4 lds_read_tr16(const _Float16* p) {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Raw buffer resource over [p, p + bytes) (gfx9-family descriptor word 3,
-// stride 0).  Loads through it are range-checked by the hardware: a load at
-// an offset at or past `bytes` returns zeros instead of touching memory.
-KVATTN_DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), static_cast<short>(0), static_cast<int>(bytes),
-                                          0x00020000);
-}
 constexpr uint32_t kOobOffset = 0x80000000u;   // past any buffer (buffers stay below 2 GiB)
-KVATTN_DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
-}
 
 // 16 B per lane from a raw buffer straight into LDS: lane l's bytes land at
 // LDS byte address lds + 16 * l (wavefront-uniform, passed through M0); an
@@ -58,8 +48,12 @@ KVATTN_DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // compiler then inserts no waits for it (it would otherwise drain every
 // such load before any later LDS read, whatever the address), so the caller
 // owns the ordering -- an s_waitcnt vmcnt(0) before the barrier that hands
-// the data to other waves.  rsrc: the four descriptor words of
-// buffer_rsrc_words.
+// the data to other waves.
+//
+// buffer_rsrc_words: the four words of a raw buffer descriptor over
+// [p, p + bytes) (gfx9-family word 3, stride 0).  Loads through it are
+// range-checked by the hardware: an offset at or past `bytes` reads (or
+// writes into LDS) zeros without touching memory.
 KVATTN_DEV u32x4 buffer_rsrc_words(const void* p, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);
   u32x4 r;
