@@ -598,8 +598,8 @@ def main():
                     help="restrict the decode runs to this workload (repeatable)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is not sharded "
-              f"across GPUs in this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the attention path is not "
+              f"sharded across GPUs; run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     from synthetic import workloads as W

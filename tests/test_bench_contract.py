@@ -1,0 +1,51 @@
+"""bench.py's contract logic, on the CPU: it refuses more than one GPU before
+touching any device, and it reports a committed HBM-traffic figure only while
+the kernel source and every local header it includes still hash to the
+digest recorded with the counters."""
+
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_is_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
+    import bench
+    csrc = tmp_path / "ubatch_attention_paged_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "include").mkdir()
+    (tmp_path / "profiles").mkdir()
+    (csrc / "k.hip").write_text('#include "a.hpp"\n#include <hip/hip_runtime.h>\nkernel\n')
+    (csrc / "a.hpp").write_text('#include "b.hpp"\n#include "api.h"\n')
+    (csrc / "b.hpp").write_text("// b\n")
+    (tmp_path / "include" / "api.h").write_text("// api\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    digest = bench.kernel_source_digest("k.hip")
+    rec = {"source_digest": digest, "bytes_per_launch": 1234.4}
+    (tmp_path / "profiles" / "k_x_traffic.json").write_text(json.dumps(rec))
+    assert bench.committed_traffic("k_x", "k.hip") == 1234
+    # a header two includes deep, then one under include/
+    (csrc / "b.hpp").write_text("// b, changed\n")
+    assert bench.kernel_source_digest("k.hip") != digest
+    assert bench.committed_traffic("k_x", "k.hip") is None
+    (csrc / "b.hpp").write_text("// b\n")
+    assert bench.committed_traffic("k_x", "k.hip") == 1234
+    (tmp_path / "include" / "api.h").write_text("// api, changed\n")
+    assert bench.committed_traffic("k_x", "k.hip") is None
+    # no summary at all
+    assert bench.committed_traffic("k_y", "k.hip") is None
+
+
+def test_committed_summaries_record_a_digest():
+    for name in ("k_attn_mfma_traffic.json", "k_attn_valu_traffic.json"):
+        rec = json.load(open(os.path.join(ROOT, "profiles", name)))
+        assert len(rec["source_digest"]) == 64 and rec["bytes_per_launch"] > 0
