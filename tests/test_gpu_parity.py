@@ -131,6 +131,34 @@ def test_mfma_head_shapes(d, g):
     ctx.close()
 
 
+@pytest.mark.parametrize("swa", [0, 4500])
+def test_mfma_long_context_items(swa):
+    """Matrix-core items longer than 64 tiles: a 5200-token context is stored
+    unmeasured, then a 100-token chunk attends over all 5300 cells (83 tiles
+    per item, so the causal tile trimming strides lanes more than once and
+    the LDS ring turns over 80 times); with a 4500-position sliding window the
+    walk starts past the first tiles."""
+    batches = (W._prompt_batches((0,), 0, 5200, 1024, measured=False) +
+               W._prompt_batches((0,), 5200, 100, 1024, measured=True))
+    wl = W.Workload("long_context", 1, 4, 2, 64, kv_size=8192, n_stream=1, n_seq_max=1, seed=2601,
+                    batches=batches, n_batch=1024, n_ubatch=512, swa=swa,
+                    note=f"5200-token context + 100-token chunk, window {swa}")
+    layers = [0]
+    print(f"[gpu] long-context items: {wl.note}", flush=True)
+    _, ref, _, _ = oracle_run(wl, layers)
+    items = {"mfma": 0}
+
+    def count(ctx, b, ub):
+        items["mfma"] += ctx.plan_stats()["n_items_mfma"]
+
+    ctx, got = gpu_run(wl, layers, on_ubatch=count)
+    assert len(ref) == 1
+    for key in ref:
+        assert_parity(got[key], ref[key], tag=f"long context, window {swa}")
+    assert items["mfma"] > 0
+    ctx.close()
+
+
 @pytest.mark.parametrize("name", ["prefill", "cb_decode", "mixed", "prefix32"])
 def test_class_lists_bit_exact(name):
     wl = small(name)
