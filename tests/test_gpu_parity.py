@@ -131,6 +131,35 @@ def test_mfma_head_shapes(d, g):
     ctx.close()
 
 
+@pytest.mark.parametrize("d,g", [(128, 1), (128, 4), (64, 1), (64, 4)])
+def test_valu_head_shapes(d, g):
+    """The vector-ALU decode kernel's other (head_dim, group) instances (the
+    workloads above run group 2): a cache row is 1024 numbers either way, so
+    lanes map to KV heads differently per head size, and the group sets how
+    many query heads each lane's K/V feeds.  Contexts up to 300 cells are cut
+    into split-K chunks, so the merge runs too."""
+    wl = W.cb_decode(n_seq=16, lengths=(5, 40, 130, 300), n_layer=1, kv_size=4096)
+    wl.n_head_kv = 1024 // d
+    wl.n_head = wl.n_head_kv * g
+    wl.head_dim = d
+    layers = [0]
+    print(f"[gpu] vector-ALU head shape d={d} g={g}", flush=True)
+    _, ref, _, _ = oracle_run(wl, layers)
+    items = {"valu": 0}
+
+    def count(ctx, b, ub):
+        items["valu"] += ctx.plan_stats()["n_items_valu"]
+
+    ctx, got = gpu_run(wl, layers, on_ubatch=count)
+    worst = 0.0
+    for key in ref:
+        ma, _ = assert_parity(got[key], ref[key], tag=f"d={d} g={g} batch {key[0]}")
+        worst = max(worst, ma)
+    assert items["valu"] > 0
+    assert worst < 2e-5, worst      # fp32 throughout on this path
+    ctx.close()
+
+
 @pytest.mark.parametrize("swa", [0, 4500])
 def test_mfma_long_context_items(swa):
     """Matrix-core items longer than 64 tiles: a 5200-token context is stored
