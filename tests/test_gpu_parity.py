@@ -103,7 +103,7 @@ def test_end_to_end_parity(name):
     ctx.close()
 
 
-HEAD_SHAPES = [(16, 1), (16, 4), (32, 2), (32, 8), (64, 1), (64, 8), (128, 1), (128, 4)]
+HEAD_SHAPES = [(d, g) for d in (16, 32, 64, 128) for g in (1, 2, 4, 8)]   # every compiled instance
 
 
 @pytest.mark.parametrize("d,g", HEAD_SHAPES)
