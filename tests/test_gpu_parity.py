@@ -106,8 +106,9 @@ def test_end_to_end_parity(name):
 HEAD_SHAPES = [(d, g) for d in (16, 32, 64, 128) for g in (1, 2, 4, 8)]   # every compiled instance
 
 
+@pytest.mark.parametrize("swa", [0, 60])
 @pytest.mark.parametrize("d,g", HEAD_SHAPES)
-def test_mfma_head_shapes(d, g):
+def test_mfma_head_shapes(d, g, swa):
     """Every head size and query-head group the matrix-core kernel is built
     for.  Its LDS tile layout differs per head size (row length, segment
     swizzle, and below 32 the zero V columns the transpose reads cover), so
@@ -116,8 +117,9 @@ def test_mfma_head_shapes(d, g):
     wl = W.mixed(n_prompt_seq=2, n_decoders=4, prompt_range=(70, 200), ctx_range=(10, 90), n_layer=1,
                  n_stream=1, kv_size=1024, n_batch=256, n_ubatch=128)
     wl.n_head, wl.n_head_kv, wl.head_dim = 2 * g, 2, d
+    wl.swa = swa              # 60 positions: prompts of up to 200 tokens skip their leading tiles
     layers = [0]
-    print(f"[gpu] head shape d={d} g={g}: {wl.note}", flush=True)
+    print(f"[gpu] head shape d={d} g={g} window {swa}: {wl.note}", flush=True)
     _, ref, _, _ = oracle_run(wl, layers, keep_masks=False)
     items = {"mfma": 0}
 
@@ -126,7 +128,7 @@ def test_mfma_head_shapes(d, g):
 
     ctx, got = gpu_run(wl, layers, on_ubatch=count)
     for key in ref:
-        assert_parity(got[key], ref[key], tag=f"d={d} g={g} batch {key[0]}")
+        assert_parity(got[key], ref[key], tag=f"d={d} g={g} window {swa} batch {key[0]}")
     assert items["mfma"] > 0
     ctx.close()
 
