@@ -164,7 +164,13 @@ int kvattn_create(const kvattn_params *p, kvattn_ctx **out);
 void kvattn_destroy(kvattn_ctx *ctx);
 
 /* HOST-ONLY.  Validate + auto-fill the batch, split it into ubatches and
- * reserve a cell for every slot of every ubatch, all-or-nothing.  Writes up
+ * reserve a cell for every slot of every ubatch, all-or-nothing.  Follows
+ * "Batch、Ubatch 与解码主循环", Part F (the decode loop validates and fills
+ * the batch, then splits it) and Part C (split_simple / split_equal /
+ * split_seq; every ubatch's cells are reserved before any runs); the
+ * n_tokens <= n_batch check is "llama.cpp and the ubatch", "Three things
+ * called batch", and output_ids the batch-row -> output-row map of "Where
+ * the memory actually sits" on the same page.  Writes up
  * to cap ubatches to ubs[] and their count to *n_ubs (cap too small ->
  * KVATTN_EINVAL, nothing reserved).  output_ids, when not NULL, receives
  * n_batch entries: the rank of each flagged batch row among flagged rows,
@@ -173,7 +179,11 @@ void kvattn_destroy(kvattn_ctx *ctx);
 int kvattn_split(kvattn_ctx *ctx, const kvattn_batch *b, kvattn_ubatch *ubs, int32_t cap,
                  int32_t *n_ubs, int32_t *output_ids);
 
-/* Write K/V rows of layers il0 .. il0+n_il-1.  k_cur/v_cur are host arrays
+/* Write K/V rows of layers il0 .. il0+n_il-1 ("Batch、Ubatch 与解码主循环",
+ * Part D: a ubatch writes its keys and values into its cells, which later
+ * ubatches read; the row layout is that of "What does llama.cpp's KV cache
+ * actually look like in memory?", "The tensor's three dimensions").
+ * k_cur/v_cur are host arrays
  * of n_il device pointers, each fp32 [n_tokens][n_head_kv*head_dim] in
  * ubatch slot order; rows are rounded to F16 (nearest-even) into the
  * ubatch's cells.  The first call with il0 == 0 commits the ubatch: its
@@ -185,7 +195,10 @@ int kvattn_store(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t 
                  const void *const *k_cur, const void *const *v_cur, void *hip_stream);
 
 /* Attention of layers il0 .. il0+n_il-1 for the most recently committed
- * ubatch.  q/out are host arrays of n_il device pointers; q is fp32
+ * ubatch: masked-softmax attention of every query slot over the cells the
+ * mask leaves visible ("llama.cpp and the ubatch", "The mask is doing the
+ * work" and "Chunked prefill is the same mechanism": a chunk's queries see
+ * the cached cells and their own ubatch's).  q/out are host arrays of n_il device pointers; q is fp32
  * [n_tokens][n_head*head_dim], out fp32 [n_tokens][n_head*head_dim] in
  * ubatch slot order -- or, with only_outputs, [n_outputs][...] holding the
  * flagged slots in slot order.  A slot with no visible cell yields zeros.
@@ -199,15 +212,17 @@ int kvattn_attend(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t
  * ubatch", "Prefill and decode are not the same shape"). */
 int32_t kvattn_n_kv(const kvattn_ctx *ctx);
 
-/* Dense F16 KQ mask of the most recently committed ubatch, built on the GPU
- * from the device cell mirror: 0x0000 visible, 0xFC00 (-inf) hidden,
+/* Dense F16 KQ mask of the most recently committed ubatch ("llama.cpp and
+ * the ubatch", "The mask is doing the work"), built on the GPU from the
+ * device cell mirror: 0x0000 visible, 0xFC00 (-inf) hidden,
  * row-major [n_tokens][n_kv].  d_mask is a device buffer of cap_elems F16;
  * *n_kv receives the row length.  Asynchronous on hip_stream. */
 int kvattn_get_mask(kvattn_ctx *ctx, const kvattn_ubatch *ub, void *d_mask, size_t cap_elems,
                     int32_t *n_kv, void *hip_stream);
 
 /* Visibility lists of the most recently committed ubatch, copied to host
- * (synchronises hip_stream).  Cells are grouped in classes of equal
+ * (synchronises hip_stream): the mask of "llama.cpp and the ubatch", "The
+ * mask is doing the work", kept in sparse form.  Cells are grouped in classes of equal
  * sequence sets; per class: stream, sequence-set bitmask, number of cells,
  * then the cells in ascending index.  Fills up to cap_classes classes and
  * cap_cells cells; *n_classes / *n_cells receive the totals. */
@@ -216,19 +231,24 @@ int kvattn_get_classes(kvattn_ctx *ctx, int32_t *n_classes, int32_t *cls_stream,
                        int32_t *n_cells, int32_t *cells, int32_t cap_cells, void *hip_stream);
 
 /* HOST-ONLY.  Copy of the committed cell table of one stream: pos (-1 =
- * empty) and the sequence-set bitmask of each of the kv_size cells. */
+ * empty) and the sequence-set bitmask of each of the kv_size cells (the
+ * per-cell metadata the mask reads, "llama.cpp and the ubatch", "The mask is
+ * doing the work").  pos and seqmask are host arrays of kv_size entries. */
 int kvattn_get_cells(const kvattn_ctx *ctx, int32_t stream, int32_t *pos, uint64_t *seqmask);
 
 /* HOST-ONLY.  Remove sequence seq_id (every sequence when < 0) from cells
- * whose position lies in [p0, p1) (p0 < 0: from 0; p1 < 0: no end).  A cell
+ * whose position lies in [p0, p1) (the retirement step of "Iteration-Level
+ * Batching", "The loop that replaces the batch") (p0 < 0: from 0; p1 < 0: no end).  A cell
  * left without a sequence becomes free.  The device mirror follows at the
  * next commit. */
 int kvattn_seq_rm(kvattn_ctx *ctx, int32_t seq_id, int32_t p0, int32_t p1);
 
-/* HOST-ONLY.  Largest committed position of seq_id, -1 when none. */
+/* HOST-ONLY.  Largest committed position of seq_id, -1 when none (what a
+ * NULL pos continues from: "Batch、Ubatch 与解码主循环", Part A). */
 int32_t kvattn_seq_pos_max(const kvattn_ctx *ctx, int32_t seq_id);
 
-/* HOST-ONLY.  Work plan of the most recently committed ubatch: number of
+/* HOST-ONLY.  Work plan of the most recently committed ubatch (this
+ * library's own decomposition; the pages give no kernel design): number of
  * visibility classes, vector-ALU work items, matrix-core work items (per
  * KV head), split-K partial rows and reduced slots.  Any pointer may be NULL. */
 int kvattn_plan_stats(const kvattn_ctx *ctx, int32_t only_outputs, int32_t *n_classes,

@@ -9,12 +9,12 @@ reader can check it against the pages by eye.
 
 Sources (cited by page title and section throughout):
 
-* P1 -- "llama.cpp and the ubatch" (joelfernandes.org, 2026-08-14)
-* P2 -- "Batch、Ubatch 与解码主循环" (jonathanding.github.io, llm-learning #4)
-* P3 -- "What does llama.cpp's KV cache actually look like in memory?"
+* "llama.cpp and the ubatch" (joelfernandes.org, 2026-08-14)
+* "Batch、Ubatch 与解码主循环" (jonathanding.github.io, llm-learning #4)
+* "What does llama.cpp's KV cache actually look like in memory?"
   (joelfernandes.org, 2026-10-05)
-* P4 -- "Iteration-Level Batching: Reforming the Batch at Every Token"
-  (mercemay.com)
+* "Iteration-Level Batching: Reforming the Batch at Every Token"
+  (mercemay.com), cited as "Iteration-Level Batching"
 
 Modules:
 

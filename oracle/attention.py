@@ -2,16 +2,16 @@
 
 Test infrastructure only (see ``oracle/__init__.py``).
 
-What is computed (P1 "Where the memory actually sits": a query is compared
+What is computed ("llama.cpp and the ubatch", "Where the memory actually sits": a query is compared
 with the key of every earlier token and the values are mixed by those
-weights; P1 "The mask is doing the work": masked keys become -inf before the
-softmax and contribute nothing; P1 "The output projection": each head's
+weights; "llama.cpp and the ubatch", "The mask is doing the work": masked keys become -inf before the
+softmax and contribute nothing; "llama.cpp and the ubatch", "The output projection": each head's
 output is a weighted sum of value vectors):
 
     O[i, h] = sum_j softmax_j(scale * q[i, h] . K[j, g] + M[i, j]) V[j, g]
 
 with g = h // (n_head / n_head_kv).  Readings (the pages give neither): the
-query heads that share a KV head are contiguous (P4 "The budget that actually
+query heads that share a KV head are contiguous ("Iteration-Level Batching", "The budget that actually
 binds" gives only the ratio), and scale = 1 / sqrt(head_dim).  A row with no
 visible key produces zeros.
 """

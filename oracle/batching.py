@@ -3,16 +3,16 @@
 Test infrastructure only (see ``oracle/__init__.py``).
 
 A batch is a list of token slots; slot i carries a position, a set of
-sequence ids and an output flag (P1 "Three things called batch"; P2 Part A,
+sequence ids and an output flag ("llama.cpp and the ubatch", "Three things called batch"; "Batch、Ubatch 与解码主循环", Part A,
 the llama_batch statement).  A ubatch is what one forward pass processes
-(P1 "Three things called batch"; P2 Part B, the llama_ubatch statement).
+("llama.cpp and the ubatch", "Three things called batch"; "Batch、Ubatch 与解码主循环", Part B, the llama_ubatch statement).
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-DEFAULT_N_BATCH = 2048   # P1 "Back to the VRAM question"; P2 two-level batch parameters
+DEFAULT_N_BATCH = 2048   # "llama.cpp and the ubatch", "Back to the VRAM question"; "Batch、Ubatch 与解码主循环" two-level batch parameters
 DEFAULT_N_UBATCH = 512
 
 
@@ -21,11 +21,11 @@ class SplitError(ValueError):
 
 
 def clamp_params(n_ctx: int, n_batch: int, n_ubatch: int, causal: bool = True):
-    """Context-creation clamps (P1 "Three things called batch").
+    """Context-creation clamps ("llama.cpp and the ubatch", "Three things called batch").
 
     Under causal attention n_batch is limited to the cache capacity n_ctx;
     n_ubatch falls back to n_batch when zero and is then limited to n_batch.
-    A zero n_batch takes the common default of 2048 (P1 "Back to the VRAM
+    A zero n_batch takes the common default of 2048 ("llama.cpp and the ubatch", "Back to the VRAM
     question" -- reading: zero means "use the default").
     """
     if n_batch < 0 or n_ubatch < 0 or n_ctx <= 0:
@@ -40,8 +40,8 @@ def clamp_params(n_ctx: int, n_batch: int, n_ubatch: int, causal: bool = True):
 def fill_batch(n_tokens, pos, seq_id, output, next_pos, n_seq_max, n_stream):
     """Validate a batch and fill the fields the caller left out.
 
-    P2 Part A says pos may be NULL (auto-increment) and that the sampler only
-    needs the last token's output; P2 Part F says llama_decode first validates
+    "Batch、Ubatch 与解码主循环", Part A says pos may be NULL (auto-increment) and that the sampler only
+    needs the last token's output; "Batch、Ubatch 与解码主循环", Part F says llama_decode first validates
     and auto-fills pos, seq_id and logits.  Readings (the pages do not say how):
 
     * ``seq_id is None``  -> every slot belongs to sequence {0};
@@ -91,7 +91,7 @@ def fill_batch(n_tokens, pos, seq_id, output, next_pos, n_seq_max, n_stream):
             out[-1] = 1
     else:
         out = [1 if int(o) else 0 for o in output[:n_tokens]]
-    # the query masks against the FIRST listed id (P1 "The mask is doing the
+    # the query masks against the FIRST listed id ("llama.cpp and the ubatch", "The mask is doing the
     # work"); keep it first, then the rest of the set in ascending order.
     if seq_id is not None:
         sids = [tuple([int(seq_id[i][0])] + [s for s in sids[i] if s != int(seq_id[i][0])])
@@ -101,8 +101,8 @@ def fill_batch(n_tokens, pos, seq_id, output, next_pos, n_seq_max, n_stream):
 
 def split_simple(unused: list, n_ubatch: int):
     """One split_simple step: the next <= n_ubatch unused slots in submission
-    order, ignoring sequence ids (P1 "Part 1: putting different conversations
-    in the same ubatch"; P2 Part C item 1: 1000 tokens -> 512 + 488)."""
+    order, ignoring sequence ids ("llama.cpp and the ubatch", "Part 1: putting different conversations
+    in the same ubatch"; "Batch、Ubatch 与解码主循环", Part C item 1: 1000 tokens -> 512 + 488)."""
     take = [i for i, u in enumerate(unused) if u][:n_ubatch]
     for i in take:
         unused[i] = False
@@ -112,9 +112,11 @@ def split_simple(unused: list, n_ubatch: int):
 def split_equal(unused: list, seq_sets: list, n_ubatch: int):
     """One split_equal(n_ubatch, sequential=true) step.
 
-    P2 Part C item 2: pick non-overlapping sequence sets, then take the same
+    "Batch、Ubatch 与解码主循环", Part C item 2: pick non-overlapping sequence sets, then take the same
     number of tokens from each set until the ubatch nears n_ubatch or a set
-    runs out; P1 Part 1: "equal-length chunks with ordered sequence ids".
+    runs out; "llama.cpp and the ubatch", "Part 1: putting different
+    conversations in the same ubatch", describes it as cutting chunks of one
+    length per sequence with the sequence ids kept in order.
     Reading of the steps the pages leave open:
 
     1. scan unused slots in submission order; a slot whose set equals an
@@ -155,7 +157,7 @@ def split_equal(unused: list, seq_sets: list, n_ubatch: int):
 
 
 def split_seq(unused: list, seq_sets: list, n_ubatch: int):
-    """One split_seq(n_ubatch) step (P2 Part C item 3: every ubatch holds the
+    """One split_seq(n_ubatch) step ("Batch、Ubatch 与解码主循环", Part C item 3: every ubatch holds the
     tokens of one sequence set, sequences are never mixed; meant for
     independent decoding).  Reading of what the page leaves open: the set is
     that of the first unused slot in submission order, and the ubatch takes
@@ -175,7 +177,7 @@ SPLIT_MODES = ("auto", "simple", "equal", "seq")
 
 
 def split_batch(seq_sets: list, n_ubatch: int, n_stream: int, mode: str = "auto"):
-    """The init_batch split loop (P2 Part C, strategy choice): one stream ->
+    """The init_batch split loop ("Batch、Ubatch 与解码主循环", Part C, strategy choice): one stream ->
     split_simple, several streams -> split_equal(n_ubatch, true) ("auto");
     a caller may instead name one of the three strategies.  Repeat until a
     split returns no slot.  Returns a list of (slots, n_seq_tokens, n_seqs)
@@ -201,7 +203,7 @@ def split_batch(seq_sets: list, n_ubatch: int, n_stream: int, mode: str = "auto"
 
 
 def output_ids(output: list, n_batch: int) -> np.ndarray:
-    """Batch row -> output row map, n_batch entries (P1 "Where the memory
+    """Batch row -> output row map, n_batch entries ("llama.cpp and the ubatch", "Where the memory
     actually sits": output_reserve sizes output_ids by n_batch).  Reading:
     flagged slots get their rank among flagged slots in batch order, the rest
     (and the unused tail) get -1."""

@@ -2,12 +2,12 @@
 
 Test infrastructure only (see ``oracle/__init__.py``).
 
-P2 Part F (the llama_decode main loop): validate and auto-fill the batch,
+"Batch、Ubatch 与解码主循环", Part F (the llama_decode main loop): validate and auto-fill the batch,
 split it into ubatches and reserve cache cells for all of them, then process
 the ubatches in order -- each one writes its K/V rows into its cells and runs
 attention over the cells it may see.  Later ubatches of the same batch see
-the cells of earlier ones (P2 Part D: a later ubatch's attention reads what an
-earlier ubatch wrote; P1 "Chunked prefill is the same mechanism").
+the cells of earlier ones ("Batch、Ubatch 与解码主循环", Part D: a later ubatch's attention reads what an
+earlier ubatch wrote; "llama.cpp and the ubatch", "Chunked prefill is the same mechanism").
 """
 
 from __future__ import annotations
@@ -61,7 +61,7 @@ class OracleEngine:
         self.V = {l: np.zeros((n_stream, kv_size, self.E), np.float16) for l in self.layers}
         self._pending = []
 
-    # -- batch intake, split and placement (P2 Part C and Part F) ---------
+    # -- batch intake, split and placement ("Batch、Ubatch 与解码主循环", Part C and Part F) ---------
     def split(self, n_tokens, pos=None, seq_id=None, output=None):
         """Returns (status, ubatches, output_ids); status 1 = no room (nothing
         reserved).  Invalid input raises SplitError.  Cells reserved by a
@@ -72,7 +72,7 @@ class OracleEngine:
                 self.cells.release([c[1] for c in ub.copies], [c[2] for c in ub.copies])
         self._pending = []
         if n_tokens > self.n_batch:
-            raise SplitError("n_tokens > n_batch")       # P1: GGML_ASSERT on n_batch
+            raise SplitError("n_tokens > n_batch")       # "llama.cpp and the ubatch": an assertion on n_batch
         next_pos = {}
         if pos is None:
             for s in range(self.n_seq_max):
@@ -81,7 +81,7 @@ class OracleEngine:
                                   self.n_seq_max, self.n_stream)
         parts = split_batch([set(x) for x in sids], self.n_ubatch, self.n_stream, self.split_mode)
         # a slot's cell is in the stream of its first id (seq % n_stream);
-        # P3 "Unified versus non-unified": with several streams a common
+        # "What does llama.cpp's KV cache actually look like in memory?", "Unified versus non-unified": with several streams a common
         # prefix needs separate copies -- a slot whose ids span streams also
         # gets a cell in each other stream it touches (ascending), holding
         # the ids that live there.  Cells are taken per stream in slot order.

@@ -2,12 +2,12 @@
 
 Test infrastructure only (see ``oracle/__init__.py``).
 
-Layout (P3 "28 layers, 56 tensors", "The tensor's three dimensions"): every
+Layout ("What does llama.cpp's KV cache actually look like in memory?", "28 layers, 56 tensors", "The tensor's three dimensions"): every
 layer owns one K and one V tensor of shape [n_stream][kv_size][n_head_kv *
 head_dim] in F16; a cell is a row index shared by all layers; stream s is the
-slab at offset s * kv_size * row_bytes (P3 "Unified versus non-unified").
+slab at offset s * kv_size * row_bytes ("What does llama.cpp's KV cache actually look like in memory?", "Unified versus non-unified").
 Each cell records whether it is empty, its position and the set of sequences
-that may read it (P1 "The mask is doing the work").
+that may read it ("llama.cpp and the ubatch", "The mask is doing the work").
 """
 
 from __future__ import annotations
@@ -16,15 +16,15 @@ import numpy as np
 
 from .batching import SplitError
 
-F16_BYTES = 2                 # P3 "One row, one token's keys": two bytes per number
-N_PAD_FLOOR = 256             # P1 "Prefill and decode are not the same shape"
+F16_BYTES = 2                 # "What does llama.cpp's KV cache actually look like in memory?", "One row, one token's keys": two bytes per number
+N_PAD_FLOOR = 256             # "llama.cpp and the ubatch", "Prefill and decode are not the same shape"
 MASK_VISIBLE = np.float16(0.0)
 MASK_HIDDEN = np.float16(-np.inf)
 
 
 def f16_round(x) -> np.ndarray:
     """fp32 -> IEEE binary16 with round-to-nearest-even (numpy's cast).
-    The pages store K/V as 2-byte F16 (P3 "One row, one token's keys");
+    The pages store K/V as 2-byte F16 ("What does llama.cpp's KV cache actually look like in memory?", "One row, one token's keys");
     the rounding mode is a reading."""
     with np.errstate(over="ignore"):
         return np.asarray(x, dtype=np.float32).astype(np.float16)
@@ -32,20 +32,20 @@ def f16_round(x) -> np.ndarray:
 
 def row_bytes(n_head_kv: int, head_dim: int) -> int:
     """Bytes of one cell's K (or V) row in one layer: n_head_kv * head_dim F16
-    numbers (P3 "One row, one token's keys": 8 x 128 -> 2048 bytes)."""
+    numbers ("What does llama.cpp's KV cache actually look like in memory?", "One row, one token's keys": 8 x 128 -> 2048 bytes)."""
     return n_head_kv * head_dim * F16_BYTES
 
 
 def cache_bytes(n_layer, n_head_kv, head_dim, kv_size, n_stream=1) -> int:
     """Total K+V allocation: every cell of every stream, in K and V, in every
-    layer (P3 "One row, one token's keys" and "The measured allocation":
+    layer ("What does llama.cpp's KV cache actually look like in memory?", "One row, one token's keys" and "The measured allocation":
     4096 cells of Qwen3-0.6B -> 448 MiB)."""
     return 2 * n_layer * n_stream * kv_size * row_bytes(n_head_kv, head_dim)
 
 
 def k_elem_offset(cell, head, elem, n_head_kv, head_dim, stream=0, kv_size=0) -> int:
     """Byte offset of one F16 element inside a layer's K tensor, from the
-    strides nb = (2, row_bytes, kv_size * row_bytes) (P3 "The tensor's three
+    strides nb = (2, row_bytes, kv_size * row_bytes) ("What does llama.cpp's KV cache actually look like in memory?", "The tensor's three
     dimensions": cell 37, head 3, element 10 -> 76,564 bytes)."""
     nb1 = row_bytes(n_head_kv, head_dim)
     nb2 = kv_size * nb1
@@ -58,9 +58,10 @@ class CellTable:
     ``pos[s, j]``        position held by cell j of stream s, -1 when empty;
     ``member[s, j, q]``  True when sequence q may read that cell.
 
-    Placement is not described on the pages beyond "prepare reserves a slot
-    for every ubatch" (P2 Part C, strategy choice) and "one cell per token
-    even when it belongs to several sequences" (P2 Part E).  Reading: each
+    Placement is not described on the pages beyond two facts: every ubatch
+    of a batch gets its cells reserved before any of them runs ("Batch、Ubatch 与解码主循环", Part C,
+    strategy choice), and a token takes one cell however many sequences it
+    belongs to ("Batch、Ubatch 与解码主循环", Part E).  Reading: each
     stream hands out its free cells lowest rank first, where rank is the
     cell's index in ``order[s]`` (ascending cell index when no order is
     given); a freed cell returns with its original rank.
@@ -89,8 +90,8 @@ class CellTable:
         return free[np.argsort(self.rank[s, free], kind="stable")]
 
     def reserve(self, streams: list):
-        """All-or-nothing placement for a whole batch (P2 Part C: prepare
-        reserves slots for every ubatch before any is processed; P2 Part F:
+        """All-or-nothing placement for a whole batch ("Batch、Ubatch 与解码主循环", Part C: prepare
+        reserves slots for every ubatch before any is processed; "Batch、Ubatch 与解码主循环", Part F:
         a full cache makes llama_decode return 1).  ``streams`` lists the
         stream of every slot in ubatch order.  Returns the cell of each slot,
         or None (nothing reserved) when a stream runs out."""
@@ -117,7 +118,7 @@ class CellTable:
 
     def commit(self, streams, cells, pos, seq_sets):
         """A ubatch's cells become occupied: position and sequence set.  Once
-        written an entry is final (P1 "Where the memory actually sits")."""
+        written an entry is final ("llama.cpp and the ubatch", "Where the memory actually sits")."""
         for s, j, p, ss in zip(streams, cells, pos, seq_sets):
             self.reserved[s, j] = False
             self.pos[s, j] = int(p)
@@ -148,7 +149,7 @@ class CellTable:
         return int(occ.max()) + 1 if occ.size else 0
 
     def n_kv(self) -> int:
-        """get_n_kv (P1 "Prefill and decode are not the same shape"): per
+        """get_n_kv ("llama.cpp and the ubatch", "Prefill and decode are not the same shape"): per
         stream, the occupied extent padded up to a multiple of 256 (and never
         below 256), capped at the stream size; the reported value is the
         largest over streams (reading of the elided running ``result``)."""
@@ -161,7 +162,7 @@ class CellTable:
 
     # -- the KQ mask -----------------------------------------------------
     def visible_row(self, s, q_pos, q_seq0, nkv, causal=True, swa=0) -> np.ndarray:
-        """P1 "The mask is doing the work": skip empty cells, cells of other
+        """"llama.cpp and the ubatch", "The mask is doing the work": skip empty cells, cells of other
         sequences, under causal attention cells from the future, and for
         models with sliding-window attention cells outside the window.  The
         query's sequence is its FIRST listed id.  Cells j < nkv of stream s.

@@ -1,8 +1,8 @@
-"""The iteration-level (continuous) batching loop, restated from P4.
+"""The iteration-level (continuous) batching loop, restated from "Iteration-Level Batching".
 
 Test infrastructure only (see ``oracle/__init__.py``).
 
-P4 "The loop that replaces the batch": the scheduler keeps the sequences that
+"Iteration-Level Batching", "The loop that replaces the batch": the scheduler keeps the sequences that
 are generating (``running``) and the ones waiting to enter (``waiting``) and
 rebuilds the batch before every forward pass.  One iteration
 
@@ -15,18 +15,18 @@ rebuilds the batch before every forward pass.  One iteration
 4. runs the model; a sampler picks one token per sequence and each running
    sequence advances (``advance`` here).
 
-P4 "The budget that actually binds": the token budget counts positions per
+"Iteration-Level Batching", "The budget that actually binds": the token budget counts positions per
 iteration, and a prompt longer than what is left of it must wait or be split
-(chunked prefill).  Cache budget: P4's sketch reserves the worst case
+(chunked prefill).  Cache budget: the sketch of "Iteration-Level Batching" reserves the worst case
 ``ceil((prompt_len + max_new) / block_size)`` blocks at admission (policy
 ``"reserve"``); with a paged cache admission only needs the cells the new
 sequence's prompt will occupy and a running sequence grows one cell per step
-(policy ``"paged"``, the policy P4 says paged allocation makes possible).
-P4 "Where it breaks": when the cache runs out the loop takes memory back from
+(policy ``"paged"``, the policy "Iteration-Level Batching" says paged allocation makes possible).
+"Iteration-Level Batching", "Where it breaks": when the cache runs out the loop takes memory back from
 a running sequence; this oracle discards the progress of the most recently
 admitted sequence of the exhausted stream and recomputes it later.
 
-Readings where P4 leaves a step open (each is a choice, stated once):
+Readings where "Iteration-Level Batching" leaves a step open (each is a choice, stated once):
 
 * A sequence is finished once it has sampled ``n_generate`` tokens; its last
   sampled token is never fed back, so a finished sequence has cached
@@ -52,8 +52,8 @@ Readings where P4 leaves a step open (each is a choice, stated once):
   prompt plus sampled tokens.  A newcomer is admitted when its pending
   positions fit in the free cells left after that need.
 * ``"reserve"``: ``kv_size // block_size`` blocks per stream; never preempts.
-* Preemption by swapping (``preempt="swap"``, the other option P4 names):
-  the victim's cells are saved first (the sequence-state blob of P3 "Opening
+* Preemption by swapping (``preempt="swap"``, the other option "Iteration-Level Batching" names):
+  the victim's cells are saved first (the sequence-state blob of "What does llama.cpp's KV cache actually look like in memory?", "Opening
   the .bin dump", ``blob_bytes``) into a swap arena of ``swap_bytes``, at the
   lowest offset where it fits (first fit, extents rounded up to 256 bytes);
   the victim keeps its cached positions and, when re-admitted, its cells
@@ -118,7 +118,7 @@ def _ceil_div(a, b):
 
 
 class OracleScheduler:
-    """P4's loop over one cache of ``n_stream`` streams of ``kv_size`` cells.
+    """The loop of "Iteration-Level Batching" over one cache of ``n_stream`` streams of ``kv_size`` cells.
 
     ``release(seq_id)`` is called whenever a sequence's cells are released
     (retirement or preemption); pass the oracle engine's ``seq_rm`` so that

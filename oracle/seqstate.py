@@ -1,8 +1,9 @@
-"""Save / restore of one sequence's cached K/V, in P3's record layout.
+"""Save / restore of one sequence's cached K/V, in the record layout of
+"What does llama.cpp's KV cache actually look like in memory?".
 
 Test infrastructure only (see ``oracle/__init__.py``).
 
-P3 "Opening the .bin dump" saves one sequence's occupied cells across all
+"What does llama.cpp's KV cache actually look like in memory?", "Opening the .bin dump" saves one sequence's occupied cells across all
 layers and describes the file: metadata first, then one record per layer
 for K (layers 0..L-1), then one per layer for V; each record is a small
 header followed by the sequence's rows.  Its numbers fix the sizes: seven
@@ -22,7 +23,7 @@ for the library): all fields little-endian,
   positions, ascending;
 * record header = u32 type (1 = F16) + u64 row bytes (4 + 8 = 12);
 * rows in the order of the positions, each the cell's full row of that
-  layer's tensor (all KV heads, P3 "One row, one token's keys").
+  layer's tensor (all KV heads, "What does llama.cpp's KV cache actually look like in memory?", "One row, one token's keys").
 
 The sequence's cells are every committed cell whose sequence set holds it
 (shared prefix cells included), ordered by position (then cell index).

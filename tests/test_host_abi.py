@@ -179,6 +179,23 @@ def test_autofill_and_defaults_match_oracle():
     assert K.kvattn_seq_pos_max(ctx.ctx, 2) == -1
 
 
+@pytest.mark.parametrize("kv_size,n_stream,n_batch,causal", [(64, 1, 0, True), (64, 2, 100, True),
+                                                             (4096, 1, 3000, True), (64, 1, 100, False)])
+def test_output_ids_sized_by_library_clamp(kv_size, n_stream, n_batch, causal):
+    """The binding sizes output_ids from kvattn_get_params (the library's
+    clamp, "llama.cpp and the ubatch", "Three things called batch"), not from
+    arithmetic of its own; the oracle's clamp must agree with it."""
+    from oracle.batching import clamp_params
+    ctx = K.Context(1, 2, 1, 16, kv_size=kv_size, n_stream=n_stream, n_seq_max=2, n_batch=n_batch,
+                    n_ubatch=0, causal=causal)
+    nb = K.kvattn_get_params(ctx.ctx).n_batch
+    assert nb == clamp_params(kv_size * n_stream, n_batch, 0, causal)[0]
+    assert ctx.n_batch() == nb
+    st, ubs, ids = ctx.split(3, [0, 1, 2], [[0], [1], [0]], [1, 0, 1], with_ids=True)
+    assert st == 0 and ids.shape == (nb,)
+    assert ids[:3].tolist() == [0, -1, 1] and (ids[3:] == -1).all()
+
+
 def test_seq_rm_and_reuse_match_oracle():
     wl = W.cb_decode(n_seq=6, lengths=(4, 9, 15), n_layer=1, kv_size=64)
     ctx, eng = host_ctx(wl), oracle_for(wl)

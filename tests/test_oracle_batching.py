@@ -156,7 +156,7 @@ def test_fill_batch_autofill_and_errors():
 
 
 def test_separate_copies_of_a_prefix_across_streams():
-    """P3 "Unified versus non-unified": with one stream per sequence a common
+    """"What does llama.cpp's KV cache actually look like in memory?", "Unified versus non-unified": with one stream per sequence a common
     prefix needs separate copies.  A 6-slot prefix shared by sequences 0..3
     takes 6 cells of the unified cache and 6 cells in each of 4 streams, each
     copy holding only the id of its stream; every sequence's decode query
@@ -204,7 +204,7 @@ def test_engine_rejects_batch_larger_than_n_batch():
 
 
 def test_split_seq_one_set_per_ubatch():
-    """split_seq (P2 Part C item 3): every ubatch holds the tokens of one
+    """split_seq ("Batch、Ubatch 与解码主循环", Part C item 3): every ubatch holds the tokens of one
     sequence set; different sequences are never mixed.  Interleaved decode
     slots of three sequences, a prefix-shared slot {0, 1} and a cap of 2."""
     sets = [{0}, {1}, {0}, {1}, {2}, {0}, {0, 1}, {0}]

@@ -1,6 +1,6 @@
 """Pins for the oracle's sequence-state save / restore (oracle/seqstate.py).
 
-* P3 "Opening the .bin dump" (tests/golden/page_numbers.json, state_dump):
+* "What does llama.cpp's KV cache actually look like in memory?", "Opening the .bin dump" (tests/golden/page_numbers.json, state_dump):
   seven cells of the Qwen3-0.6B shape serialize to 803,596 bytes = 802,816
   payload + 780 metadata; the first K record starts at byte 108, its 12-byte
   header puts the first K value at byte 120, where the page's eight bytes

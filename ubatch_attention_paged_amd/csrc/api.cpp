@@ -76,6 +76,7 @@ struct kvattn_ctx {
   size_t ws_bytes = 0;
   WsLayout wl{};
   bool dev_ready = false;
+  bool broken = false;        // a commit could not reach the device mirror
   void* stage[kStages] = {};
   size_t stage_cap[kStages] = {};
   char* stage_dev[kStages] = {};     // device view of each pinned staging buffer
@@ -124,6 +125,7 @@ namespace {
 
 int ensure_device(kvattn_ctx* c) {
   if (!c->has_dev) return c->fail(KVATTN_ENODEV, "context was created without device buffers");
+  if (c->broken) return c->fail(KVATTN_ESTATE, "the device cell mirror is out of date (an earlier commit failed)");
   HIP_TRY(c, hipSetDevice(c->device));
   if (c->dev_ready) return KVATTN_OK;
   for (int i = 0; i < kStages; ++i) HIP_TRY(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
@@ -177,7 +179,6 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
     c->plan[0] = Plan();
     c->plan[1] = Plan();
   }
-  const Plan& P0 = c->plan[0];
   // destination rows of the store: the slots' cells, then the separate
   // copies; after them the source slot of each copy
   const size_t n_slot = u.cells.size(), n_copy = u.copy_cell.size();
@@ -189,30 +190,48 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
     dst[n_slot + n_copy + i] = u.copy_src[i];
   }
 
-  // arena layout
-  ArenaLayout& A = c->al;
-  size_t o = 0;
-  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
-  A.classes = take(P0.classes.size() * sizeof(ClassInfo));
-  A.lookup = take(P0.lookup.size() * sizeof(LookupEntry));
-  A.lookup_off = take(P0.lookup_off.size() * 4);
-  A.dst_rows = take(dst.size() * 4);
-  for (int v = 0; v < 2; ++v) {
-    const Plan& P = c->plan[v];
-    A.v[v].slots = take(P.slots.size() * sizeof(SlotInfo));
-    A.v[v].qlist = take(P.qlist.size() * 4);
-    A.v[v].items_valu = take(P.items_valu.size() * sizeof(WorkItem));
-    A.v[v].items_mfma = take(P.items_mfma.size() * sizeof(WorkItem));
-    A.v[v].red_slot = take(P.red_slot.size() * 4);
-    A.v[v].red_off = take(P.red_off.size() * 4);
-    A.v[v].red_rows = take(P.red_rows.size() * 4);
+  // arena layout.  A plan too large for the arena is dropped like one
+  // build_plan refused: the mirror update and the stores still run, attend
+  // reports the missing plan.  The arena is sized (16 MiB + 48 B per cell)
+  // so that the store rows and mirror updates alone always fit; if they did
+  // not, nothing is launched and the context's previous layout stays.
+  auto layout = [&](ArenaLayout& A) {
+    size_t o = 0;
+    auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
+    const Plan& P0 = c->plan[0];
+    A.classes = take(P0.classes.size() * sizeof(ClassInfo));
+    A.lookup = take(P0.lookup.size() * sizeof(LookupEntry));
+    A.lookup_off = take(P0.lookup_off.size() * 4);
+    A.dst_rows = take(dst.size() * 4);
+    for (int v = 0; v < 2; ++v) {
+      const Plan& P = c->plan[v];
+      A.v[v].slots = take(P.slots.size() * sizeof(SlotInfo));
+      A.v[v].qlist = take(P.qlist.size() * 4);
+      A.v[v].items_valu = take(P.items_valu.size() * sizeof(WorkItem));
+      A.v[v].items_mfma = take(P.items_mfma.size() * sizeof(WorkItem));
+      A.v[v].red_slot = take(P.red_slot.size() * 4);
+      A.v[v].red_off = take(P.red_off.size() * 4);
+      A.v[v].red_rows = take(P.red_rows.size() * 4);
+    }
+    A.updates = take(c->upd.size() * sizeof(CellUpdate));
+    A.total = o;
+  };
+  ArenaLayout A{};
+  layout(A);
+  if (A.total > c->wl.arena_bytes && c->plan_ok) {
+    c->plan_ok = false;
+    c->plan[0] = Plan();
+    c->plan[1] = Plan();
+    rc0 = KVATTN_ENOMEM;
+    e0 = "ubatch plan exceeds the workspace plan arena";
+    layout(A);
   }
-  A.updates = take(c->upd.size() * sizeof(CellUpdate));
-  A.total = o;
   if (A.total > c->wl.arena_bytes) {
     c->plan_ok = false;
-    return c->fail(KVATTN_ENOMEM, "ubatch plan exceeds the workspace plan arena");
+    return c->fail(KVATTN_ENOMEM, "store rows and cell updates exceed the workspace plan arena");
   }
+  c->al = A;
+  const Plan& P0 = c->plan[0];
   // stage
   int st = 0;
   if (int rc = acquire_stage(c, A.total, &st)) return rc;
@@ -432,7 +451,14 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
     c->upd.clear();
     if ((rc = c->core.commit(k, &c->upd, c->err))) return rc;
     rc = upload_commit(c, k, s, n_il > 0);
-    if (rc && rc != KVATTN_ENOMEM) return rc;
+    // ENOMEM with the commit still pending: only the attention plan is
+    // missing (attend reports it).  Without a pending commit nothing is
+    // launched; the host table is committed but the device mirror cannot
+    // follow, so every later device call on this context is refused.
+    if (rc && !c->commit_pending) {
+      c->broken = true;
+      return rc;
+    }
   } else if (c->core.latest_committed() != k || !plan_current(c, k)) {
     return c->fail(KVATTN_ESTATE, "only the most recently committed ubatch can be stored again");
   }

@@ -233,9 +233,11 @@ class SeqIds:
         return len(self.counts)
 
 
-def kvattn_split(ctx, n_tokens, pos=None, seq_ids=None, output=None, cap=None, n_batch_ids=0):
+def kvattn_split(ctx, n_tokens, pos=None, seq_ids=None, output=None, cap=None, with_ids=False):
     """Returns (status, [Ubatch], output_ids or None).  status is 0 or 1
-    (no room); invalid input raises KvattnError."""
+    (no room); invalid input raises KvattnError.  With ``with_ids`` the
+    output_ids buffer holds the library's clamped n_batch entries
+    (kvattn_get_params), as kvattn_split fills."""
     lib = load()
     keep = []
     b = kvattn_batch()
@@ -255,7 +257,7 @@ def kvattn_split(ctx, n_tokens, pos=None, seq_ids=None, output=None, cap=None, n
         a, p = _arr(output, np.int8)
         keep.append(a)
         b.output = p
-    return _split(lib, ctx, b, keep, cap, n_batch_ids)
+    return _split(lib, ctx, b, keep, cap, kvattn_get_params(ctx).n_batch if with_ids else 0)
 
 
 def kvattn_split_batch(ctx, b: kvattn_batch, cap=None):
@@ -468,16 +470,14 @@ class Context:
         return torch.cuda.current_stream(torch.device(self.device)).cuda_stream
 
     def split(self, n_tokens, pos=None, seq_ids=None, output=None, with_ids=False):
-        from_ids = self.n_batch_clamped() if with_ids else 0
-        return kvattn_split(self.ctx, n_tokens, pos, seq_ids, output, n_batch_ids=from_ids)
+        return kvattn_split(self.ctx, n_tokens, pos, seq_ids, output, with_ids=with_ids)
 
     def split_batch(self, b: kvattn_batch):
         return kvattn_split_batch(self.ctx, b)
 
-    def n_batch_clamped(self):
-        n_ctx = self.kv_size * self.n_stream
-        nb = self.params.n_batch if self.params.n_batch > 0 else 2048
-        return min(n_ctx, nb) if self.params.causal else nb
+    def n_batch(self):
+        """The context's n_batch as the library clamped it (sizes output_ids)."""
+        return kvattn_get_params(self.ctx).n_batch
 
     def store(self, ub, il0, k_list, v_list, stream=None):
         kvattn_store(self.ctx, ub, il0, [t.data_ptr() for t in k_list], [t.data_ptr() for t in v_list],
