@@ -206,6 +206,26 @@ int kvattn_store(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t 
 int kvattn_attend(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t n_il,
                   const void *const *q, void *const *out, int32_t only_outputs, void *hip_stream);
 
+/* Size of the static device array kvattn_attend_noalloc keeps its split-K
+ * partials in (one per GPU, held until the process ends). */
+#define KVATTN_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments and results as kvattn_attend, but the split-K partial
+ * results live in a static device array of the library
+ * (KVATTN_STATIC_SCRATCH_BYTES per GPU) instead of the context's workspace,
+ * and the call allocates nothing (no hipMalloc / hipFree, no allocating
+ * library routine).  The array is located at the context's device set-up
+ * (its first store).  Limit: one layer's partial rows must fit the array --
+ * 16 MiB / ((n_head * head_dim + 2 * n_head) * 4 B), 2016 rows for 16 heads
+ * of 128 -- else KVATTN_ENOMEM and nothing is launched; layer ranges are cut
+ * into as many launches as the array needs.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (two streams, two
+ * threads) race and must be serialised by the caller. */
+int kvattn_attend_noalloc(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0, int32_t n_il,
+                          const void *const *q, void *const *out, int32_t only_outputs, void *hip_stream);
+
 /* ---- diagnostics (tests and benchmarks) ---------------------------------- */
 
 /* HOST-ONLY.  n_kv reported for the current state ("llama.cpp and the

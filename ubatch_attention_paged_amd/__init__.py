@@ -10,7 +10,7 @@ from .kvattn import (  # noqa: F401
     KVATTN_OK, KVATTN_NO_SLOT, KVATTN_EINVAL, KVATTN_ESTATE, KVATTN_ENOMEM, KVATTN_EHIP, KVATTN_ENODEV,
     KvattnError, Context, Ubatch, SeqIds, kvattn_params, kvattn_batch, kvattn_ubatch, load, LIB_PATH,
     kvattn_workspace_bytes, kvattn_cache_bytes, kvattn_create, kvattn_destroy, kvattn_split,
-    kvattn_store, kvattn_attend, kvattn_n_kv, kvattn_get_mask, kvattn_get_classes, kvattn_get_cells,
+    kvattn_store, kvattn_attend, kvattn_attend_noalloc, kvattn_n_kv, kvattn_get_mask, kvattn_get_classes, kvattn_get_cells,
     kvattn_seq_rm, kvattn_seq_pos_max, kvattn_plan_stats, kvattn_last_error, kvattn_get_params,
     kvattn_split_batch, Scheduler, kvattn_sched_params, kvattn_sched_iter, kvattn_sched_create,
     kvattn_sched_destroy, kvattn_sched_submit, kvattn_sched_step, kvattn_sched_advance,

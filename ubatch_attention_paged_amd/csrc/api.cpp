@@ -129,6 +129,9 @@ int ensure_device(kvattn_ctx* c) {
   HIP_TRY(c, hipSetDevice(c->device));
   if (c->dev_ready) return KVATTN_OK;
   for (int i = 0; i < kStages; ++i) HIP_TRY(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
+  // the allocation-free entry point's static array, located once per device
+  if (int rc = static_scratch_init(c->device))
+    return c->fail(rc, "hipGetSymbolAddress of the static scratch array failed");
   // empty device mirror: every cell free
   const size_t sc = static_cast<size_t>(c->core.geo().n_stream) * c->core.geo().kv_size;
   HIP_TRY(c, hipMemset(c->ws + c->wl.cpos, 0xFF, sc * 4));
@@ -500,6 +503,15 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
 int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_il, const void* const* q,
                   void* const* out, int32_t only_outputs, void* hip_stream) {
   if (!c) return KVATTN_EINVAL;
+  return kvattn::attend_with_partials(c, ub, il0, n_il, q, out, only_outputs, hip_stream, nullptr, nullptr, 0);
+}
+
+}  // extern "C"
+
+int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_il,
+                                 const void* const* q, void* const* out, int32_t only_outputs, void* hip_stream,
+                                 float* part_acc, float* part_ml, int64_t part_rows) {
+  if (!c) return KVATTN_EINVAL;
   int k, rc;
   if ((rc = check_ubatch(c, ub, &k)) || (rc = check_layers(c, il0, n_il))) return rc;
   if (n_il > 0 && (!q || !out)) return c->fail(KVATTN_EINVAL, "q / out is NULL");
@@ -523,8 +535,18 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   a.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);
   a.tile_min = c->dptr<int32_t>(c->wl.tile_min);
   a.tile_max = c->dptr<int32_t>(c->wl.tile_max);
-  a.part_acc = c->dptr<float>(c->wl.part_acc);
-  a.part_ml = c->dptr<float>(c->wl.part_ml);
+  // split-K partials: the workspace's region, or the caller's (the
+  // allocation-free entry point), which must hold one launch's rows
+  if (!part_acc) {
+    part_acc = c->dptr<float>(c->wl.part_acc);
+    part_ml = c->dptr<float>(c->wl.part_ml);
+    part_rows = kPartialRowsCap;
+  }
+  if (P.n_partial_rows > part_rows)
+    return c->fail(KVATTN_ENOMEM, "split-K partial rows of one layer (" + std::to_string(P.n_partial_rows) +
+                                      ") exceed the partial buffer (" + std::to_string(part_rows) + " rows)");
+  a.part_acc = part_acc;
+  a.part_ml = part_ml;
   a.red_slot = reinterpret_cast<const int32_t*>(arena + VL.red_slot);
   a.red_off = reinterpret_cast<const int32_t*>(arena + VL.red_off);
   a.red_rows = reinterpret_cast<const int32_t*>(arena + VL.red_rows);
@@ -537,7 +559,7 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   a.scale_log2e = g.kq_scale * 1.4426950408889634f;
   a.layer_bytes = static_cast<uint32_t>(static_cast<size_t>(g.n_stream) * g.kv_size * g.E() * 2);
   const int64_t per = std::max<int64_t>(1, P.n_partial_rows);
-  const int32_t chunk = static_cast<int32_t>(std::min<int64_t>(kMaxLayersPerLaunch, kPartialRowsCap / per));
+  const int32_t chunk = static_cast<int32_t>(std::min<int64_t>(kMaxLayersPerLaunch, part_rows / per));
   for (int32_t l0 = 0; l0 < n_il; l0 += chunk) {
     const int n = std::min<int32_t>(chunk, n_il - l0);
     for (int i = 0; i < n; ++i) {
@@ -559,6 +581,8 @@ int kvattn_attend(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n
   }
   return KVATTN_OK;
 }
+
+extern "C" {
 
 int32_t kvattn_n_kv(const kvattn_ctx* c) { return c ? c->core.n_kv() : 0; }
 

@@ -101,6 +101,8 @@ SIGNATURES = {
                                     ctypes.c_int32, _vpp, _vpp, ctypes.c_void_p]),
     "kvattn_attend": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_int32,
                                      ctypes.c_int32, _vpp, _vpp, ctypes.c_int32, ctypes.c_void_p]),
+    "kvattn_attend_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_int32,
+                                             ctypes.c_int32, _vpp, _vpp, ctypes.c_int32, ctypes.c_void_p]),
     "kvattn_n_kv": (ctypes.c_int32, [ctypes.c_void_p]),
     "kvattn_get_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_void_p,
                                        ctypes.c_size_t, _i32p, ctypes.c_void_p]),
@@ -302,6 +304,15 @@ def kvattn_attend(ctx, ub: Ubatch, il0, q_ptrs: Sequence[int], out_ptrs: Sequenc
         raise KvattnError(rc, kvattn_last_error(ctx))
 
 
+def kvattn_attend_noalloc(ctx, ub: Ubatch, il0, q_ptrs: Sequence[int], out_ptrs: Sequence[int], only_outputs=0,
+                          stream=0):
+    rc = load().kvattn_attend_noalloc(ctx, ctypes.byref(ub.raw), il0, len(q_ptrs),
+                                      ctypes.cast(_ptrs(q_ptrs), _vpp), ctypes.cast(_ptrs(out_ptrs), _vpp),
+                                      int(only_outputs), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+
+
 def kvattn_n_kv(ctx) -> int:
     return load().kvattn_n_kv(ctx)
 
@@ -486,6 +497,10 @@ class Context:
     def attend(self, ub, il0, q_list, out_list, only_outputs=False, stream=None):
         kvattn_attend(self.ctx, ub, il0, [t.data_ptr() for t in q_list], [t.data_ptr() for t in out_list],
                       only_outputs, self._stream(stream))
+
+    def attend_noalloc(self, ub, il0, q_list, out_list, only_outputs=False, stream=None):
+        kvattn_attend_noalloc(self.ctx, ub, il0, [t.data_ptr() for t in q_list], [t.data_ptr() for t in out_list],
+                              only_outputs, self._stream(stream))
 
     def mask(self, ub, stream=None):
         import torch
