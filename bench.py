@@ -45,6 +45,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+
+
 def gen_tensors(wl, b, layers, with_q, dev):
     import torch
     from synthetic import workloads as W
@@ -245,12 +247,15 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
     row = 2 * wl.n_head_kv * wl.head_dim * 2                       # K + V bytes per cell per layer
     kv_bytes = cells * row * wl.n_layer
     qo_bytes = 2 * bt.n_tokens * HD * 4 * wl.n_layer
-    per_launch = (kv_bytes + qo_bytes) / (n_launch / steps)
-    gbs = per_launch / (avg_ms * 1e-3) / 1e9
+    launches = n_launch / steps
+    # the decode metric counts the unique K/V bytes a step must read; the
+    # fp32 query and output rows are reported beside it, not in it
+    gbs = kv_bytes / launches / (avg_ms * 1e-3) / 1e9
     res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens_per_step=bt.n_tokens,
                tokens_per_s=bt.n_tokens * steps / wall, unique_cells=float(cells),
-               kv_bytes_step=kv_bytes, attend_avg_ms=avg_ms, attend_launches_per_step=n_launch / steps,
-               kv_read_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS, plan=ctx.plan_stats())
+               kv_bytes_step=kv_bytes, qo_bytes_step=qo_bytes, attend_avg_ms=avg_ms,
+               attend_launches_per_step=launches, kv_read_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
+               kv_qo_gbs=(kv_bytes + qo_bytes) / launches / (avg_ms * 1e-3) / 1e9, plan=ctx.plan_stats())
     ctx.close()
     return res
 
@@ -324,13 +329,12 @@ def bench_mixed(wl, dev, steps, warmup, layer_chunk):
     ms_single = sum(per_ub[u] for u in single)
     ms_chunks = sum(per_ub[u] for u in chunks)
     kv_bytes = sum(cells(u) for u in single) * row * wl.n_layer
-    qo_bytes = sum(2 * len(shapes[u][1]) * HD * 4 * wl.n_layer for u in single)
     flops = sum(cells(u) for u in chunks) * 4.0 * HD * wl.n_layer
     tokens = sum(wl.batches[b].n_tokens for b in meas)
     res = dict(workload=wl.note, tokens_per_s=round(tokens * steps / wall, 1), ms_per_step=round(1e3 * wall / steps, 4),
                tokens_per_step=tokens, ubatches_per_step=len(shapes))
     if single:
-        gbs = (kv_bytes + qo_bytes) / (ms_single * 1e-3) / 1e9
+        gbs = kv_bytes / (ms_single * 1e-3) / 1e9
         res["single_token_ubatches"] = dict(count=len(single), attend_ms=round(ms_single, 4),
                                             kv_read_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
     if chunks:
@@ -492,16 +496,30 @@ def bench_seq_state(dev, n_pos=2048, reps=10):
 # ---------------------------------------------------------------------------
 # oracle on the host cores
 
-def cpu_baseline(wl, budget_s=25.0):
+def host_description():
+    """Host cores, the BLAS threads numpy's matrix products use (the threads
+    the oracle actually runs on) and the CPU model."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(host_cpus=os.cpu_count(), blas_threads=int(blas), cpu_model=model)
+
+
+def cpu_baseline_prefill(wl, budget_s=25.0):
     """The fp64 oracle over the same prompt for as many layers as fit in
     about budget_s, scaled to the full step."""
     from oracle import OracleEngine
     from synthetic import workloads as W
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
     done_layers, t_all = 0, 0.0
     for layer in range(wl.n_layer):
         eng = OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
@@ -522,10 +540,68 @@ def cpu_baseline(wl, budget_s=25.0):
         if t_all >= budget_s:
             break
     per_step = t_all / done_layers * wl.n_layer
-    return dict(value=wl.measured_tokens() / per_step, unit="tokens/s", cores=int(threads), kind="oracle",
+    return dict(value=round(wl.measured_tokens() / per_step, 2), unit="tokens/s",
                 sample=f"{done_layers} of {wl.n_layer} layers of the full {wl.measured_tokens()}-token prompt "
-                       f"(all {sum(1 for _ in wl.batches)} calls, every ubatch), {t_all:.1f}s, scaled x"
-                       f"{wl.n_layer / done_layers:.1f}")
+                       f"(all {len(wl.batches)} calls, every ubatch: split, placement, mask, store, attention), "
+                       f"{t_all:.1f}s, scaled x{wl.n_layer / done_layers:.2f}")
+
+
+def cpu_baseline_decode(wl, layers):
+    """The fp64 oracle on one decode step of ``wl`` for the sampled layers:
+    the context is stored first (untimed, as on the GPU), then the step's
+    split + placement + mask (once) and store + attention (per layer) are
+    timed and scaled to every layer."""
+    from oracle import OracleEngine
+    from synthetic import workloads as W
+    eng = OracleEngine(wl.n_layer, wl.n_head, wl.n_head_kv, wl.head_dim, wl.kv_size, wl.n_stream,
+                       wl.n_seq_max, wl.n_batch, wl.n_ubatch, wl.causal, cell_order=wl.cell_order, layers=layers)
+    t_setup = time.perf_counter()
+    for b, bt in enumerate(wl.batches):
+        if bt.measured:
+            continue
+        st, ubs, _ = eng.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        assert st == 0
+        tens = {l: (wl.tensor(b, l, W.KIND_K), wl.tensor(b, l, W.KIND_V)) for l in layers}
+        for ub in ubs:
+            eng.commit(ub, build_mask=False)
+            for l in layers:
+                eng.store(ub, l, tens[l][0][ub.src], tens[l][1][ub.src])
+    t_setup = time.perf_counter() - t_setup
+    mb = len(wl.batches) - 1
+    bt = wl.batches[mb]
+    tens = {l: [wl.tensor(mb, l, k) for k in (W.KIND_K, W.KIND_V, W.KIND_Q)] for l in layers}
+    t0 = time.perf_counter()
+    st, ubs, _ = eng.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+    for ub in ubs:
+        eng.commit(ub)
+    t_once = time.perf_counter() - t0
+    t_layers = 0.0
+    for l in layers:
+        k, v, q = tens[l]
+        t0 = time.perf_counter()
+        for ub in ubs:
+            eng.store(ub, l, k[ub.src], v[ub.src])
+            eng.attend(ub, l, q[ub.src])
+        t_layers += time.perf_counter() - t0
+    per_step = t_once + t_layers / len(layers) * wl.n_layer
+    return dict(value=round(bt.n_tokens / per_step, 2), unit="tokens/s",
+                sample=f"one decode step of {bt.n_tokens} sequences ({wl.note}): split, placement and mask "
+                       f"{t_once:.2f}s once, store + attention of {len(layers)} of {wl.n_layer} layers "
+                       f"{t_layers:.1f}s, scaled x{wl.n_layer / len(layers):.2f}; the context "
+                       f"({t_setup:.0f}s to store) is not timed, as on the GPU")
+
+
+def cpu_baseline(wl_prefill):
+    """The oracle as it stands, on this host's cores, for the prefill (the
+    headline) and the two decode workloads."""
+    from synthetic import workloads as W
+    pre = cpu_baseline_prefill(wl_prefill)
+    cfg = {"qwen_prefill": pre,
+           "cb_decode": cpu_baseline_decode(W.cb_decode(), [0, 27]),
+           "prefix_decode": cpu_baseline_decode(W.prefix_decode(), [0, 9, 18, 27])}
+    host = host_description()
+    return dict(value=pre["value"], unit="tokens/s", cores=host["blas_threads"], kind="oracle",
+                sample=pre["sample"], **host, configs=cfg)
 
 
 def kernel_source_digest(source):
@@ -560,6 +636,89 @@ def kernel_source_digest(source):
     return h.hexdigest()
 
 
+def committed_trace_ms(kernel, source, leg):
+    """Mean duration (ms) of ``kernel`` over the timed dispatches of ``leg``
+    from the committed rocprofv3 kernel-trace summary (profiles/
+    <kernel>_trace.json, taken with --selected-regions around exactly the
+    loop the HIP events time); None when absent or the kernel's sources
+    changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_trace.json")
+    try:
+        rec = json.load(open(path))
+        digest = kernel_source_digest(source)
+    except (OSError, ValueError):
+        return None
+    legs = rec.get("legs", {})
+    if rec.get("source_digest") != digest or leg not in legs:
+        return None
+    return legs[leg]["avg_ns"] * 1e-6
+
+
+def trace_stats(csv_path, kernel, skip, take):
+    """Duration statistics of the dispatches of ``kernel`` (name prefix, after
+    an optional "void " and namespace) in a rocprofv3 kernel_trace.csv, in
+    dispatch order: the first ``skip`` are dropped (warm-up), the next
+    ``take`` kept (0 = all the rest)."""
+    import csv
+    durs = []
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            name = name[5:] if name.startswith("void ") else name
+            bare = name.split("(")[0].split("<")[0].split("::")[-1]
+            if bare != kernel:
+                continue
+            durs.append((int(row["Dispatch_Id"]), int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+    durs.sort()
+    sel = [d for _, d in durs[skip:skip + take if take else None]]
+    if not sel:
+        raise SystemExit(f"no dispatches of {kernel} left after skipping {skip} of {len(durs)}")
+    a = np.asarray(sel, dtype=np.float64)
+    return dict(kernel=kernel, dispatches_total=len(durs), skipped=skip, n=len(sel), avg_ns=round(float(a.mean()), 1),
+                min_ns=int(a.min()), max_ns=int(a.max()), median_ns=float(np.median(a)))
+
+
+KERNEL_SOURCES = {"k_attn_mfma": "attn_mfma.hip", "k_attn_valu": "attn_valu.hip", "k_attn_reduce": "attn_valu.hip",
+                  "k_store_commit": "kernels_commit.hip", "k_store": "kernels_commit.hip"}
+
+
+def write_trace_record(path, kernel, leg, rec, argv):
+    """Merge one leg's statistics into the per-kernel summary JSON, with the
+    digest of the kernel's sources as they are now (run it in the tree that
+    was profiled)."""
+    try:
+        out = json.load(open(path))
+    except (OSError, ValueError):
+        out = {}
+    out["kernel"] = kernel
+    out["source_digest"] = kernel_source_digest(KERNEL_SOURCES[kernel])
+    out["profile_command"] = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
+                              "python -u <repo>/bench.py --gpus 1 --steps 20 --warmup 5 --no-cpu-baseline")
+    out.setdefault("legs", {})[leg] = dict(rec, summary_command=f"python bench.py {argv}".replace(ROOT + "/", ""))
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+
+
+def hbm_copy_gbs(dev, nbytes=2 << 30, reps=10):
+    """Device-to-device copy of nbytes with torch (read + write both
+    counted), timed with HIP events: what the memory system delivers to a
+    plain streaming kernel, for context beside the 8 TB/s spec."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def committed_traffic(kernel, source):
     """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE /
     WRITE_SIZE summary, scaled by the copy-kernel calibration recorded there;
@@ -585,7 +744,16 @@ def main():
                     help="layers per store/attend call (28 = one call per ubatch, 1 = per layer)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--per-layer", action="store_true", help="also time one call per layer")
+    ap.add_argument("--no-per-layer", action="store_true",
+                    help="skip the one-call-per-layer runs of the prefill and 64-sequence decode")
+    ap.add_argument("--trace-stats", metavar="CSV",
+                    help="no GPU: statistics of one kernel's dispatches in a rocprofv3 kernel_trace.csv, "
+                         "skipping the first --skip (warm-up) and taking the next --take (the timed loop)")
+    ap.add_argument("--kernel", help="with --trace-stats: kernel name prefix (e.g. k_attn_mfma)")
+    ap.add_argument("--skip", type=int, default=0)
+    ap.add_argument("--take", type=int, default=0)
+    ap.add_argument("--leg", help="with --trace-stats: record the result under this leg in --trace-out")
+    ap.add_argument("--trace-out", metavar="JSON", help="with --trace-stats: merge the result into this file")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode workloads (for profiling their kernels alone)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode workload")
@@ -597,6 +765,12 @@ def main():
     ap.add_argument("--decode-workload", choices=["cb_decode", "prefix_decode"], action="append",
                     help="restrict the decode runs to this workload (repeatable)")
     args = ap.parse_args()
+    if args.trace_stats:
+        rec = trace_stats(args.trace_stats, args.kernel, args.skip, args.take)
+        print(json.dumps(rec), flush=True)
+        if args.trace_out:
+            write_trace_record(args.trace_out, args.kernel, args.leg, rec, " ".join(sys.argv[1:]))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the attention path is not "
               f"sharded across GPUs; run it with --gpus 1", file=sys.stderr)
@@ -626,7 +800,8 @@ def main():
     wl = W.qwen_prefill()
     pre = bench_prefill(wl, dev, args.steps, args.warmup, args.layer_chunk)
     tok_s = pre["tokens"] * args.steps / pre["wall_s"]
-    mfma_tf = pre["flops_step"] / pre["attend_launches_per_step"] / (pre["attend_avg_ms"] * 1e-3) / 1e12
+    per_launch_flop = pre["flops_step"] / pre["attend_launches_per_step"]
+    mfma_tf = per_launch_flop / (pre["attend_avg_ms"] * 1e-3) / 1e12
     log(f"[bench] prefill: {tok_s:,.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
         f"attend {pre['attend_avg_ms']:.3f} ms/launch x {pre['attend_launches_per_step']:.0f}, "
         f"{mfma_tf:.1f} TFLOP/s")
@@ -652,15 +827,28 @@ def main():
                      "achieved": round(mfma_tf, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(mfma_tf / MFMA_F16_PEAK_TFLOPS, 4),
                      "traffic": committed_traffic("k_attn_mfma", "attn_mfma.hip"),
-                     "per_launch": f"{pre['flops_step'] / pre['attend_launches_per_step'] / 1e9:.2f} GFLOP "
-                                   f"(4*H*d per visible (query, cell) pair x 28 layers of one ubatch), "
-                                   f"avg {pre['attend_avg_ms']:.3f} ms"},
+                     "per_launch": f"{per_launch_flop / 1e9:.2f} GFLOP "
+                                   f"(4*H*d per visible (query, cell) pair x 28 layers of one ubatch)",
+                     "event_avg_ms": round(pre["attend_avg_ms"], 4)},
     }
-    if args.per_layer:
-        pl = bench_prefill(wl, dev, max(2, args.steps // 2), 1, 1)
-        line["per_layer_calls"] = {"tokens_per_s": round(pl["tokens"] * max(2, args.steps // 2) / pl["wall_s"], 1),
-                                   "ms_per_step": round(pl["ms_per_step"], 3),
-                                   "attend_avg_ms": round(pl["attend_avg_ms"], 4)}
+    trace_ms = committed_trace_ms("k_attn_mfma", "attn_mfma.hip", "prefill")
+    if trace_ms is not None:
+        tf_trace = per_launch_flop / (trace_ms * 1e-3) / 1e12
+        line["roofline"].update(trace_avg_ms=round(trace_ms, 4), frac_trace=round(tf_trace / MFMA_F16_PEAK_TFLOPS, 4))
+    line["hbm_copy_gbs"] = hbm_copy_gbs(dev)
+    log(f"[bench] device-to-device copy: {line['hbm_copy_gbs']:.0f} GB/s")
+    if not args.no_per_layer:
+        # a forward pass calls attend once per layer (layer l+1's q depends on
+        # layer l): the same prompt with one store and one attend per layer
+        ps = max(2, args.steps // 2)
+        pl = bench_prefill(wl, dev, ps, 1, 1)
+        line["per_layer_calls"] = {"prefill": {
+            "tokens_per_s": round(pl["tokens"] * ps / pl["wall_s"], 1), "ms_per_step": round(pl["ms_per_step"], 4),
+            "attend_launches_per_step": round(pl["attend_launches_per_step"], 1),
+            "attend_us_per_launch": round(1e3 * pl["attend_avg_ms"], 2),
+            "attend_ms_per_step": round(pl["attend_ms_per_step"], 4),
+            "tflops_attend": round(pre["flops_step"] / (pl["attend_ms_per_step"] * 1e-3) / 1e12, 1)}}
+        log(f"[bench] prefill, one call per layer: {line['per_layer_calls']['prefill']}")
     if not args.no_decode:
         dec = {}
         for name, w in decode_wls:
@@ -670,8 +858,18 @@ def main():
             dec[name] = {"workload": w.note, "tokens_per_s": round(r["tokens_per_s"], 1),
                          "ms_per_step": round(r["ms_per_step"], 4),
                          "kv_read_gbs": round(r["kv_read_gbs"], 1), "hbm_frac": round(r["hbm_frac"], 4),
+                         "kv_bytes_per_step": round(r["kv_bytes_step"]), "qo_bytes_per_step": round(r["qo_bytes_step"]),
+                         "kv_qo_gbs": round(r["kv_qo_gbs"], 1),
                          "attend_avg_ms": round(r["attend_avg_ms"], 4),
                          "unique_cells_per_step": r["unique_cells"], "plan": r["plan"]}
+            if name == "cb_decode" and not args.no_per_layer:
+                rp = bench_decode(w, dev, args.steps, args.warmup, 1)
+                line.setdefault("per_layer_calls", {})["cb_decode"] = {
+                    "tokens_per_s": round(rp["tokens_per_s"], 1), "ms_per_step": round(rp["ms_per_step"], 4),
+                    "attend_launches_per_step": round(rp["attend_launches_per_step"], 1),
+                    "attend_us_per_launch": round(1e3 * rp["attend_avg_ms"], 2),
+                    "kv_read_gbs": round(rp["kv_read_gbs"], 1), "hbm_frac": round(rp["hbm_frac"], 4)}
+                log(f"[bench] cb_decode, one call per layer: {line['per_layer_calls']['cb_decode']}")
             if name == "cb_decode":
                 # the vector-ALU kernel's HBM bytes per launch from the committed
                 # FETCH_SIZE / WRITE_SIZE summary of this workload (None if stale)
@@ -709,6 +907,8 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(wl)
+        log(f"[bench] oracle: " + ", ".join(f"{k} {v['value']:.1f} tok/s"
+                                            for k, v in line["cpu_baseline"]["configs"].items()))
     print(json.dumps(line), flush=True)
 
 

@@ -10,7 +10,14 @@ import numpy as np
 from oracle import OracleEngine
 from synthetic import workloads as W
 
-ATOL, RTOL = 2e-3, 5e-3        # |g - r| <= ATOL + RTOL * |r| elementwise
+ATOL, RTOL = 2e-3, 5e-3        # |g - r| <= ATOL + RTOL * |r| elementwise, and max |g - r| <= ATOL
+# Internal bounds, tighter than the tolerance, to catch mistakes that stay
+# inside it.  The fp32 vector-ALU path differs from the fp64 oracle only by
+# fp32 rounding.  The matrix-core path rounds the scaled q and the softmax
+# weights to F16; the first-order effect on an output is bounded by the
+# weights' relative error times the spread of the visible values.
+VALU_BOUND = 2e-5
+MFMA_BOUND = 1.6e-3
 
 
 def batch_tensors(wl, b, layers, with_q):
@@ -110,8 +117,9 @@ def gpu_run(wl, layers, layer_chunk=None, only_outputs=False, on_ubatch=None, ct
     return ctx, res
 
 
-def assert_parity(got, ref, rows=None, tag=""):
-    """Elementwise |g - r| <= ATOL + RTOL |r|; returns (max abs, max rel)."""
+def assert_parity(got, ref, rows=None, tag="", strict_abs=True):
+    """Elementwise |g - r| <= ATOL + RTOL |r| and, with strict_abs, also
+    max |g - r| <= ATOL; returns (max abs, max rel over |r| >= 1e-2)."""
     g, r = got, ref
     if rows is not None:
         g, r = g[rows], r[rows]
@@ -124,4 +132,5 @@ def assert_parity(got, ref, rows=None, tag=""):
         i = np.argwhere(bad)[0]
         raise AssertionError(f"{tag}: {bad.sum()} elements out of tolerance; first at {tuple(i)}: "
                              f"got {g[tuple(i)]!r} ref {r[tuple(i)]!r}; max abs {err.max():.3e}")
+    assert not strict_abs or err.max() <= ATOL, f"{tag}: max abs error {err.max():.3e} above {ATOL}"
     return float(err.max()), float(rel)

@@ -49,3 +49,38 @@ def test_committed_summaries_record_a_digest():
     for name in ("k_attn_mfma_traffic.json", "k_attn_valu_traffic.json"):
         rec = json.load(open(os.path.join(ROOT, "profiles", name)))
         assert len(rec["source_digest"]) == 64 and rec["bytes_per_launch"] > 0
+
+
+def test_trace_average_is_reported_only_for_unchanged_sources(tmp_path, monkeypatch):
+    import bench
+    csrc = tmp_path / "ubatch_attention_paged_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "include").mkdir()
+    (tmp_path / "profiles").mkdir()
+    (csrc / "k.hip").write_text("kernel\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    rec = {"source_digest": bench.kernel_source_digest("k.hip"), "legs": {"prefill": {"avg_ns": 250000.0}}}
+    (tmp_path / "profiles" / "k_x_trace.json").write_text(json.dumps(rec))
+    assert abs(bench.committed_trace_ms("k_x", "k.hip", "prefill") - 0.25) < 1e-12
+    assert bench.committed_trace_ms("k_x", "k.hip", "cb_decode") is None
+    (csrc / "k.hip").write_text("kernel, changed\n")
+    assert bench.committed_trace_ms("k_x", "k.hip", "prefill") is None
+
+
+def test_trace_stats_skips_warmup_dispatches(tmp_path):
+    """--trace-stats keeps exactly the dispatches after the warm-up ones, of
+    the named kernel only, in dispatch order."""
+    import bench
+    hdr = '"Kind","Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp"\n'
+    rows = []
+    for i in range(10):
+        rows.append(f'"KERNEL_DISPATCH",{2 * i + 1},"void kvattn::k_attn_mfma<128, 2, false>(kvattn::AttnArgs)",'
+                    f'{1000 * i},{1000 * i + 100 + i}\n')
+        rows.append(f'"KERNEL_DISPATCH",{2 * i + 2},"kvattn::k_store_commit(kvattn::StoreArgs, kvattn::CsrArgs)",'
+                    f'{1000 * i + 500},{1000 * i + 550}\n')
+    p = tmp_path / "t.csv"
+    p.write_text(hdr + "".join(reversed(rows)))
+    r = bench.trace_stats(str(p), "k_attn_mfma", 3, 4)
+    assert (r["n"], r["dispatches_total"], r["min_ns"], r["max_ns"]) == (4, 10, 103, 106)
+    assert r["avg_ns"] == 104.5
+    assert bench.trace_stats(str(p), "k_store_commit", 0, 0)["n"] == 10

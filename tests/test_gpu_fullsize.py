@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from synthetic import workloads as W
-from tests.helpers import assert_parity, gpu_run, oracle_run
+from tests.helpers import MFMA_BOUND, VALU_BOUND, assert_parity, gpu_run, oracle_run
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow, pytest.mark.timeout(300)]
 
@@ -81,7 +81,7 @@ def test_full_size_sampled_layers(name):
     for key in sorted(ref):
         ma, _ = assert_parity(got[key], ref[key], tag=f"{name} batch {key[0]} layer {key[1]}")
         worst = max(worst, ma)
-    bound = 2e-5 if name == "cb_decode" else 1.6e-3
+    bound = VALU_BOUND if name == "cb_decode" else MFMA_BOUND
     assert worst < bound, worst
     occ = eng.cells.pos >= 0
     for l in keep:

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from synthetic import workloads as W
-from tests.helpers import assert_parity, gpu_run, oracle_run, make_ctx
+from tests.helpers import MFMA_BOUND, VALU_BOUND, assert_parity, gpu_run, oracle_run, make_ctx
 
 pytestmark = pytest.mark.gpu
 
@@ -84,14 +84,16 @@ def test_end_to_end_parity(name):
     ub_index = {b: 0 for b in range(len(wl.batches))}
     ctx, got = gpu_run(wl, layers, on_ubatch=check)
     assert seen["mask"] == len(meta)
-    worst = 0.0
+    worst, worst_rel = 0.0, 0.0
     for key in ref:
         ma, mr = assert_parity(got[key], ref[key], tag=f"{name} batch {key[0]} layer {key[1]}")
-        worst = max(worst, ma)
+        worst, worst_rel = max(worst, ma), max(worst_rel, mr)
     # tighter than the tolerance: the fp32 vector-ALU path (decode-only
     # workloads) agrees to ~1e-6; the MFMA path rounds q and the softmax
-    # weights to F16 (relative 2^-11), which moves outputs by ~1e-3 at most
-    bound = 2e-5 if name == "cb_decode" else 1.6e-3
+    # weights to F16 (relative 2^-11)
+    bound = VALU_BOUND if name == "cb_decode" else MFMA_BOUND
+    print(f"[gpu] end_to_end {name}: max abs error {worst:.3e} (bound {bound:.1e}), "
+          f"max rel error {worst_rel:.3e} over |ref| >= 1e-2", flush=True)
     assert worst < bound, worst
     # cache bytes: every committed cell row equals the oracle's F16 rounding
     for l in layers:
@@ -127,8 +129,12 @@ def test_mfma_head_shapes(d, g, swa):
         items["mfma"] += ctx.plan_stats()["n_items_mfma"]
 
     ctx, got = gpu_run(wl, layers, on_ubatch=count)
+    worst = 0.0
     for key in ref:
-        assert_parity(got[key], ref[key], tag=f"d={d} g={g} window {swa} batch {key[0]}")
+        ma, _ = assert_parity(got[key], ref[key], tag=f"d={d} g={g} window {swa} batch {key[0]}")
+        worst = max(worst, ma)
+    print(f"[gpu] head shape d={d} g={g} window {swa}: max abs error {worst:.3e}", flush=True)
+    assert worst < MFMA_BOUND, worst
     assert items["mfma"] > 0
     ctx.close()
 
@@ -230,13 +236,44 @@ def test_only_outputs_and_layer_chunks():
     _, per_layer = gpu_run(wl, layers, layer_chunk=1)
     _, outs = gpu_run(wl, layers, only_outputs=True)
     for key in ref:
-        assert np.array_equal(full[key], per_layer[key])          # same kernels, same result
+        # items are sized for the layers per call (one layer per call may cut
+        # prompt classes into chunks merged by split-K), so the two agree to
+        # rounding, and each against the oracle
+        assert_parity(per_layer[key], ref[key], tag=f"one layer per call {key}")
+        assert np.abs(per_layer[key] - full[key]).max() < MFMA_BOUND
         b = key[0]
         flagged = np.nonzero(wl.batches[b].output)[0]
         assert_parity(outs[key], ref[key], rows=flagged, tag=f"only_outputs {key}")
         # fewer query rows can move a class from the MFMA kernel to the fp32
         # vector kernel, so the two runs agree to rounding, not bit for bit
-        assert np.abs(outs[key][flagged] - full[key][flagged]).max() < 1.6e-3
+        assert np.abs(outs[key][flagged] - full[key][flagged]).max() < MFMA_BOUND
+
+
+@pytest.mark.parametrize("n_prompt", [700, 1200])
+def test_prompt_split_k_one_layer_per_call(n_prompt):
+    """One layer per attend call: a prompt ubatch's 128-row matrix-core items
+    alone would leave most of the GPU idle, so their cell lists are cut into
+    chunks (multiples of the 64-cell tile) whose partial softmax states the
+    merge kernel combines -- including chunks wholly in the future of an
+    item's queries, which contribute nothing."""
+    wl = W.qwen_prefill(n_prompt=n_prompt, n_layer=2, kv_size=2048, n_batch=n_prompt, n_ubatch=512)
+    layers = [0, 1]
+    print(f"[gpu] prompt split-K, {n_prompt} tokens, one layer per call", flush=True)
+    _, ref, _, _ = oracle_run(wl, layers)
+    split = {"rows": 0}
+
+    def count(ctx, b, ub):
+        split["rows"] = max(split["rows"], ctx.plan_stats()["n_partial_rows"])
+
+    ctx, got = gpu_run(wl, layers, layer_chunk=1, on_ubatch=count)
+    assert split["rows"] > 0
+    worst = 0.0
+    for key in ref:
+        ma, _ = assert_parity(got[key], ref[key], tag=f"prompt split-K {n_prompt} {key}")
+        worst = max(worst, ma)
+    print(f"[gpu] prompt split-K {n_prompt}: max abs error {worst:.3e}", flush=True)
+    assert worst < MFMA_BOUND, worst
+    ctx.close()
 
 
 @pytest.mark.parametrize("n_ubatch", [512, 64, 7])
@@ -371,7 +408,11 @@ def test_mfma_running_max_jumps(needle_pos):
         eng.commit(ub)
         eng.store(ub, 0, k[ub.src], v[ub.src])
         ref[ub.src] = eng.attend(ub, 0, q[ub.src])
-    assert_parity(got, ref, tag=f"needle at {needle_pos}")
+    # the needle's scores are ~30x those of N(0,1) keys, and rounding the
+    # scaled q to F16 moves them by up to ~0.01 (log2 units): outputs near the
+    # needle's value (|r| ~ 1) move by up to ~2.5e-3, inside the elementwise
+    # tolerance 2e-3 + 5e-3 |r| but not always below 2e-3 in absolute terms
+    assert_parity(got, ref, tag=f"needle at {needle_pos}", strict_abs=False)
 
 
 @pytest.mark.parametrize("needle_pos", [3, 150, 199])
@@ -423,7 +464,8 @@ def test_noncausal_parity(name):
     for key in ref:
         ma, _ = assert_parity(got[key], ref[key], tag=f"non-causal {name} {key}")
         worst = max(worst, ma)
-    assert worst < (2e-5 if name == "cb_decode" else 1.6e-3), worst
+    print(f"[gpu] non-causal {name}: max abs error {worst:.3e}", flush=True)
+    assert worst < (VALU_BOUND if name == "cb_decode" else MFMA_BOUND), worst
 
 
 @pytest.mark.parametrize("name,mode", [("mixed", "seq"), ("prefix", "seq"), ("prefill", "seq"), ("mixed", "simple")])

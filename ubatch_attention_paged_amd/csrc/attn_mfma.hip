@@ -67,11 +67,12 @@ struct BoolTag {
 
 // SWA: the sliding-window variant (a.swa > 0); the other compiles without any
 // of its tests
-template <int D, int G, bool SWA>
-__global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(AttnArgs a) {
-  constexpr int RB = kMfmaRowBlocks;              // 32-row blocks per wavefront
+template <int D, int G, bool SWA, int RB>
+__global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
+  // RB 32-row blocks per wavefront, NW wavefronts of 32 * RB rows
+  constexpr int NW = 4 / RB;
   constexpr int QT = kMfmaRowsPerItem / G;        // queries per item
-  static_assert(kMfmaRowsPerItem == 128 * RB, "4 wavefronts x RB x 32 rows");
+  static_assert(kMfmaRowsPerItem == 128 && NW * RB == 4, "NW wavefronts x RB x 32 rows = 128");
   constexpr int KT = kTileCells;                  // cells per tile (64)
   constexpr int DP = D < 32 ? 32 : D;             // O^T rows, padded to a 32-row block
   // LDS tiles: K rows of D halfs, V rows of DP halfs (columns D.. of a V
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   constexpr int SV = DP / 8;                      // per V row; segments >= SK are zero padding
   constexpr int RK = 64 / SK, RV = 64 / SV;       // rows per instruction
   constexpr int NK = KT / RK, NV = KT / RV;       // instructions per tile
-  constexpr int JK = (NK + 3) / 4, JV = (NV + 3) / 4;   // per wavefront
+  constexpr int JK = (NK + NW - 1) / NW, JV = (NV + NW - 1) / NW;   // per wavefront
   constexpr bool SAME_ROWS = SK == SV;            // K and V instructions cover the same rows
   // Swizzles, for LDS serving 256 B (64 banks of 4 B) per cycle.  K: a
   // 16 B fragment read serves 16 lanes per cycle, 16 consecutive rows at one
@@ -199,13 +200,13 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   uint32_t colk[JK], colv[JV];     // byte column in the cache row; kOobOffset = zero padding
 #pragma unroll
   for (int j = 0; j < JK; ++j) {
-    rowk[j] = (wv + 4 * j) * RK + lane / SK;
+    rowk[j] = (wv + NW * j) * RK + lane / SK;
     const int sg = (lane % SK) ^ ((rowk[j] / RBK) & MK);
     colk[j] = static_cast<uint32_t>(kvh * D + sg * 8) * 2;
   }
 #pragma unroll
   for (int j = 0; j < JV; ++j) {
-    rowv[j] = (wv + 4 * j) * RV + lane / SV;
+    rowv[j] = (wv + NW * j) * RV + lane / SV;
     const int sg = (lane % SV) ^ (((rowv[j] & 3) >> VSH) << 2);
     colv[j] = sg < SK ? static_cast<uint32_t>(kvh * D + sg * 8) * 2 : kOobOffset;
   }
@@ -217,8 +218,8 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
   int cnext[JC];                                   // raw list entries; validity is decided at use
   int pk = INT32_MAX, nmin = 0, nmax = 0;
   uint64_t mk = 0;
-  auto has_k = [&](int j) { return NK % 4 == 0 || wv + 4 * j < NK; };   // wave-uniform
-  auto has_v = [&](int j) { return NV % 4 == 0 || wv + 4 * j < NV; };
+  auto has_k = [&](int j) { return NK % NW == 0 || wv + NW * j < NK; };   // wave-uniform
+  auto has_v = [&](int j) { return NV % NW == 0 || wv + NW * j < NV; };
   // the list entry is read at a clamped index (no branch, no wait)
   auto cells_of = [&](int tile, int* cells) {
     const int base = it.c0 + tile * KT;
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
       if (has_k(j)) {
         const uint32_t off =
             rowk[j] < lim ? sbase_bytes + static_cast<uint32_t>(cells[j]) * row_bytes + colk[j] : kOobOffset;
-        buffer_load16_lds(krw, lds_addr(&Ks[bsel][(wv + 4 * j) * 512]), off);
+        buffer_load16_lds(krw, lds_addr(&Ks[bsel][(wv + NW * j) * 512]), off);
       }
 #pragma unroll
     for (int j = 0; j < JV; ++j)
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
         const uint32_t off = rowv[j] < lim && colv[j] != kOobOffset
                                  ? sbase_bytes + static_cast<uint32_t>(cl) * row_bytes + colv[j]
                                  : kOobOffset;
-        buffer_load16_lds(vrw, lds_addr(&Vs[bsel][(wv + 4 * j) * 512]), off);
+        buffer_load16_lds(vrw, lds_addr(&Vs[bsel][(wv + NW * j) * 512]), off);
       }
     if (tid < KT) {
       const int idx = it.c0 + tile * KT + tid;
@@ -448,10 +449,11 @@ __global__ __launch_bounds__(256, kMfmaRowBlocks == 1 ? 2 : 1) void k_attn_mfma(
 
 template <int D, int G>
 static void mfma_launch(const AttnArgs& a, int n_il, hipStream_t s) {
+  constexpr int RB = kMfmaRowBlocks;
   if (a.swa > 0)
-    hipLaunchKernelGGL((k_attn_mfma<D, G, true>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_attn_mfma<D, G, true, RB>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256 / RB), 0, s, a);
   else
-    hipLaunchKernelGGL((k_attn_mfma<D, G, false>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_attn_mfma<D, G, false, RB>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256 / RB), 0, s, a);
 }
 
 template <int D>

@@ -579,11 +579,12 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   // the launch still reaches its workgroup target, so a long context is
   // split only when there are too few queries to fill the GPU.
   const int64_t L = std::max(1, g_.attend_layers);
-  std::vector<std::pair<int32_t, int32_t>> valu_lists, low_lists;   // (cells, copies)
+  std::vector<std::pair<int32_t, int32_t>> valu_lists, low_lists, high_lists;   // (cells, copies)
   for (const auto& c : P.classes) {
     if (c.n_q == 0 || c.n_cells == 0) continue;
     if (valu_ok && c.n_q <= kValuMaxQueries) valu_lists.push_back({c.n_cells, c.n_q});
     else if (c.n_q * G <= 64) low_lists.push_back({c.n_cells, ceil_div(c.n_q, QT) * g_.n_head_kv});
+    else high_lists.push_back({c.n_cells, ceil_div(c.n_q, QT) * g_.n_head_kv});
   }
   auto pick_chunk = [&](const std::vector<std::pair<int32_t, int32_t>>& lists, int64_t target, int32_t lo,
                         int32_t hi) {
@@ -596,10 +597,14 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
     }
     return ch;
   };
-  int32_t chv = pick_chunk(valu_lists, kValuTargetWorkgroups, 256, 8192);
+  int32_t chv = pick_chunk(valu_lists, kValuTargetWorkgroups, kValuMinChunk, 8192);
   // matrix-core items with few query rows are bandwidth-bound too: their
   // cells (multiples of the 64-cell tile) are cut the same way
   int32_t chm_lowreuse = pick_chunk(low_lists, kMfmaTargetWorkgroups, 256, 4096);
+  // prompt-sized classes are cut only when the launch would not fill the
+  // GPU otherwise (one layer per call): every cut costs a partial row per
+  // query and merge work, so a layer range keeps whole cell lists
+  int32_t chm_high = pick_chunk(high_lists, kMfmaHighTargetWorkgroups, 256, 1 << 30);
 
   for (int attempt = 0; attempt < 16; ++attempt) {
     P.items_valu.clear();
@@ -626,7 +631,7 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
         }
       } else {
         // few query rows per KV head -> bandwidth-bound -> split the cells
-        const int32_t ch = (c.n_q * G <= 64) ? chm_lowreuse : c.n_cells;
+        const int32_t ch = (c.n_q * G <= 64) ? chm_lowreuse : chm_high;
         for (int32_t t0 = 0; t0 < c.n_q; t0 += QT) {
           const int32_t nq = std::min(QT, c.n_q - t0);
           int32_t pmin = INT32_MAX, pmax = INT32_MIN;
@@ -660,6 +665,7 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
     if (rows > prow_max) {
       chv *= 2;
       chm_lowreuse *= 2;
+      chm_high = std::min(chm_high, 1 << 29) * 2;
       continue;
     }
     P.n_partial_rows = rows;

@@ -24,7 +24,7 @@ constexpr int kSmallCommitClasses = 64;   // and this many classes (and lookup e
 constexpr int kSmallCommitStreams = 64;   // and streams run in one workgroup beside the stores
 constexpr int kValuMaxQueries = 2;     // classes with more queries go to the MFMA kernel
 constexpr int kMfmaRowBlocks = 1;      // 32-row blocks per wavefront of the matrix-core kernel
-constexpr int kMfmaRowsPerItem = 128 * kMfmaRowBlocks;  // query rows (queries x heads of one KV head) per item
+constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV head) per item
 // Workgroups a split-K launch should reach before its items are cut finer
 // (256 CUs; the vector-ALU kernel keeps 5 workgroups per CU, the
 // matrix-core kernel 2).  Measured on decode steps: long items win over a
@@ -33,6 +33,14 @@ constexpr int kMfmaRowsPerItem = 128 * kMfmaRowBlocks;  // query rows (queries x
 // resident workgroups or below.
 constexpr int kValuTargetWorkgroups = 1024;
 constexpr int kMfmaTargetWorkgroups = 320;
+// Prompt-sized matrix-core classes (more than 64 query rows per KV head) are
+// cut only below this many workgroups per launch -- in practice only when a
+// launch covers one layer -- and never into pieces under 256 cells.
+constexpr int kMfmaHighTargetWorkgroups = 512;
+// Decode chunks never shrink below 256 cells: measured on one-layer decode
+// launches, 64-cell chunks (4x the workgroups) ran slower than 256 (more
+// partial rows to merge, more per-item ramp).
+constexpr int kValuMinChunk = 256;
 
 struct SlotInfo {        // one query slot
   int32_t stream;

@@ -15,7 +15,9 @@ from typing import Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvattn.so")
+# KVATTN_LIB selects another build of the same library (the host-sanitizer
+# build for CPU test runs); the default is the in-tree libkvattn.so
+LIB_PATH = os.environ.get("KVATTN_LIB") or os.path.join(HERE, "libkvattn.so")
 
 KVATTN_OK, KVATTN_NO_SLOT = 0, 1
 KVATTN_SPLIT_AUTO, KVATTN_SPLIT_SIMPLE, KVATTN_SPLIT_EQUAL, KVATTN_SPLIT_SEQ = 0, 1, 2, 3
