@@ -56,7 +56,7 @@ WsLayout ws_layout(const Geometry& g) {
 
 // Device offsets of one plan inside the arena.
 struct VariantLayout {
-  size_t slots, qlist, items_valu, items_mfma, red_slot, red_off, red_rows;
+  size_t slots, qslots, items_valu, items_mfma, red_slot, red_off, red_rows;
 };
 struct ArenaLayout {
   size_t classes, lookup, lookup_off, dst_rows, updates;
@@ -209,7 +209,7 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
     for (int v = 0; v < 2; ++v) {
       const Plan& P = c->plan[v];
       A.v[v].slots = take(P.slots.size() * sizeof(SlotInfo));
-      A.v[v].qlist = take(P.qlist.size() * 4);
+      A.v[v].qslots = take(P.qlist.size() * sizeof(SlotInfo));
       A.v[v].items_valu = take(P.items_valu.size() * sizeof(WorkItem));
       A.v[v].items_mfma = take(P.items_mfma.size() * sizeof(WorkItem));
       A.v[v].red_slot = take(P.red_slot.size() * 4);
@@ -247,7 +247,10 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
   for (int v = 0; v < 2; ++v) {
     const Plan& P = c->plan[v];
     copy(A.v[v].slots, P.slots.data(), P.slots.size() * sizeof(SlotInfo));
-    copy(A.v[v].qlist, P.qlist.data(), P.qlist.size() * 4);
+    // each class's queries as slot records in class order (one load per
+    // query row in the kernels instead of a list entry, then its slot)
+    SlotInfo* qs = reinterpret_cast<SlotInfo*>(b + A.v[v].qslots);
+    for (size_t i = 0; i < P.qlist.size(); ++i) qs[i] = P.slots[P.qlist[i]];
     copy(A.v[v].items_valu, P.items_valu.data(), P.items_valu.size() * sizeof(WorkItem));
     copy(A.v[v].items_mfma, P.items_mfma.data(), P.items_mfma.size() * sizeof(WorkItem));
     copy(A.v[v].red_slot, P.red_slot.data(), P.red_slot.size() * 4);
@@ -529,7 +532,7 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
   AttnArgs a{};
   a.slots = reinterpret_cast<const SlotInfo*>(arena + VL.slots);
   a.classes = reinterpret_cast<const ClassInfo*>(arena + c->al.classes);
-  a.qlist = reinterpret_cast<const int32_t*>(arena + VL.qlist);
+  a.qslots = reinterpret_cast<const SlotInfo*>(arena + VL.qslots);
   a.csr_cell = c->dptr<int32_t>(c->wl.csr_cell);
   a.csr_pos = c->dptr<int32_t>(c->wl.csr_pos);
   a.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);

@@ -14,7 +14,13 @@
 //    barrier per tile.
 //  * Wavefront w computes S^T[64 cells][its 32 rows] = K Q^T with
 //    v_mfma_f32_32x32x16_f16 (A = K rows from LDS, B = its queries, held in
-//    registers as F16 and pre-scaled by scale*log2(e)).
+//    registers as F16 and pre-scaled by scale*log2(e)).  The q rows are read
+//    once, coalesced (1 KB of contiguous q per wavefront instruction), and
+//    reach the operand layout through a swizzled staging pass in the second
+//    ring buffer, which the tile loop only fills after its first barrier.
+//    The loads that depend on the work item alone (tile ranges, the first
+//    cell indices, the query slots) go out together, then q, then the first
+//    tile's gather.
 //  * Each lane owns one query row (column lane % 32 of the accumulators):
 //    mask, online base-2 softmax, then P^T goes straight from the S^T
 //    accumulators into the B operand of O^T = V^T P^T -- a lane's 16 scores
@@ -102,98 +108,34 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   const int HK = a.n_head_kv;
   const int H = a.n_head;
   const int E = HK * D;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int half_id = lane >> 5;
   const int kvh = blockIdx.x % HK;
   const WorkItem it = a.items[blockIdx.x / HK];
   const int il = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int half_id = lane >> 5;
-  const ClassInfo ci = a.classes[it.cls];
-  const bool pure = ci.pure;
+  const bool pure = it.pure;
   // K / V rows are gathered with range-checked buffer loads: 32-bit byte
   // offsets, and an empty slot reads zeros from an out-of-range offset
   const u32x4 krw = buffer_rsrc_words(a.k[il], a.layer_bytes);
   const u32x4 vrw = buffer_rsrc_words(a.v[il], a.layer_bytes);
   const uint32_t row_bytes = static_cast<uint32_t>(E) * 2;
-  const uint32_t sbase_bytes = static_cast<uint32_t>(ci.stream) * static_cast<uint32_t>(a.kv_size) * row_bytes;
+  const uint32_t sbase_bytes = static_cast<uint32_t>(it.stream) * static_cast<uint32_t>(a.kv_size) * row_bytes;
 
-  // this lane's query rows: row block b of wavefront w is rows
-  // 32 * (w * RB + b) .. +31, the lane owning row lane % 32 of it
-  int t_r[RB], h_r[RB], pos_lim[RB], pos_lo[RB], qseq[RB];
-  bool qvalid[RB];
-  SlotInfo si[RB];
-  bool any_row = false;
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    const int r = 32 * (w * RB + b) + (lane & 31);
-    const int hg = r / QT;
-    t_r[b] = r % QT;
-    qvalid[b] = t_r[b] < it.n_q;
-    si[b] = a.slots[a.qlist[it.q_off + (qvalid[b] ? t_r[b] : 0)]];
-    h_r[b] = kvh * G + hg;
-    pos_lim[b] = a.causal ? si[b].pos : INT32_MAX - 1;   // largest visible cell position
-    pos_lo[b] = SWA ? si[b].pos - a.swa + 1 : INT32_MIN;   // smallest, with a sliding window
-    qseq[b] = si[b].seq0;
-    any_row |= qvalid[b];
-  }
-  const bool wave_rows = ballot(any_row) != 0ULL;   // wave-uniform: padding-only waves skip the math
-
-  // B operand of S^T = K Q^T: q[row][16*ks + 8*half + 0..7], scaled, F16
-  half8 qb[RB][D / 16];
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    const float* qp = a.q[il] + static_cast<int64_t>(si[b].q_row) * H * D + h_r[b] * D + 8 * half_id;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const float4 x0 = qvalid[b] ? *reinterpret_cast<const float4*>(qp + 16 * ks) : make_float4(0, 0, 0, 0);
-      const float4 x1 = qvalid[b] ? *reinterpret_cast<const float4*>(qp + 16 * ks + 4) : make_float4(0, 0, 0, 0);
-      qb[b][ks][0] = static_cast<_Float16>(x0.x * a.scale_log2e);
-      qb[b][ks][1] = static_cast<_Float16>(x0.y * a.scale_log2e);
-      qb[b][ks][2] = static_cast<_Float16>(x0.z * a.scale_log2e);
-      qb[b][ks][3] = static_cast<_Float16>(x0.w * a.scale_log2e);
-      qb[b][ks][4] = static_cast<_Float16>(x1.x * a.scale_log2e);
-      qb[b][ks][5] = static_cast<_Float16>(x1.y * a.scale_log2e);
-      qb[b][ks][6] = static_cast<_Float16>(x1.z * a.scale_log2e);
-      qb[b][ks][7] = static_cast<_Float16>(x1.w * a.scale_log2e);
-    }
-  }
-
-  // tiles of this item; trailing tiles in the future of every query are
-  // dropped, and with a sliding window leading tiles behind every query's
-  // window (tiles are walked from t0)
-  const int tb = ci.tile_base + (it.c0 - ci.cell_off) / KT;
+  // The first loads depend on the work item alone and go out together: the
+  // per-tile position ranges (trimming), the cell indices of the first two
+  // tiles (without a sliding window the walk starts at tile 0) and the slot
+  // records of this lane's query rows.  Then the first tile's gather and
+  // the q rows.
+  const int tb = it.tile_base;
   int ntile = (it.c1 - it.c0 + KT - 1) / KT;
+  int last = -1;
   if (a.causal) {
-    int last = -1;
     for (int k = lane; k < ntile; k += 64)
       if (a.tile_min[tb + k] <= it.qpos_max) last = k;
-    ntile = wave_max_i(last) + 1;
-  }
-  const int win_lo = SWA ? it.qpos_min - a.swa + 1 : INT32_MIN;   // no query sees below this
-  int t0 = 0;
-  if constexpr (SWA) {
-    int first = ntile;
-    for (int k = lane; k < ntile; k += 64)
-      if (a.tile_max[tb + k] >= win_lo) first = min(first, k);
-    t0 = wave_min_i(first);
-  }
-
-  floatx16 oacc[RB][DP / 32];
-  // l_run: this lane's share of each row's sum (its 16 cells of every
-  // 32-cell block); lanes l and l ^ 32 always hold the same running maximum,
-  // so the two shares are rescaled alike and added once at the end
-  float m_run[RB], l_run[RB];
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    m_run[b] = -INFINITY;
-    l_run[b] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DP / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[b][db][i] = 0.f;
   }
 
   // loader geometry: instruction j of wavefront wv fills LDS kilobyte
-  // t = wv + 4 j of the tile; lane -> row t * R + lane / S, stored segment
+  // t = wv + NW j of the tile; lane -> row t * R + lane / S, stored segment
   // lane % S, which holds the row's segment (lane % S) ^ swizzle(row)
   const int wv = __builtin_amdgcn_readfirstlane(w);
   int rowk[JK], rowv[JV];
@@ -210,14 +152,8 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
     const int sg = (lane % SV) ^ (((rowv[j] & 3) >> VSH) << 2);
     colv[j] = sg < SK ? static_cast<uint32_t>(kvh * D + sg * 8) * 2 : kOobOffset;
   }
-  // Everything a tile needs from memory is requested one tile (cell
-  // indices: two tiles) ahead and first read after the vmcnt(0) that opens
-  // that tile, so no wait inside a tile's compute covers the loads in flight
-  // (vmcnt retires in order: any wait would also wait for the next tile).
   constexpr int JC = SAME_ROWS ? JK : JK + JV;     // cell indices a lane needs per tile
-  int cnext[JC];                                   // raw list entries; validity is decided at use
-  int pk = INT32_MAX, nmin = 0, nmax = 0;
-  uint64_t mk = 0;
+  int cfirst[JC], cnext[JC];                       // raw list entries; validity is decided at use
   auto has_k = [&](int j) { return NK % NW == 0 || wv + NW * j < NK; };   // wave-uniform
   auto has_v = [&](int j) { return NV % NW == 0 || wv + NW * j < NV; };
   // the list entry is read at a clamped index (no branch, no wait)
@@ -230,6 +166,48 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
       for (int j = 0; j < JV; ++j) cells[JK + j] = has_v(j) ? a.csr_cell[min(base + rowv[j], it.c1 - 1)] : 0;
     }
   };
+  if constexpr (!SWA) {
+    cells_of(0, cfirst);
+    cells_of(1, cnext);
+  }
+
+  // this lane's query rows: row block b of wavefront w is rows
+  // 32 * (w * RB + b) .. +31, the lane owning row lane % 32 of it
+  int t_r[RB], h_r[RB], pos_lim[RB], pos_lo[RB], qseq[RB];
+  bool qvalid[RB];
+  SlotInfo si[RB];
+  bool any_row = false;
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int r = 32 * (w * RB + b) + (lane & 31);
+    const int hg = r / QT;
+    t_r[b] = r % QT;
+    qvalid[b] = t_r[b] < it.n_q;
+    si[b] = a.qslots[it.q_off + (qvalid[b] ? t_r[b] : 0)];
+    h_r[b] = kvh * G + hg;
+  }
+
+  // tiles of this item; trailing tiles in the future of every query are
+  // dropped, and with a sliding window leading tiles behind every query's
+  // window (tiles are walked from t0)
+  if (a.causal) ntile = wave_max_i(last) + 1;
+  const int win_lo = SWA ? it.qpos_min - a.swa + 1 : INT32_MIN;   // no query sees below this
+  int t0 = 0;
+  if constexpr (SWA) {
+    int first = ntile;
+    for (int k = lane; k < ntile; k += 64)
+      if (a.tile_max[tb + k] >= win_lo) first = min(first, k);
+    t0 = wave_min_i(first);
+    cells_of(t0, cfirst);
+    cells_of(t0 + 1, cnext);
+  }
+
+  // Everything a tile needs from memory is requested one tile (cell
+  // indices: two tiles) ahead and first read after the vmcnt(0) that opens
+  // that tile, so no wait inside a tile's compute covers the loads in flight
+  // (vmcnt retires in order: any wait would also wait for the next tile).
+  int pk = INT32_MAX, nmin = 0, nmax = 0;
+  uint64_t mk = 0;
   auto issue = [&](int tile, int bsel, const int* cells) {
     const int lim = it.c1 - (it.c0 + tile * KT);     // rows of this tile inside the list
 #pragma unroll
@@ -257,11 +235,87 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
     nmin = a.tile_min[tb + tile];
     nmax = a.tile_max[tb + tile];
   };
-  if (ntile > t0) {
-    int cfirst[JC];
-    cells_of(t0, cfirst);
-    issue(t0, 0, cfirst);
-    if (ntile > t0 + 1) cells_of(t0 + 1, cnext);
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    pos_lim[b] = a.causal ? si[b].pos : INT32_MAX - 1;     // largest visible cell position
+    pos_lo[b] = SWA ? si[b].pos - a.swa + 1 : INT32_MIN;   // smallest, with a sliding window
+    qseq[b] = si[b].seq0;
+    any_row |= qvalid[b];
+  }
+  const bool wave_rows = ballot(any_row) != 0ULL;   // wave-uniform: padding-only waves skip the math
+
+  // B operand of S^T = K Q^T: q[row][16*ks + 8*half + 0..7], scaled, F16.
+  // Loaded coalesced -- each wavefront instruction reads 1 KB of contiguous
+  // q (whole rows of D numbers: LPR lanes per row) -- converted, written to
+  // this wavefront's 32 rows of a staging area, and read back in the
+  // operand layout.  The staging area is ring buffer 1 (K half for waves 0
+  // and 1, V half for waves 2 and 3), unused until the tile loop's first
+  // barrier; each wavefront reads only the rows it wrote, so no barrier is
+  // needed here.  16 B segments are XOR-swizzled by row for the reads.
+  static_assert(RB == 1, "q staging assumes one 32-row block per wavefront");
+  half8 qb[RB][D / 16];
+  {
+    constexpr int LPR = D / 4;                     // lanes per row (16 B each)
+    constexpr int RPI = 64 / LPR;                  // rows per instruction
+    constexpr int SEG = D / 8;                     // 16 B segments per F16 row
+    _Float16* stg = (w < 2 ? &Ks[1][0] : &Vs[1][0]) + (w & 1) * 32 * D;
+    constexpr int NJ = 32 / RPI;                   // instructions per wavefront
+    const int p = lane % LPR;                      // this lane's 4 numbers: d = 4p .. 4p+3
+    // every load is issued before any is used: addresses first (a row past
+    // the item's queries reads its first row instead and is zeroed after)
+    const float* src[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int rr = j * RPI + lane / LPR;         // row of the wavefront's 32
+      const int r = 32 * w + rr;
+      int qrow = 0;                                // lane rr holds row rr's slot
+#pragma unroll
+      for (int k = 0; k < RPI; ++k) {
+        const int v = __builtin_amdgcn_readlane(si[0].q_row, j * RPI + k);
+        qrow = lane / LPR == k ? v : qrow;
+      }
+      src[j] = a.q[il] + static_cast<int64_t>(qrow) * H * D + (kvh * G + r / QT) * D + 4 * p;
+    }
+    float4 xs[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) xs[j] = *reinterpret_cast<const float4*>(src[j]);
+    // the first tile's gather goes out behind the q loads: waiting for q
+    // (in-order completion) then leaves the gather in flight
+    if (ntile > t0) issue(t0, 0, cfirst);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int rr = j * RPI + lane / LPR;
+      const bool ok = (32 * w + rr) % QT < it.n_q;
+      const float4 x = ok ? xs[j] : make_float4(0, 0, 0, 0);
+      half4 h4;
+      h4[0] = static_cast<_Float16>(x.x * a.scale_log2e);
+      h4[1] = static_cast<_Float16>(x.y * a.scale_log2e);
+      h4[2] = static_cast<_Float16>(x.z * a.scale_log2e);
+      h4[3] = static_cast<_Float16>(x.w * a.scale_log2e);
+      const int sgw = (p >> 1) ^ (rr & (SEG - 1));
+      *reinterpret_cast<half4*>(stg + rr * D + sgw * 8 + (p & 1) * 4) = h4;
+    }
+    const int rl = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int sgr = (2 * ks + half_id) ^ (rl & (SEG - 1));
+      qb[0][ks] = *reinterpret_cast<const half8*>(stg + rl * D + sgr * 8);
+    }
+  }
+
+  floatx16 oacc[RB][DP / 32];
+  // l_run: this lane's share of each row's sum (its 16 cells of every
+  // 32-cell block); lanes l and l ^ 32 always hold the same running maximum,
+  // so the two shares are rescaled alike and added once at the end
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    m_run[b] = -INFINITY;
+    l_run[b] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[b][db][i] = 0.f;
   }
 
   const int s16 = lane & 15;
@@ -447,13 +501,18 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   }
 }
 
+template <int D, int G, bool SWA>
+static void mfma_launch_swa(const AttnArgs& a, int n_il, hipStream_t s) {
+  constexpr int RB = kMfmaRowBlocks;
+  hipLaunchKernelGGL((k_attn_mfma<D, G, SWA, RB>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256 / RB), 0, s, a);
+}
+
 template <int D, int G>
 static void mfma_launch(const AttnArgs& a, int n_il, hipStream_t s) {
-  constexpr int RB = kMfmaRowBlocks;
   if (a.swa > 0)
-    hipLaunchKernelGGL((k_attn_mfma<D, G, true, RB>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256 / RB), 0, s, a);
+    mfma_launch_swa<D, G, true>(a, n_il, s);
   else
-    hipLaunchKernelGGL((k_attn_mfma<D, G, false, RB>), dim3(a.n_items * a.n_head_kv, n_il), dim3(256 / RB), 0, s, a);
+    mfma_launch_swa<D, G, false>(a, n_il, s);
 }
 
 template <int D>

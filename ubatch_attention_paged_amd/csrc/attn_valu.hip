@@ -57,9 +57,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   const int il = blockIdx.x % n_il;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int kvh = lane / LPH, part = lane % LPH;
-  const int qslot = a.qlist[it.q_off];
-  const SlotInfo si = a.slots[qslot];
-  const bool check_mask = !a.classes[it.cls].pure;
+  const SlotInfo si = a.qslots[it.q_off];
+  const bool check_mask = !it.pure;
   const _Float16* __restrict__ Kl = a.k[il];
   const _Float16* __restrict__ Vl = a.v[il];
 

@@ -624,7 +624,7 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
           const int32_t q = P.qlist[c.q_off + t];
           for (int32_t a = 0; a < c.n_cells; a += len) {
             WorkItem it{ci, c.q_off + t, 1, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + len), -1,
-                        P.slots[q].pos, P.slots[q].pos};
+                        P.slots[q].pos, P.slots[q].pos, c.tile_base + a / kTileCells, c.stream, c.pure, 0};
             pend.push_back({it, true});
             ++coverage[q];
           }
@@ -642,7 +642,7 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
           }
           for (int32_t a = 0; a < c.n_cells; a += ch) {
             WorkItem it{ci, c.q_off + t0, nq, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + ch), -1,
-                        pmin, pmax};
+                        pmin, pmax, c.tile_base + a / kTileCells, c.stream, c.pure, 0};
             pend.push_back({it, false});
             for (int32_t t = 0; t < nq; ++t) ++coverage[P.qlist[c.q_off + t0 + t]];
           }

@@ -55,7 +55,7 @@ struct AttnArgs {
   const _Float16* v[kMaxLayersPerLaunch];
   const SlotInfo* slots;
   const ClassInfo* classes;
-  const int32_t* qlist;
+  const SlotInfo* qslots;     // the query slots of each class, in class order (WorkItem::q_off)
   const WorkItem* items;
   const int32_t* csr_cell;
   const int32_t* csr_pos;

@@ -77,16 +77,22 @@ struct ClassInfo {
 
 struct WorkItem {        // one workgroup (per KV head for the MFMA kernel)
   int32_t cls;
-  int32_t q_off;         // queries qlist[q_off .. q_off + n_q)
+  int32_t q_off;         // queries qslots[q_off .. q_off + n_q)
   int32_t n_q;
   int32_t c0, c1;        // csr range [c0, c1)
   int32_t prow;          // first partial row, -1 = write the output directly
   int32_t qpos_min, qpos_max;
+  // copies of the class's fields, so a workgroup's first loads depend on
+  // the item alone
+  int32_t tile_base;     // the class's first entry in the per-tile tables
+  int32_t stream;
+  int32_t pure;
+  int32_t pad;
 };
 
 // Byte offsets of each plan array inside the device plan arena.
 struct PlanLayout {
-  int64_t slots, classes, lookup, lookup_off, qlist, items_valu, items_mfma;
+  int64_t slots, classes, lookup, lookup_off, qslots, items_valu, items_mfma;
   int64_t red_slot, red_off, red_rows, updates;
   int64_t total;
 };
