@@ -70,6 +70,10 @@ template <bool B>
 struct BoolTag {
   static constexpr bool value = B;
 };
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
 
 // SWA: the sliding-window variant (a.swa > 0); the other compiles without any
 // of its tests
@@ -156,14 +160,20 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   int cfirst[JC], cnext[JC];                       // raw list entries; validity is decided at use
   auto has_k = [&](int j) { return NK % NW == 0 || wv + NW * j < NK; };   // wave-uniform
   auto has_v = [&](int j) { return NV % NW == 0 || wv + NW * j < NV; };
-  // the list entry is read at a clamped index (no branch, no wait)
+  // list entries through a range-checked buffer over [0, c1): an entry past
+  // the item's end reads as cell 0, and its row is never gathered (see
+  // issue); 32-bit offsets, no clamp, no branch
+  const __amdgpu_buffer_rsrc_t cellr =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(a.csr_cell), 0, it.c1 * 4, 0x00020000);
   auto cells_of = [&](int tile, int* cells) {
     const int base = it.c0 + tile * KT;
 #pragma unroll
-    for (int j = 0; j < JK; ++j) cells[j] = has_k(j) ? a.csr_cell[min(base + rowk[j], it.c1 - 1)] : 0;
+    for (int j = 0; j < JK; ++j)
+      cells[j] = has_k(j) ? __builtin_amdgcn_raw_buffer_load_b32(cellr, (base + rowk[j]) * 4, 0, 0) : 0;
     if constexpr (!SAME_ROWS) {
 #pragma unroll
-      for (int j = 0; j < JV; ++j) cells[JK + j] = has_v(j) ? a.csr_cell[min(base + rowv[j], it.c1 - 1)] : 0;
+      for (int j = 0; j < JV; ++j)
+        cells[JK + j] = has_v(j) ? __builtin_amdgcn_raw_buffer_load_b32(cellr, (base + rowv[j]) * 4, 0, 0) : 0;
     }
   };
   if constexpr (!SWA) {
@@ -210,21 +220,23 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   uint64_t mk = 0;
   auto issue = [&](int tile, int bsel, const int* cells) {
     const int lim = it.c1 - (it.c0 + tile * KT);     // rows of this tile inside the list
+    // a whole tile inside the list (wave-uniform) needs no per-row test;
+    // V rows need the padding test only below head size 32
+    const bool whole = lim >= KT;
 #pragma unroll
     for (int j = 0; j < JK; ++j)
       if (has_k(j)) {
-        const uint32_t off =
-            rowk[j] < lim ? sbase_bytes + static_cast<uint32_t>(cells[j]) * row_bytes + colk[j] : kOobOffset;
-        buffer_load16_lds(krw, lds_addr(&Ks[bsel][(wv + NW * j) * 512]), off);
+        const uint32_t at = sbase_bytes + static_cast<uint32_t>(cells[j]) * row_bytes + colk[j];
+        buffer_load16_lds(krw, lds_addr(&Ks[bsel][(wv + NW * j) * 512]), whole || rowk[j] < lim ? at : kOobOffset);
       }
 #pragma unroll
     for (int j = 0; j < JV; ++j)
       if (has_v(j)) {
         const int cl = SAME_ROWS ? cells[j] : cells[JK + j];
-        const uint32_t off = rowv[j] < lim && colv[j] != kOobOffset
-                                 ? sbase_bytes + static_cast<uint32_t>(cl) * row_bytes + colv[j]
-                                 : kOobOffset;
-        buffer_load16_lds(vrw, lds_addr(&Vs[bsel][(wv + NW * j) * 512]), off);
+        const uint32_t at = sbase_bytes + static_cast<uint32_t>(cl) * row_bytes + colv[j];
+        const bool pad = SV != SK && colv[j] == kOobOffset;
+        buffer_load16_lds(vrw, lds_addr(&Vs[bsel][(wv + NW * j) * 512]),
+                          !pad && (whole || rowv[j] < lim) ? at : kOobOffset);
       }
     if (tid < KT) {
       const int idx = it.c0 + tile * KT + tid;
@@ -327,10 +339,13 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   // every row belongs to) visibility is the position test alone, otherwise
   // each cell's set membership is tested too.  Purity is per work item, so
   // the branch is taken once, outside the loop.
+  // The walk is unrolled by two tiles so that the ring buffer of each tile
+  // is a compile-time constant: every LDS address is then a loop-invariant
+  // per-lane offset plus an immediate, with no address arithmetic per tile.
   auto tile_loop = [&](auto pure_tag) {
   constexpr bool PURE = decltype(pure_tag)::value;
-  for (int i = t0; i < ntile; ++i) {
-    const int buf = SWA ? (i - t0) & 1 : i & 1;
+  auto tile = [&](const int i, auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     // stage tile i: its rows arrived by the LDS-direct loads this thread
     // issued (vmcnt), positions and masks go through registers
     if (tid < KT) {
@@ -346,11 +361,11 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
       issue(i + 1, buf ^ 1, cnext);
       if (i + 2 < ntile) cells_of(i + 2, cnext);
     }
-    if (!wave_rows) continue;
+    if (!wave_rows) return;
 
     const int nk = min(KT, it.c1 - (it.c0 + i * KT));
-    if (a.causal && tmin > it.qpos_max) continue;
-    if (SWA && tmax < win_lo) continue;
+    if (a.causal && tmin > it.qpos_max) return;
+    if (SWA && tmax < win_lo) return;
     const bool full = nk == KT && PURE && (!a.causal || tmax <= it.qpos_min) &&
                       (!SWA || tmin >= it.qpos_max - a.swa + 1);
 
@@ -456,6 +471,11 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int b = 0; b < RB; ++b) weights(b, s1[b], mu[b], p1[b]);
     pv_block(1, p1);
+  };
+  // tile t0 + 2k sits in buffer 0, t0 + 2k + 1 in buffer 1
+  for (int i = t0; i < ntile; i += 2) {
+    tile(i, IntTag<0>{});
+    if (i + 1 < ntile) tile(i + 1, IntTag<1>{});
   }
   };
   if (pure)
