@@ -678,6 +678,28 @@ def trace_stats(csv_path, kernel, skip, take):
                 min_ns=int(a.min()), max_ns=int(a.max()), median_ns=float(np.median(a)))
 
 
+def counter_stats(csv_path, kernel, skip, take):
+    """Mean per dispatch of every counter in a rocprofv3 --pmc
+    counter_collection.csv, over the dispatches of ``kernel`` (same
+    selection as trace_stats)."""
+    import csv
+    per = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            name = name[5:] if name.startswith("void ") else name
+            if name.split("(")[0].split("<")[0].split("::")[-1] != kernel:
+                continue
+            d = per.setdefault(int(row["Dispatch_Id"]), {})
+            d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    ids = sorted(per)[skip:skip + take if take else None]
+    if not ids:
+        raise SystemExit(f"no dispatches of {kernel} left after skipping {skip} of {len(per)}")
+    names = sorted({k for i in ids for k in per[i]})
+    return dict(kernel=kernel, dispatches_total=len(per), skipped=skip, n=len(ids),
+                mean=dict((k, float(np.mean([per[i].get(k, 0.0) for i in ids]))) for k in names))
+
+
 KERNEL_SOURCES = {"k_attn_mfma": "attn_mfma.hip", "k_attn_valu": "attn_valu.hip", "k_attn_reduce": "attn_valu.hip",
                   "k_store_commit": "kernels_commit.hip", "k_store": "kernels_commit.hip"}
 
@@ -749,7 +771,10 @@ def main():
     ap.add_argument("--trace-stats", metavar="CSV",
                     help="no GPU: statistics of one kernel's dispatches in a rocprofv3 kernel_trace.csv, "
                          "skipping the first --skip (warm-up) and taking the next --take (the timed loop)")
-    ap.add_argument("--kernel", help="with --trace-stats: kernel name prefix (e.g. k_attn_mfma)")
+    ap.add_argument("--counter-stats", metavar="CSV",
+                    help="no GPU: per-dispatch means of the counters in a rocprofv3 --pmc counter_collection.csv "
+                         "for --kernel, with the same --skip / --take selection")
+    ap.add_argument("--kernel", help="with --trace-stats / --counter-stats: kernel name (e.g. k_attn_mfma)")
     ap.add_argument("--skip", type=int, default=0)
     ap.add_argument("--take", type=int, default=0)
     ap.add_argument("--leg", help="with --trace-stats: record the result under this leg in --trace-out")
@@ -765,6 +790,9 @@ def main():
     ap.add_argument("--decode-workload", choices=["cb_decode", "prefix_decode"], action="append",
                     help="restrict the decode runs to this workload (repeatable)")
     args = ap.parse_args()
+    if args.counter_stats:
+        print(json.dumps(counter_stats(args.counter_stats, args.kernel, args.skip, args.take)), flush=True)
+        return
     if args.trace_stats:
         rec = trace_stats(args.trace_stats, args.kernel, args.skip, args.take)
         print(json.dumps(rec), flush=True)

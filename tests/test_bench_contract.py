@@ -84,3 +84,20 @@ def test_trace_stats_skips_warmup_dispatches(tmp_path):
     assert (r["n"], r["dispatches_total"], r["min_ns"], r["max_ns"]) == (4, 10, 103, 106)
     assert r["avg_ns"] == 104.5
     assert bench.trace_stats(str(p), "k_store_commit", 0, 0)["n"] == 10
+
+
+def test_counter_stats_average_per_dispatch(tmp_path):
+    """--counter-stats sums a kernel's counter rows per dispatch (rocprofv3
+    may report one row per XCD) and averages over the selected dispatches."""
+    import bench
+    hdr = '"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value"\n'
+    rows = []
+    for i in range(6):
+        for part in (1.0, 2.0):       # two rows per dispatch and counter
+            rows.append(f'{i},"void kvattn::k_attn_valu<128, 2>(kvattn::AttnArgs)","FETCH_SIZE",{part * (i + 1)}\n')
+        rows.append(f'{i},"kvattn::k_store(kvattn::StoreArgs)","FETCH_SIZE",1000.0\n')
+    p = tmp_path / "c.csv"
+    p.write_text(hdr + "".join(rows))
+    r = bench.counter_stats(str(p), "k_attn_valu", 2, 3)
+    assert r["n"] == 3 and r["dispatches_total"] == 6
+    assert abs(r["mean"]["FETCH_SIZE"] - 3.0 * (3 + 4 + 5) / 3) < 1e-9
