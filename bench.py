@@ -639,9 +639,9 @@ def kernel_source_digest(source):
 def committed_trace_ms(kernel, source, leg):
     """Mean duration (ms) of ``kernel`` over the timed dispatches of ``leg``
     from the committed rocprofv3 kernel-trace summary (profiles/
-    <kernel>_trace.json, taken with --selected-regions around exactly the
-    loop the HIP events time); None when absent or the kernel's sources
-    changed since."""
+    <kernel>_trace.json: the dispatches of exactly the loop the HIP events
+    time, picked out of the whole run's trace by --trace-stats --skip /
+    --take); None when absent or the kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_trace.json")
     try:
         rec = json.load(open(path))
@@ -654,28 +654,63 @@ def committed_trace_ms(kernel, source, leg):
     return legs[leg]["avg_ns"] * 1e-6
 
 
+def _trace_rows(csv_path):
+    """(dispatch id, bare kernel name, full name, duration ns) of every
+    dispatch in a rocprofv3 kernel_trace.csv, in dispatch order."""
+    import csv
+    out = []
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            bare = (name[5:] if name.startswith("void ") else name).split("(")[0].split("<")[0].split("::")[-1]
+            out.append((int(row["Dispatch_Id"]), bare, name, int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+    out.sort()
+    return out
+
+
 def trace_stats(csv_path, kernel, skip, take):
     """Duration statistics of the dispatches of ``kernel`` (name prefix, after
     an optional "void " and namespace) in a rocprofv3 kernel_trace.csv, in
     dispatch order: the first ``skip`` are dropped (warm-up), the next
     ``take`` kept (0 = all the rest)."""
-    import csv
-    durs = []
-    with open(csv_path, newline="") as f:
-        for row in csv.DictReader(f):
-            name = row["Kernel_Name"]
-            name = name[5:] if name.startswith("void ") else name
-            bare = name.split("(")[0].split("<")[0].split("::")[-1]
-            if bare != kernel:
-                continue
-            durs.append((int(row["Dispatch_Id"]), int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
-    durs.sort()
-    sel = [d for _, d in durs[skip:skip + take if take else None]]
+    durs = [d for _, bare, _, d in _trace_rows(csv_path) if bare == kernel]
+    sel = durs[skip:skip + take if take else None]
     if not sel:
         raise SystemExit(f"no dispatches of {kernel} left after skipping {skip} of {len(durs)}")
     a = np.asarray(sel, dtype=np.float64)
     return dict(kernel=kernel, dispatches_total=len(durs), skipped=skip, n=len(sel), avg_ns=round(float(a.mean()), 1),
                 min_ns=int(a.min()), max_ns=int(a.max()), median_ns=float(np.median(a)))
+
+
+def trace_table(csv_path, kernel, skip, take, step_start):
+    """Per-kernel calls / mean / total of every dispatch in the steps that
+    hold the selected dispatches of ``kernel``: a step begins at a dispatch
+    of ``step_start`` (the first kernel each step launches; several names
+    joined by commas) and the window ends before the next step's first
+    dispatch, the next dispatch of ``kernel`` or the first kernel of another
+    library (the next bench leg)."""
+    rows = _trace_rows(csv_path)
+    starts = set(step_start.split(","))
+    idx = [i for i, r in enumerate(rows) if r[1] == kernel]
+    sel = idx[skip:skip + take if take else None]
+    if not sel:
+        raise SystemExit(f"no dispatches of {kernel} left after skipping {skip} of {len(idx)}")
+    a = sel[0]
+    while a > 0 and rows[a][1] not in starts:
+        a -= 1
+    b = sel[-1] + 1
+    while b < len(rows) and "kvattn::" in rows[b][2] and rows[b][1] not in starts and rows[b][1] != kernel:
+        b += 1
+    stats = {}
+    for _, _, name, d in rows[a:b]:
+        s = stats.setdefault(name, [0, 0])
+        s[0] += 1
+        s[1] += d
+    total = sum(v[1] for v in stats.values())
+    lines = [f"{'kernel':<64}{'calls':>7}{'avg_us':>10}{'total_ms':>10}{'pct':>7}"]
+    for name, (c, d) in sorted(stats.items(), key=lambda kv: -kv[1][1]):
+        lines.append(f"{name[:62]:<64}{c:>7}{d / c / 1e3:>10.2f}{d / 1e6:>10.3f}{100 * d / total:>7.2f}")
+    return "\n".join(lines)
 
 
 def counter_stats(csv_path, kernel, skip, take):
@@ -700,23 +735,26 @@ def counter_stats(csv_path, kernel, skip, take):
                 mean=dict((k, float(np.mean([per[i].get(k, 0.0) for i in ids]))) for k in names))
 
 
+PROFILE_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> "
+                   "-o run -- python -u <repo>/bench.py --gpus 1 --steps 20 --warmup 5 --no-cpu-baseline")
+
 KERNEL_SOURCES = {"k_attn_mfma": "attn_mfma.hip", "k_attn_valu": "attn_valu.hip", "k_attn_reduce": "attn_valu.hip",
                   "k_store_commit": "kernels_commit.hip", "k_store": "kernels_commit.hip"}
 
 
-def write_trace_record(path, kernel, leg, rec, argv):
+def write_trace_record(path, kernel, leg, rec, argv, profile_command):
     """Merge one leg's statistics into the per-kernel summary JSON, with the
     digest of the kernel's sources as they are now (run it in the tree that
-    was profiled)."""
+    was profiled) and the rocprofv3 command whose trace it summarises."""
     try:
         out = json.load(open(path))
     except (OSError, ValueError):
         out = {}
     out["kernel"] = kernel
     out["source_digest"] = kernel_source_digest(KERNEL_SOURCES[kernel])
-    out["profile_command"] = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o run -- "
-                              "python -u <repo>/bench.py --gpus 1 --steps 20 --warmup 5 --no-cpu-baseline")
-    out.setdefault("legs", {})[leg] = dict(rec, summary_command=f"python bench.py {argv}".replace(ROOT + "/", ""))
+    out.pop("profile_command", None)
+    out.setdefault("legs", {})[leg] = dict(rec, profile_command=profile_command,
+                                           summary_command=f"python bench.py {argv}".replace(ROOT + "/", ""))
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
 
@@ -779,6 +817,11 @@ def main():
     ap.add_argument("--take", type=int, default=0)
     ap.add_argument("--leg", help="with --trace-stats: record the result under this leg in --trace-out")
     ap.add_argument("--trace-out", metavar="JSON", help="with --trace-stats: merge the result into this file")
+    ap.add_argument("--profile-command", default=PROFILE_COMMAND,
+                    help="with --trace-out: the rocprofv3 command that wrote the trace, recorded beside the leg")
+    ap.add_argument("--table", metavar="STEP_START",
+                    help="with --trace-stats: print every kernel of the steps that hold the selected dispatches, "
+                         "a step beginning at a dispatch of the kernel STEP_START (comma-separated names)")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the decode workloads (for profiling their kernels alone)")
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed prefill + decode workload")
@@ -793,11 +836,18 @@ def main():
     if args.counter_stats:
         print(json.dumps(counter_stats(args.counter_stats, args.kernel, args.skip, args.take)), flush=True)
         return
+    if args.trace_stats and args.table:
+        print(trace_table(args.trace_stats, args.kernel, args.skip, args.take, args.table), flush=True)
+        return
     if args.trace_stats:
         rec = trace_stats(args.trace_stats, args.kernel, args.skip, args.take)
         print(json.dumps(rec), flush=True)
         if args.trace_out:
-            write_trace_record(args.trace_out, args.kernel, args.leg, rec, " ".join(sys.argv[1:]))
+            argv = [a for a in sys.argv[1:]]
+            if "--profile-command" in argv:
+                k = argv.index("--profile-command")
+                del argv[k:k + 2]
+            write_trace_record(args.trace_out, args.kernel, args.leg, rec, " ".join(argv), args.profile_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the attention path is not "

@@ -101,3 +101,34 @@ def test_counter_stats_average_per_dispatch(tmp_path):
     r = bench.counter_stats(str(p), "k_attn_valu", 2, 3)
     assert r["n"] == 3 and r["dispatches_total"] == 6
     assert abs(r["mean"]["FETCH_SIZE"] - 3.0 * (3 + 4 + 5) / 3) < 1e-9
+
+
+def test_trace_table_covers_whole_steps(tmp_path):
+    """--table lists every kernel of the steps holding the selected
+    dispatches: from the step's first kernel to just before the next step,
+    without the next bench leg's kernels."""
+    import bench
+    hdr = '"Kind","Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp"\n'
+    rows, d = [], 0
+
+    def add(name, dur):
+        nonlocal d
+        d += 1
+        rows.append(f'"KERNEL_DISPATCH",{d},"{name}",{10 ** 6 * d},{10 ** 6 * d + 1000 * dur}\n')
+    for step in range(5):
+        add("kvattn::k_apply_updates(kvattn::CsrArgs, long)", 4)
+        add("kvattn::k_store(kvattn::StoreArgs)", 5)
+        add("void kvattn::k_attn_mfma<128, 2, false, 1>(kvattn::AttnArgs)", 50)
+        add("void kvattn::k_attn_valu<128, 2>(kvattn::AttnArgs)", 100 + step)
+        add("kvattn::k_attn_reduce(kvattn::AttnArgs, int)", 10)
+    add("void at::native::vectorized_elementwise_kernel<8>(int)", 7)
+    p = tmp_path / "t.csv"
+    p.write_text(hdr + "".join(rows))
+    t = bench.trace_table(str(p), "k_attn_valu", 2, 3, "k_apply_updates")
+    lines = t.splitlines()[1:]
+    calls = {ln[:62].strip(): int(ln[64:71]) for ln in lines}
+    assert len(lines) == 5 and all(c == 3 for c in calls.values()), t
+    assert "vectorized" not in t
+    # the mean of the selected valu dispatches only (steps 2, 3, 4)
+    valu = [ln for ln in lines if "k_attn_valu" in ln][0]
+    assert float(valu[71:81]) == 103.0
