@@ -81,19 +81,44 @@ def make_ctx(wl, dev, layer_chunk):
 class Runner:
     """Drives measured batches through the library with HIP events around
     every attend call (on torch's current stream, where the library
-    launches)."""
+    launches) and, when ``kernel`` names one of the attend call's kernels
+    (KVATTN_KERNEL_*), a second pair per call that the library binds to that
+    kernel's own start and end (hipExtLaunchKernel): its execution time
+    alone, without the stream's gaps around it."""
 
-    def __init__(self, ctx, layer_chunk):
+    def __init__(self, ctx, layer_chunk, kernel=None):
         self.ctx = ctx
         self.chunk = layer_chunk
+        self.kernel = kernel
         self.attend_ms = []
+        self.kernel_ev = []
+        self._pool = []
+        self.calls = 0
         self.store_calls = 0
+
+    def reserve(self, n):
+        """Create n kernel-event pairs before the timed region (torch creates
+        a HIP event at its first record; the library re-records it)."""
+        import torch
+        if self.kernel is None:
+            return
+        while len(self._pool) < n:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            e1.record()
+            self._pool.append((e0, e1))
+        torch.cuda.synchronize()
+
+    def _kernel_pair(self):
+        if not self._pool:
+            self.reserve(1)
+        return self._pool.pop()
 
     def run_batch(self, n, pos, seqs, out_flags, K, V, Q, outs, timed):
         """K, V, Q: [layers][n][width] fp32 device tensors in batch order;
         outs: [layers][>= n_ubatch][n_head*head_dim]."""
         import torch
-        from ubatch_attention_paged_amd import kvattn_store, kvattn_attend
+        from ubatch_attention_paged_amd import kvattn_store, kvattn_attend, kvattn_time_next_attend
         ctx = self.ctx
         st, ubs, _ = ctx.split(n, pos, seqs, out_flags)
         if st != 0:
@@ -110,7 +135,12 @@ class Runner:
             for a in range(0, L, self.chunk):
                 b = min(L, a + self.chunk)
                 kvattn_store(ctx.ctx, ub, a, row_ptrs(Kb, a, b, r0), row_ptrs(Vb, a, b, r0), stream)
+                self.calls += 1
                 if timed:
+                    if self.kernel is not None:
+                        k0, k1 = self._kernel_pair()
+                        kvattn_time_next_attend(ctx.ctx, self.kernel, k0.cuda_event, k1.cuda_event)
+                        self.kernel_ev.append((k0, k1))
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record()
@@ -125,6 +155,13 @@ class Runner:
         torch.cuda.synchronize()
         vals = [a.elapsed_time(b) for a, b in self.attend_ms]
         return float(np.mean(vals)) if vals else float("nan"), len(vals)
+
+    def kernel_avg_ms(self):
+        """Mean execution time of the timed kernel over the timed calls."""
+        import torch
+        torch.cuda.synchronize()
+        vals = [a.elapsed_time(b) for a, b in self.kernel_ev]
+        return float(np.mean(vals)) if vals else None
 
     def attend_by_position(self, per_step):
         """Mean attend time of the k-th attend call of a step, k < per_step."""
@@ -151,7 +188,8 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
     sids = [SeqIds(bt.seq_ids) for bt in wl.batches]
     HD = wl.n_head * wl.head_dim
     outs = torch.empty((len(layers), wl.n_ubatch, HD), dtype=torch.float32, device=dev)
-    runner = Runner(ctx, layer_chunk)
+    from ubatch_attention_paged_amd import KVATTN_KERNEL_MFMA
+    runner = Runner(ctx, layer_chunk, kernel=KVATTN_KERNEL_MFMA)
 
     def step(timed):
         ctx.seq_rm(-1)                          # retire the previous request
@@ -161,6 +199,7 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
 
     for _ in range(warmup):
         step(False)
+    runner.reserve(steps * runner.calls // max(1, warmup))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -184,7 +223,7 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
             f"{ms:.3f} ms {f / (ms * 1e-3) / 1e12:.0f} TF/s" for ms, f in zip(per_ub, ub_flops)))
     res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens=wl.measured_tokens(),
                flops_step=flops_step, attend_launches_per_step=n_ub_step, attend_avg_ms=avg_ms,
-               attend_ms_per_step=avg_ms * n_ub_step, last_plan=stats)
+               attend_ms_per_step=avg_ms * n_ub_step, kernel_avg_ms=runner.kernel_avg_ms(), last_plan=stats)
     ctx.close()
     return res
 
@@ -229,11 +268,13 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
     sid = SeqIds(bt.seq_ids)
     HD = wl.n_head * wl.head_dim
     outs = torch.empty((len(layers), bt.n_tokens, HD), dtype=torch.float32, device=dev)
-    runner = Runner(ctx, layer_chunk)
+    from ubatch_attention_paged_amd import KVATTN_KERNEL_VALU
+    runner = Runner(ctx, layer_chunk, kernel=KVATTN_KERNEL_VALU)
     t = 0
     for _ in range(warmup):
         runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, False)
         t += 1
+    runner.reserve(steps * runner.calls // max(1, warmup))
     torch.cuda.synchronize()
     t_first = t
     t0 = time.perf_counter()
@@ -254,6 +295,7 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
     res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens_per_step=bt.n_tokens,
                tokens_per_s=bt.n_tokens * steps / wall, unique_cells=float(cells),
                kv_bytes_step=kv_bytes, qo_bytes_step=qo_bytes, attend_avg_ms=avg_ms,
+               kernel_avg_ms=runner.kernel_avg_ms(),
                attend_launches_per_step=launches, kv_read_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
                kv_qo_gbs=(kv_bytes + qo_bytes) / launches / (avg_ms * 1e-3) / 1e9, plan=ctx.plan_stats())
     ctx.close()
@@ -879,10 +921,13 @@ def main():
     pre = bench_prefill(wl, dev, args.steps, args.warmup, args.layer_chunk)
     tok_s = pre["tokens"] * args.steps / pre["wall_s"]
     per_launch_flop = pre["flops_step"] / pre["attend_launches_per_step"]
-    mfma_tf = per_launch_flop / (pre["attend_avg_ms"] * 1e-3) / 1e12
+    # the kernel's own execution time (events bound to its launch); the
+    # events around the whole attend call also hold the stream's gaps
+    kern_ms = pre["kernel_avg_ms"] if pre["kernel_avg_ms"] is not None else pre["attend_avg_ms"]
+    mfma_tf = per_launch_flop / (kern_ms * 1e-3) / 1e12
     log(f"[bench] prefill: {tok_s:,.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
-        f"attend {pre['attend_avg_ms']:.3f} ms/launch x {pre['attend_launches_per_step']:.0f}, "
-        f"{mfma_tf:.1f} TFLOP/s")
+        f"attend {pre['attend_avg_ms']:.3f} ms/call x {pre['attend_launches_per_step']:.0f}, "
+        f"kernel {kern_ms:.4f} ms, {mfma_tf:.1f} TFLOP/s")
     line = {
         "metric": "ubatch attention tokens/s + decode KV-read GB/s (% HBM peak), 1xMI355X",
         "value": round(tok_s, 1),
@@ -907,7 +952,9 @@ def main():
                      "traffic": committed_traffic("k_attn_mfma", "attn_mfma.hip"),
                      "per_launch": f"{per_launch_flop / 1e9:.2f} GFLOP "
                                    f"(4*H*d per visible (query, cell) pair x 28 layers of one ubatch)",
-                     "event_avg_ms": round(pre["attend_avg_ms"], 4)},
+                     "event_avg_ms": round(kern_ms, 4),
+                     "event_kind": "kernel execution (hipExtLaunchKernel start/stop events, every timed launch)",
+                     "call_event_avg_ms": round(pre["attend_avg_ms"], 4)},
     }
     trace_ms = committed_trace_ms("k_attn_mfma", "attn_mfma.hip", "prefill")
     if trace_ms is not None:
@@ -924,6 +971,7 @@ def main():
             "tokens_per_s": round(pl["tokens"] * ps / pl["wall_s"], 1), "ms_per_step": round(pl["ms_per_step"], 4),
             "attend_launches_per_step": round(pl["attend_launches_per_step"], 1),
             "attend_us_per_launch": round(1e3 * pl["attend_avg_ms"], 2),
+            "mfma_kernel_us_per_launch": round(1e3 * pl["kernel_avg_ms"], 2),
             "attend_ms_per_step": round(pl["attend_ms_per_step"], 4),
             "tflops_attend": round(pre["flops_step"] / (pl["attend_ms_per_step"] * 1e-3) / 1e12, 1)}}
         log(f"[bench] prefill, one call per layer: {line['per_layer_calls']['prefill']}")
@@ -939,6 +987,7 @@ def main():
                          "kv_bytes_per_step": round(r["kv_bytes_step"]), "qo_bytes_per_step": round(r["qo_bytes_step"]),
                          "kv_qo_gbs": round(r["kv_qo_gbs"], 1),
                          "attend_avg_ms": round(r["attend_avg_ms"], 4),
+                         "valu_kernel_avg_ms": round(r["kernel_avg_ms"], 4),
                          "unique_cells_per_step": r["unique_cells"], "plan": r["plan"]}
             if name == "cb_decode" and not args.no_per_layer:
                 rp = bench_decode(w, dev, args.steps, args.warmup, 1)
@@ -946,6 +995,7 @@ def main():
                     "tokens_per_s": round(rp["tokens_per_s"], 1), "ms_per_step": round(rp["ms_per_step"], 4),
                     "attend_launches_per_step": round(rp["attend_launches_per_step"], 1),
                     "attend_us_per_launch": round(1e3 * rp["attend_avg_ms"], 2),
+                    "valu_kernel_us_per_launch": round(1e3 * rp["kernel_avg_ms"], 2),
                     "kv_read_gbs": round(rp["kv_read_gbs"], 1), "hbm_frac": round(rp["hbm_frac"], 4)}
                 log(f"[bench] cb_decode, one call per layer: {line['per_layer_calls']['cb_decode']}")
             if name == "cb_decode":

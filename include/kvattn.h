@@ -228,6 +228,26 @@ int kvattn_attend_noalloc(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0,
 
 /* ---- diagnostics (tests and benchmarks) ---------------------------------- */
 
+/* The kernels of one attend call, for kvattn_time_next_attend. */
+#define KVATTN_KERNEL_MFMA 0   /* matrix-core tile kernel (query blocks of 32+ rows) */
+#define KVATTN_KERNEL_VALU 1   /* vector-ALU kernel (short query blocks, decode) */
+#define KVATTN_KERNEL_MERGE 2  /* split-K merge of partial results */
+
+/* Kernel timing for benchmarks and profilers (not an operation of the
+ * method).  The next kvattn_attend or kvattn_attend_noalloc call on this
+ * context launches kernel `kind` with hipExtLaunchKernel, which stamps
+ * start_event with that kernel's own start time and stop_event with its end
+ * time (kernel execution only, not the time the stream reached them).
+ * When the call cuts its layers into several launches, start_event belongs
+ * to the first and stop_event to the last.  Both are hipEvent_t created by
+ * the caller on the context's device; the library keeps neither beyond the
+ * next attend call, which uses the setting once and clears it.  A call that
+ * launches no kernel of that kind records both events back to back on its
+ * stream (elapsed time about zero); a call that fails before launching
+ * records neither.  kind < 0 disarms.  KVATTN_EINVAL for an unknown kind or
+ * a NULL event. */
+int kvattn_time_next_attend(kvattn_ctx *ctx, int32_t kind, void *start_event, void *stop_event);
+
 /* HOST-ONLY.  n_kv reported for the current state ("llama.cpp and the
  * ubatch", "Prefill and decode are not the same shape"). */
 int32_t kvattn_n_kv(const kvattn_ctx *ctx);

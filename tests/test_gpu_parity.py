@@ -313,6 +313,64 @@ def test_repeat_store_attend_is_idempotent():
     ctx.close()
 
 
+@pytest.mark.parametrize("name", ["prefix", "cb_decode"])
+def test_kernel_timing_events_change_nothing(name):
+    """Arming kernel timing (hipExtLaunchKernel start/stop events) leaves the
+    results bit-identical; a timed kernel's elapsed time is positive and
+    within the events around the whole call; a kind the call does not launch
+    gets both events back to back (about zero)."""
+    wl = small(name)
+    print(f"[gpu] kernel timing events {name}", flush=True)
+    ctx = make_ctx(wl)
+    dev = torch.device("cuda:0")
+    from tests.helpers import batch_tensors
+    layers = list(range(wl.n_layer))
+    checked = 0
+    for b, bt in enumerate(wl.batches):
+        t = batch_tensors(wl, b, layers, bt.measured)
+        Kt = [torch.from_numpy(t[(l, W.KIND_K)]).to(dev) for l in layers]
+        Vt = [torch.from_numpy(t[(l, W.KIND_V)]).to(dev) for l in layers]
+        st, ubs, _ = ctx.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        assert st == 0 and len(ubs) == 1
+        ub = ubs[0]
+        ctx.store(ub, 0, Kt, Vt)
+        if not bt.measured:
+            continue
+        Q = [torch.from_numpy(t[(l, W.KIND_Q)]).to(dev) for l in layers]
+        ref = [torch.empty_like(q) for q in Q]
+        ctx.attend(ub, 0, Q, ref)
+        stats = ctx.plan_stats()
+        launched = {K.KVATTN_KERNEL_MFMA: stats["n_items_mfma"] > 0, K.KVATTN_KERNEL_VALU: stats["n_items_valu"] > 0,
+                    K.KVATTN_KERNEL_MERGE: stats["n_reduced"] > 0}
+        for kind, has in launched.items():
+            k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            k0.record()
+            k1.record()                        # creates the HIP events
+            K.kvattn_time_next_attend(ctx.ctx, kind, k0.cuda_event, k1.cuda_event)
+            out = [torch.full_like(q, float("nan")) for q in Q]
+            c0.record()
+            ctx.attend(ub, 0, Q, out)
+            c1.record()
+            torch.cuda.synchronize()
+            for a, c in zip(ref, out):
+                assert torch.equal(a, c)
+            kt, ct = k0.elapsed_time(k1), c0.elapsed_time(c1)
+            print(f"  kind {kind} launched {has}: kernel {kt:.4f} ms, call {ct:.4f} ms", flush=True)
+            if has:
+                assert 0 < kt <= ct
+            else:
+                assert 0 <= kt < 0.05
+            checked += 1
+        # an untimed call afterwards is unaffected by the earlier arming
+        out = [torch.full_like(q, float("nan")) for q in Q]
+        ctx.attend(ub, 0, Q, out)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, c) for a, c in zip(ref, out))
+    assert checked == 3
+    ctx.close()
+
+
 def test_needles_on_gpu():
     """A dominant key in a visible cell takes over head 0's output; the same
     key planted in a hidden cell (other sequence, future position, stale row

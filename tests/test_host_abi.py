@@ -270,6 +270,25 @@ def test_error_codes():
         K.Context(1, 2, 1, 16, kv_size=4, cell_order=[0, 1, 1, 2])
 
 
+def test_time_next_attend_arguments():
+    """Kernel timing is armed per context and checked on the host: unknown
+    kinds and NULL events are refused; a failing attend call disarms it."""
+    ctx = K.Context(1, 2, 1, 16, kv_size=8, n_ubatch=4)
+    for kind, e0, e1 in ((3, 1, 2), (K.KVATTN_KERNEL_MFMA, 0, 2), (K.KVATTN_KERNEL_VALU, 1, 0)):
+        with pytest.raises(K.KvattnError) as e:
+            K.kvattn_time_next_attend(ctx.ctx, kind, e0, e1)
+        assert e.value.code == K.KVATTN_EINVAL
+    K.kvattn_time_next_attend(ctx.ctx, -1, 0, 0)          # disarm: always accepted
+    # armed with stand-in handles: the host-only attend fails before any
+    # launch, so the handles are never used, and the call clears them
+    K.kvattn_time_next_attend(ctx.ctx, K.KVATTN_KERNEL_MERGE, 1, 2)
+    st, ubs, _ = ctx.split(2)
+    ctx.store(ubs[0], 0, [], [])
+    with pytest.raises(K.KvattnError) as e:
+        ctx.attend(ubs[0], 0, [], [])
+    assert e.value.code == K.KVATTN_ENODEV
+
+
 def test_empty_batch_and_uncommitted_release():
     ctx = K.Context(1, 2, 1, 16, kv_size=8, n_ubatch=4)
     st, ubs, _ = ctx.split(0)

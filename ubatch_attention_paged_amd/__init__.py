@@ -17,6 +17,7 @@ from .kvattn import (  # noqa: F401
     kvattn_sched_request, kvattn_sched_last_error, KVATTN_ADMIT_RESERVE, KVATTN_ADMIT_PAGED,
     KVATTN_REQ_WAITING, KVATTN_REQ_RUNNING, KVATTN_REQ_DONE,
     kvattn_seq_state_size, kvattn_seq_state_save, kvattn_seq_state_load,
+    kvattn_time_next_attend, KVATTN_KERNEL_MFMA, KVATTN_KERNEL_VALU, KVATTN_KERNEL_MERGE,
 )
 
 load()

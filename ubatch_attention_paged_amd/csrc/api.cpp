@@ -101,6 +101,9 @@ struct kvattn_ctx {
   void* peek = nullptr;
   size_t peek_cap = 0;
   char* peek_dev = nullptr;
+  // kernel timing armed for the next attend call (kind -1: none)
+  int32_t time_kind = -1;
+  hipEvent_t time_ev[2] = {};
   char* arena() { return ws + wl.arena; }
 
   int fail(int code, const std::string& msg) {
@@ -515,6 +518,20 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
                                  const void* const* q, void* const* out, int32_t only_outputs, void* hip_stream,
                                  float* part_acc, float* part_ml, int64_t part_rows) {
   if (!c) return KVATTN_EINVAL;
+  // kernel timing is used by this call alone, whatever its outcome
+  const int32_t tkind = c->time_kind;
+  const hipEvent_t tev0 = c->time_ev[0], tev1 = c->time_ev[1];
+  c->time_kind = -1;
+  c->time_ev[0] = c->time_ev[1] = nullptr;
+  bool timed = false;
+  // the armed events of a call that launches no kernel of the chosen kind
+  // are recorded back to back on its stream (elapsed time about zero)
+  auto untimed = [&](hipStream_t st) -> int {
+    if (tkind < 0 || timed) return KVATTN_OK;
+    HIP_TRY(c, hipEventRecord(tev0, st));
+    HIP_TRY(c, hipEventRecord(tev1, st));
+    return KVATTN_OK;
+  };
   int k, rc;
   if ((rc = check_ubatch(c, ub, &k)) || (rc = check_layers(c, il0, n_il))) return rc;
   if (n_il > 0 && (!q || !out)) return c->fail(KVATTN_EINVAL, "q / out is NULL");
@@ -526,7 +543,7 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
   const Geometry& g = c->core.geo();
   const int v = only_outputs ? 1 : 0;
   const Plan& P = c->plan[v];
-  if (P.slots.empty()) return KVATTN_OK;      // no query rows (e.g. no flagged slot)
+  if (P.slots.empty()) return untimed(s);     // no query rows (e.g. no flagged slot)
   const VariantLayout& VL = c->al.v[v];
   char* arena = c->arena();
   AttnArgs a{};
@@ -563,8 +580,18 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
   a.layer_bytes = static_cast<uint32_t>(static_cast<size_t>(g.n_stream) * g.kv_size * g.E() * 2);
   const int64_t per = std::max<int64_t>(1, P.n_partial_rows);
   const int32_t chunk = static_cast<int32_t>(std::min<int64_t>(kMaxLayersPerLaunch, part_rows / per));
+  const int32_t n_red = static_cast<int32_t>(P.red_slot.size());
+  const int32_t kind_items[3] = {static_cast<int32_t>(P.items_mfma.size()), static_cast<int32_t>(P.items_valu.size()),
+                                 n_red};
   for (int32_t l0 = 0; l0 < n_il; l0 += chunk) {
     const int n = std::min<int32_t>(chunk, n_il - l0);
+    // the timed kernel's first launch starts the events, its last one stops them
+    KernelEvents ev[3];
+    if (tkind >= 0 && kind_items[tkind] > 0) {
+      ev[tkind].start = l0 == 0 ? tev0 : nullptr;
+      ev[tkind].stop = l0 + n >= n_il ? tev1 : nullptr;
+      timed = true;
+    }
     for (int i = 0; i < n; ++i) {
       if (!q[l0 + i] || !out[l0 + i]) return c->fail(KVATTN_EINVAL, "NULL q / out entry");
       a.q[i] = static_cast<const float*>(q[l0 + i]);
@@ -576,16 +603,31 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
     // would otherwise wait for vector-ALU workgroups to drain
     a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_mfma);
     a.n_items = static_cast<int32_t>(P.items_mfma.size());
-    HIP_TRY(c, launch_attn_mfma(a, n, g.head_dim, g.G(), s));
+    HIP_TRY(c, launch_attn_mfma(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_MFMA]));
     a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
     a.n_items = static_cast<int32_t>(P.items_valu.size());
-    HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s));
-    HIP_TRY(c, launch_reduce(a, static_cast<int32_t>(P.red_slot.size()), n, g.head_dim, s));
+    HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_VALU]));
+    HIP_TRY(c, launch_reduce(a, n_red, n, g.head_dim, s, ev[KVATTN_KERNEL_MERGE]));
   }
-  return KVATTN_OK;
+  return untimed(s);
 }
 
 extern "C" {
+
+int kvattn_time_next_attend(kvattn_ctx* c, int32_t kind, void* start_event, void* stop_event) {
+  if (!c) return KVATTN_EINVAL;
+  if (kind < 0) {
+    c->time_kind = -1;
+    c->time_ev[0] = c->time_ev[1] = nullptr;
+    return KVATTN_OK;
+  }
+  if (kind > KVATTN_KERNEL_MERGE) return c->fail(KVATTN_EINVAL, "unknown kernel kind " + std::to_string(kind));
+  if (!start_event || !stop_event) return c->fail(KVATTN_EINVAL, "kernel timing needs both events");
+  c->time_kind = kind;
+  c->time_ev[0] = static_cast<hipEvent_t>(start_event);
+  c->time_ev[1] = static_cast<hipEvent_t>(stop_event);
+  return KVATTN_OK;
+}
 
 int32_t kvattn_n_kv(const kvattn_ctx* c) { return c ? c->core.n_kv() : 0; }
 

@@ -14,6 +14,8 @@
 // it grows by more than 2^8.
 #include <algorithm>
 
+#include <hip/hip_ext.h>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -234,18 +236,21 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
 }
 
 template <int D, int G>
-static void valu_launch(const AttnArgs& a, int n_il, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn_valu<D, G>), dim3(a.n_items * n_il), dim3(256), 0, s, a);
+static void valu_launch(const AttnArgs& a, int n_il, hipStream_t s, const KernelEvents& ev) {
+  if (ev.any())
+    hipExtLaunchKernelGGL((k_attn_valu<D, G>), dim3(a.n_items * n_il), dim3(256), 0, s, ev.start, ev.stop, 0, a);
+  else
+    hipLaunchKernelGGL((k_attn_valu<D, G>), dim3(a.n_items * n_il), dim3(256), 0, s, a);
 }
 
-hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int D, int G, hipStream_t s) {
+hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int D, int G, hipStream_t s, const KernelEvents& ev) {
   if (a.n_items == 0 || n_il == 0) return hipSuccess;
-  if (D == 128 && G == 1) valu_launch<128, 1>(a, n_il, s);
-  else if (D == 128 && G == 2) valu_launch<128, 2>(a, n_il, s);
-  else if (D == 128 && G == 4) valu_launch<128, 4>(a, n_il, s);
-  else if (D == 64 && G == 1) valu_launch<64, 1>(a, n_il, s);
-  else if (D == 64 && G == 2) valu_launch<64, 2>(a, n_il, s);
-  else if (D == 64 && G == 4) valu_launch<64, 4>(a, n_il, s);
+  if (D == 128 && G == 1) valu_launch<128, 1>(a, n_il, s, ev);
+  else if (D == 128 && G == 2) valu_launch<128, 2>(a, n_il, s, ev);
+  else if (D == 128 && G == 4) valu_launch<128, 4>(a, n_il, s, ev);
+  else if (D == 64 && G == 1) valu_launch<64, 1>(a, n_il, s, ev);
+  else if (D == 64 && G == 2) valu_launch<64, 2>(a, n_il, s, ev);
+  else if (D == 64 && G == 4) valu_launch<64, 4>(a, n_il, s, ev);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -285,11 +290,14 @@ __global__ __launch_bounds__(1024) void k_attn_reduce(AttnArgs a, int D) {
   }
 }
 
-hipError_t launch_reduce(const AttnArgs& a, int n_reduced, int n_il, int D, hipStream_t s) {
+hipError_t launch_reduce(const AttnArgs& a, int n_reduced, int n_il, int D, hipStream_t s, const KernelEvents& ev) {
   if (n_reduced == 0 || n_il == 0) return hipSuccess;
   const int quads = a.n_head * D / 4;
   const int threads = std::min(1024, (quads + 63) / 64 * 64);
-  hipLaunchKernelGGL(k_attn_reduce, dim3(n_reduced, n_il), dim3(threads), 0, s, a, D);
+  if (ev.any())
+    hipExtLaunchKernelGGL(k_attn_reduce, dim3(n_reduced, n_il), dim3(threads), 0, s, ev.start, ev.stop, 0, a, D);
+  else
+    hipLaunchKernelGGL(k_attn_reduce, dim3(n_reduced, n_il), dim3(threads), 0, s, a, D);
   return hipGetLastError();
 }
 

@@ -116,9 +116,20 @@ bool commit_is_small(const CsrArgs& a);
 // the stores of n_il >= 1 layers and, in one extra workgroup, a small commit
 hipError_t launch_store_commit(const StoreArgs& a, int n_il, const CsrArgs& c, hipStream_t s);
 hipError_t launch_mask(const MaskArgs& a, hipStream_t s);
+// Optional kernel timing: a launch given either event goes through
+// hipExtLaunchKernel, which stamps `start` with the kernel's own start time
+// and `stop` with its end time (not the time the stream reached them).
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool any() const { return start || stop; }
+};
+
 // head_dim / group size are dispatched at run time
-hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s);
-hipError_t launch_attn_mfma(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s);
-hipError_t launch_reduce(const AttnArgs& a, int n_reduced, int n_il, int head_dim, hipStream_t s);
+hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s,
+                            const KernelEvents& ev = {});
+hipError_t launch_attn_mfma(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s,
+                            const KernelEvents& ev = {});
+hipError_t launch_reduce(const AttnArgs& a, int n_reduced, int n_il, int head_dim, hipStream_t s,
+                         const KernelEvents& ev = {});
 
 }  // namespace kvattn

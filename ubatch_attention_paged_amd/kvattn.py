@@ -28,6 +28,7 @@ KVATTN_ADMIT_RESERVE, KVATTN_ADMIT_PAGED = 0, 1
 ADMIT_POLICIES = {"reserve": KVATTN_ADMIT_RESERVE, "paged": KVATTN_ADMIT_PAGED}
 KVATTN_REQ_WAITING, KVATTN_REQ_RUNNING, KVATTN_REQ_DONE = 0, 1, 2
 KVATTN_PREEMPT_RECOMPUTE, KVATTN_PREEMPT_SWAP = 0, 1
+KVATTN_KERNEL_MFMA, KVATTN_KERNEL_VALU, KVATTN_KERNEL_MERGE = 0, 1, 2
 PREEMPT_MODES = {"recompute": KVATTN_PREEMPT_RECOMPUTE, "swap": KVATTN_PREEMPT_SWAP}
 MAX_SEQ = 64
 
@@ -105,6 +106,7 @@ SIGNATURES = {
                                      ctypes.c_int32, _vpp, _vpp, ctypes.c_int32, ctypes.c_void_p]),
     "kvattn_attend_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_int32,
                                              ctypes.c_int32, _vpp, _vpp, ctypes.c_int32, ctypes.c_void_p]),
+    "kvattn_time_next_attend": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "kvattn_n_kv": (ctypes.c_int32, [ctypes.c_void_p]),
     "kvattn_get_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_void_p,
                                        ctypes.c_size_t, _i32p, ctypes.c_void_p]),
@@ -311,6 +313,14 @@ def kvattn_attend_noalloc(ctx, ub: Ubatch, il0, q_ptrs: Sequence[int], out_ptrs:
     rc = load().kvattn_attend_noalloc(ctx, ctypes.byref(ub.raw), il0, len(q_ptrs),
                                       ctypes.cast(_ptrs(q_ptrs), _vpp), ctypes.cast(_ptrs(out_ptrs), _vpp),
                                       int(only_outputs), ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, kvattn_last_error(ctx))
+
+
+def kvattn_time_next_attend(ctx, kind, start_event, stop_event):
+    """Bind two HIP events (hipEvent_t handles) to the start and end of
+    kernel ``kind`` (KVATTN_KERNEL_*) in the next attend call."""
+    rc = load().kvattn_time_next_attend(ctx, int(kind), ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event))
     if rc != 0:
         raise KvattnError(rc, kvattn_last_error(ctx))
 
