@@ -78,41 +78,99 @@ def make_ctx(wl, dev, layer_chunk):
                    device=dev, attend_layers=layer_chunk)
 
 
+class TimingEvents:
+    """HIP events for kernel timing, created with hipEventDisableSystemFence
+    (timing kept, no system-scope cache writeback and invalidation when the
+    kernel they are bound to ends -- with the default flags that fence slows
+    the work after every timed kernel) through the HIP runtime torch has
+    loaded."""
+
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if TimingEvents._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            TimingEvents._hip = hip
+        self.ct = ctypes
+        self.pool = []
+        self.used = []
+
+    def reserve(self, n):
+        """Create event pairs up to n unused ones (before the timed region)."""
+        ct, hip = self.ct, TimingEvents._hip
+        while len(self.pool) < n:
+            pair = []
+            for _ in range(2):
+                e = ct.c_void_p()
+                if hip.hipEventCreateWithFlags(ct.byref(e), 0x20000000) != 0:    # hipEventDisableSystemFence
+                    raise RuntimeError("hipEventCreateWithFlags failed")
+                pair.append(e.value)
+            self.pool.append(tuple(pair))
+
+    def take(self):
+        if not self.pool:
+            self.reserve(1)
+        pair = self.pool.pop()
+        self.used.append(pair)
+        return pair
+
+    def record(self, event, stream):
+        if TimingEvents._hip.hipEventRecord(event, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def recycle(self):
+        """Return the taken pairs to the pool (after synchronising): the
+        warm-up steps run with timing too, so that the runtime has built
+        whatever it keeps per timed launch before the timed region."""
+        import torch
+        torch.cuda.synchronize()
+        self.pool.extend(self.used)
+        self.used = []
+
+    def elapsed_ms(self):
+        """Elapsed times of the taken pairs, in order (synchronises)."""
+        import torch
+        torch.cuda.synchronize()
+        ct, hip = self.ct, TimingEvents._hip
+        out = []
+        for a, b in self.used:
+            f = ct.c_float()
+            if hip.hipEventElapsedTime(ct.byref(f), a, b) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out.append(f.value)
+        return out
+
+    def close(self):
+        for a, b in self.pool + self.used:
+            TimingEvents._hip.hipEventDestroy(a)
+            TimingEvents._hip.hipEventDestroy(b)
+        self.pool, self.used = [], []
+
+
 class Runner:
-    """Drives measured batches through the library with HIP events around
-    every attend call (on torch's current stream, where the library
-    launches) and, when ``kernel`` names one of the attend call's kernels
-    (KVATTN_KERNEL_*), a second pair per call that the library binds to that
-    kernel's own start and end (hipExtLaunchKernel): its execution time
-    alone, without the stream's gaps around it."""
+    """Drives measured batches through the library and times every timed
+    attend call with a pair of HIP events on the stream it runs on: by
+    default recorded around the call (its kernels plus the gaps between
+    them), or -- with ``kernel`` one of KVATTN_KERNEL_* -- bound by the
+    library to that kernel's own start and end (kvattn_time_next_attend,
+    hipExtLaunchKernel)."""
 
     def __init__(self, ctx, layer_chunk, kernel=None):
         self.ctx = ctx
         self.chunk = layer_chunk
         self.kernel = kernel
-        self.attend_ms = []
-        self.kernel_ev = []
-        self._pool = []
+        self.events = TimingEvents()
         self.calls = 0
-        self.store_calls = 0
 
     def reserve(self, n):
-        """Create n kernel-event pairs before the timed region (torch creates
-        a HIP event at its first record; the library re-records it)."""
-        import torch
-        if self.kernel is None:
-            return
-        while len(self._pool) < n:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            e1.record()
-            self._pool.append((e0, e1))
-        torch.cuda.synchronize()
-
-    def _kernel_pair(self):
-        if not self._pool:
-            self.reserve(1)
-        return self._pool.pop()
+        """n pairs ready for the timed region; the warm-up's are recycled."""
+        self.events.recycle()
+        self.events.reserve(n)
 
     def run_batch(self, n, pos, seqs, out_flags, K, V, Q, outs, timed):
         """K, V, Q: [layers][n][width] fp32 device tensors in batch order;
@@ -137,35 +195,23 @@ class Runner:
                 kvattn_store(ctx.ctx, ub, a, row_ptrs(Kb, a, b, r0), row_ptrs(Vb, a, b, r0), stream)
                 self.calls += 1
                 if timed:
-                    if self.kernel is not None:
-                        k0, k1 = self._kernel_pair()
-                        kvattn_time_next_attend(ctx.ctx, self.kernel, k0.cuda_event, k1.cuda_event)
-                        self.kernel_ev.append((k0, k1))
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record()
+                    e0, e1 = self.events.take()
+                    if self.kernel is None:
+                        self.events.record(e0, stream)
+                    else:
+                        kvattn_time_next_attend(ctx.ctx, self.kernel, e0, e1)
                 kvattn_attend(ctx.ctx, ub, a, row_ptrs(Qb, a, b, r0), row_ptrs(outs, a, b, 0), 0, stream)
-                if timed:
-                    e1.record()
-                    self.attend_ms.append((e0, e1))
+                if timed and self.kernel is None:
+                    self.events.record(e1, stream)
         return ubs
 
     def attend_avg_ms(self):
-        import torch
-        torch.cuda.synchronize()
-        vals = [a.elapsed_time(b) for a, b in self.attend_ms]
+        vals = self.events.elapsed_ms()
         return float(np.mean(vals)) if vals else float("nan"), len(vals)
-
-    def kernel_avg_ms(self):
-        """Mean execution time of the timed kernel over the timed calls."""
-        import torch
-        torch.cuda.synchronize()
-        vals = [a.elapsed_time(b) for a, b in self.kernel_ev]
-        return float(np.mean(vals)) if vals else None
 
     def attend_by_position(self, per_step):
         """Mean attend time of the k-th attend call of a step, k < per_step."""
-        vals = np.array([a.elapsed_time(b) for a, b in self.attend_ms]).reshape(-1, per_step)
+        vals = np.array(self.events.elapsed_ms()).reshape(-1, per_step)
         return vals.mean(axis=0).tolist()
 
 
@@ -178,7 +224,9 @@ def prefill_pairs(wl):
     return sum(int((bt.pos.astype(np.int64) + 1).sum()) for bt in wl.batches)
 
 
-def bench_prefill(wl, dev, steps, warmup, layer_chunk):
+def bench_prefill(wl, dev, steps, warmup, layer_chunk, kernel=None):
+    """kernel: the attend call's kernel to time (KVATTN_KERNEL_*), default
+    the whole call."""
     import torch
     ctx = make_ctx(wl, dev, layer_chunk)
     layers = list(range(wl.n_layer))
@@ -188,8 +236,7 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
     sids = [SeqIds(bt.seq_ids) for bt in wl.batches]
     HD = wl.n_head * wl.head_dim
     outs = torch.empty((len(layers), wl.n_ubatch, HD), dtype=torch.float32, device=dev)
-    from ubatch_attention_paged_amd import KVATTN_KERNEL_MFMA
-    runner = Runner(ctx, layer_chunk, kernel=KVATTN_KERNEL_MFMA)
+    runner = Runner(ctx, layer_chunk, kernel)
 
     def step(timed):
         ctx.seq_rm(-1)                          # retire the previous request
@@ -198,7 +245,7 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
             runner.run_batch(bt.n_tokens, bt.pos, sids[b], bt.output, K, V, Q, outs, timed)
 
     for _ in range(warmup):
-        step(False)
+        step(True)
     runner.reserve(steps * runner.calls // max(1, warmup))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -223,7 +270,8 @@ def bench_prefill(wl, dev, steps, warmup, layer_chunk):
             f"{ms:.3f} ms {f / (ms * 1e-3) / 1e12:.0f} TF/s" for ms, f in zip(per_ub, ub_flops)))
     res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens=wl.measured_tokens(),
                flops_step=flops_step, attend_launches_per_step=n_ub_step, attend_avg_ms=avg_ms,
-               attend_ms_per_step=avg_ms * n_ub_step, kernel_avg_ms=runner.kernel_avg_ms(), last_plan=stats)
+               attend_ms_per_step=avg_ms * n_ub_step, last_plan=stats)
+    runner.events.close()
     ctx.close()
     return res
 
@@ -268,11 +316,10 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
     sid = SeqIds(bt.seq_ids)
     HD = wl.n_head * wl.head_dim
     outs = torch.empty((len(layers), bt.n_tokens, HD), dtype=torch.float32, device=dev)
-    from ubatch_attention_paged_amd import KVATTN_KERNEL_VALU
-    runner = Runner(ctx, layer_chunk, kernel=KVATTN_KERNEL_VALU)
+    runner = Runner(ctx, layer_chunk)
     t = 0
     for _ in range(warmup):
-        runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, False)
+        runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, True)
         t += 1
     runner.reserve(steps * runner.calls // max(1, warmup))
     torch.cuda.synchronize()
@@ -295,9 +342,9 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
     res = dict(wall_s=wall, ms_per_step=1e3 * wall / steps, tokens_per_step=bt.n_tokens,
                tokens_per_s=bt.n_tokens * steps / wall, unique_cells=float(cells),
                kv_bytes_step=kv_bytes, qo_bytes_step=qo_bytes, attend_avg_ms=avg_ms,
-               kernel_avg_ms=runner.kernel_avg_ms(),
                attend_launches_per_step=launches, kv_read_gbs=gbs, hbm_frac=gbs / HBM_PEAK_GBS,
                kv_qo_gbs=(kv_bytes + qo_bytes) / launches / (avg_ms * 1e-3) / 1e9, plan=ctx.plan_stats())
+    runner.events.close()
     ctx.close()
     return res
 
@@ -352,7 +399,8 @@ def bench_mixed(wl, dev, steps, warmup, layer_chunk):
         return shapes
 
     for _ in range(warmup):
-        shapes = step(False)
+        shapes = step(True)
+    runner.reserve(steps * runner.calls // max(1, warmup))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -381,8 +429,22 @@ def bench_mixed(wl, dev, steps, warmup, layer_chunk):
                                             kv_read_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
     if chunks:
         tf = flops / (ms_chunks * 1e-3) / 1e12
+        # a chunk's fp32 q rows are read and its fp32 outputs written once,
+        # and each sequence's visible cells (its positions 0..max) once per
+        # layer: short chunks over short histories carry ~80 flop per byte,
+        # far below the ~310 at which the matrix cores would bind
+        qo = sum(shapes[u][1].size for u in chunks) * HD * 4 * 2
+        kv = sum(float((shapes[u][1].reshape(-1, shapes[u][0]).max(axis=1) + 1).sum()) for u in chunks) * row
+        chunk_bytes = (qo + kv) * wl.n_layer
+        hbm_ms = chunk_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+        mfma_ms = flops / (MFMA_F16_PEAK_TFLOPS * 1e12) * 1e3
         res["prompt_chunk_ubatches"] = dict(count=len(chunks), attend_ms=round(ms_chunks, 4),
-                                            tflops=round(tf, 1), mfma_frac=round(tf / MFMA_F16_PEAK_TFLOPS, 4))
+                                            tflops=round(tf, 1), mfma_frac=round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                            bytes=round(chunk_bytes), flop_per_byte=round(flops / chunk_bytes, 1),
+                                            gbs=round(chunk_bytes / (ms_chunks * 1e-3) / 1e9, 1),
+                                            bound="hbm" if hbm_ms >= mfma_ms else "mfma",
+                                            roofline_frac=round(max(hbm_ms, mfma_ms) / ms_chunks, 4))
+    runner.events.close()
     ctx.close()
     return res
 
@@ -413,7 +475,8 @@ def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk, swap_bytes=
     Q = torch.randn((L, nb, HD), generator=g, device=dev)
     outs = torch.empty((L, stream.n_ubatch, HD), dtype=torch.float32, device=dev)
     cur = torch.cuda.current_stream().cuda_stream
-    attend_ev = []
+    # event pairs recorded around each timed attend call, created before timing
+    events = TimingEvents()
 
     def iteration(k, timed):
         for r in stream.arrivals(k):
@@ -444,25 +507,28 @@ def bench_serving(stream, dev, warm_iters, timed_iters, layer_chunk, swap_bytes=
                     b = min(L, a + layer_chunk)
                     kvattn_store(ctx.ctx, ub, a, row_ptrs(K, a, b, r0), row_ptrs(V, a, b, r0), cur)
                     if timed:
-                        e0 = torch.cuda.Event(enable_timing=True)
-                        e1 = torch.cuda.Event(enable_timing=True)
-                        e0.record()
+                        e0, e1 = events.take()
+                        events.record(e0, cur)
                     kvattn_attend(ctx.ctx, ub, a, row_ptrs(Q, a, b, r0), row_ptrs(outs, a, b, 0), 0, cur)
                     if timed:
-                        e1.record()
-                        attend_ev.append((e0, e1))
+                        events.record(e1, cur)
         sch.advance()
         return t_sched, info
 
     log(f"[bench] serving: {warm_iters} warm-up iterations")
     for k in range(warm_iters):
-        iteration(k, False)
+        iteration(k, True)
+    events.recycle()
+    # at most token_budget / n_ubatch + n_stream ubatches per iteration
+    events.reserve(timed_iters * ((nb + stream.n_ubatch - 1) // stream.n_ubatch + stream.n_stream)
+                   * ((L + layer_chunk - 1) // layer_chunk))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     recs = [iteration(warm_iters + k, True) for k in range(timed_iters)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    attend_ms = sum(a.elapsed_time(b) for a, b in attend_ev)
+    attend_ms = sum(events.elapsed_ms())
+    events.close()
     sched_us = np.array([r[0] for r in recs]) * 1e6
     info = np.array([r[1] for r in recs], dtype=np.int64)
     slots, dec, gen = int(info[:, 0].sum()), int(info[:, 1].sum()), int(info[:, 2].sum())
@@ -918,16 +984,15 @@ def main():
                                           for k, v in dec.items()}}), flush=True)
         return
     wl = W.qwen_prefill()
-    pre = bench_prefill(wl, dev, args.steps, args.warmup, args.layer_chunk)
+    from ubatch_attention_paged_amd import KVATTN_KERNEL_MFMA
+    pre = bench_prefill(wl, dev, args.steps, args.warmup, args.layer_chunk, KVATTN_KERNEL_MFMA)
     tok_s = pre["tokens"] * args.steps / pre["wall_s"]
     per_launch_flop = pre["flops_step"] / pre["attend_launches_per_step"]
-    # the kernel's own execution time (events bound to its launch); the
-    # events around the whole attend call also hold the stream's gaps
-    kern_ms = pre["kernel_avg_ms"] if pre["kernel_avg_ms"] is not None else pre["attend_avg_ms"]
+    # the matrix-core kernel's own execution time, every timed launch
+    kern_ms = pre["attend_avg_ms"]
     mfma_tf = per_launch_flop / (kern_ms * 1e-3) / 1e12
     log(f"[bench] prefill: {tok_s:,.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
-        f"attend {pre['attend_avg_ms']:.3f} ms/call x {pre['attend_launches_per_step']:.0f}, "
-        f"kernel {kern_ms:.4f} ms, {mfma_tf:.1f} TFLOP/s")
+        f"k_attn_mfma {kern_ms:.4f} ms/launch x {pre['attend_launches_per_step']:.0f}, {mfma_tf:.1f} TFLOP/s")
     line = {
         "metric": "ubatch attention tokens/s + decode KV-read GB/s (% HBM peak), 1xMI355X",
         "value": round(tok_s, 1),
@@ -953,8 +1018,8 @@ def main():
                      "per_launch": f"{per_launch_flop / 1e9:.2f} GFLOP "
                                    f"(4*H*d per visible (query, cell) pair x 28 layers of one ubatch)",
                      "event_avg_ms": round(kern_ms, 4),
-                     "event_kind": "kernel execution (hipExtLaunchKernel start/stop events, every timed launch)",
-                     "call_event_avg_ms": round(pre["attend_avg_ms"], 4)},
+                     "event_kind": "k_attn_mfma execution, HIP events bound to every timed launch "
+                                   "(hipExtLaunchKernel start/stop)"},
     }
     trace_ms = committed_trace_ms("k_attn_mfma", "attn_mfma.hip", "prefill")
     if trace_ms is not None:
@@ -971,7 +1036,6 @@ def main():
             "tokens_per_s": round(pl["tokens"] * ps / pl["wall_s"], 1), "ms_per_step": round(pl["ms_per_step"], 4),
             "attend_launches_per_step": round(pl["attend_launches_per_step"], 1),
             "attend_us_per_launch": round(1e3 * pl["attend_avg_ms"], 2),
-            "mfma_kernel_us_per_launch": round(1e3 * pl["kernel_avg_ms"], 2),
             "attend_ms_per_step": round(pl["attend_ms_per_step"], 4),
             "tflops_attend": round(pre["flops_step"] / (pl["attend_ms_per_step"] * 1e-3) / 1e12, 1)}}
         log(f"[bench] prefill, one call per layer: {line['per_layer_calls']['prefill']}")
@@ -987,7 +1051,6 @@ def main():
                          "kv_bytes_per_step": round(r["kv_bytes_step"]), "qo_bytes_per_step": round(r["qo_bytes_step"]),
                          "kv_qo_gbs": round(r["kv_qo_gbs"], 1),
                          "attend_avg_ms": round(r["attend_avg_ms"], 4),
-                         "valu_kernel_avg_ms": round(r["kernel_avg_ms"], 4),
                          "unique_cells_per_step": r["unique_cells"], "plan": r["plan"]}
             if name == "cb_decode" and not args.no_per_layer:
                 rp = bench_decode(w, dev, args.steps, args.warmup, 1)
@@ -995,7 +1058,6 @@ def main():
                     "tokens_per_s": round(rp["tokens_per_s"], 1), "ms_per_step": round(rp["ms_per_step"], 4),
                     "attend_launches_per_step": round(rp["attend_launches_per_step"], 1),
                     "attend_us_per_launch": round(1e3 * rp["attend_avg_ms"], 2),
-                    "valu_kernel_us_per_launch": round(1e3 * rp["kernel_avg_ms"], 2),
                     "kv_read_gbs": round(rp["kv_read_gbs"], 1), "hbm_frac": round(rp["hbm_frac"], 4)}
                 log(f"[bench] cb_decode, one call per layer: {line['per_layer_calls']['cb_decode']}")
             if name == "cb_decode":

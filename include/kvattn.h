@@ -237,15 +237,21 @@ int kvattn_attend_noalloc(kvattn_ctx *ctx, const kvattn_ubatch *ub, int32_t il0,
  * method).  The next kvattn_attend or kvattn_attend_noalloc call on this
  * context launches kernel `kind` with hipExtLaunchKernel, which stamps
  * start_event with that kernel's own start time and stop_event with its end
- * time (kernel execution only, not the time the stream reached them).
- * When the call cuts its layers into several launches, start_event belongs
- * to the first and stop_event to the last.  Both are hipEvent_t created by
+ * time (kernel execution only, not the time the stream reached them, and
+ * no marker packet of its own in the stream).  When the call cuts its
+ * layers into several launches, start_event belongs to the first and
+ * stop_event to the last (recorded on the stream right after it: one
+ * launch per call carries events, since the runtime holds the host thread
+ * at a second event-carrying launch).  Both are hipEvent_t created by
  * the caller on the context's device; the library keeps neither beyond the
  * next attend call, which uses the setting once and clears it.  A call that
  * launches no kernel of that kind records both events back to back on its
  * stream (elapsed time about zero); a call that fails before launching
- * records neither.  kind < 0 disarms.  KVATTN_EINVAL for an unknown kind or
- * a NULL event. */
+ * records neither.  Create the events with hipEventDisableSystemFence: a kernel
+ * bound to an event with the default flags ends with a system-scope cache
+ * writeback and invalidation that slows the work after it (measured: a
+ * shared-prefix decode step from 0.31 to 0.62 ms).  kind < 0 disarms.
+ * KVATTN_EINVAL for an unknown kind or a NULL event. */
 int kvattn_time_next_attend(kvattn_ctx *ctx, int32_t kind, void *start_event, void *stop_event);
 
 /* HOST-ONLY.  n_kv reported for the current state ("llama.cpp and the

@@ -104,6 +104,7 @@ struct kvattn_ctx {
   // kernel timing armed for the next attend call (kind -1: none)
   int32_t time_kind = -1;
   hipEvent_t time_ev[2] = {};
+  hipEvent_t time_spare = nullptr;
   char* arena() { return ws + wl.arena; }
 
   int fail(int code, const std::string& msg) {
@@ -132,6 +133,7 @@ int ensure_device(kvattn_ctx* c) {
   HIP_TRY(c, hipSetDevice(c->device));
   if (c->dev_ready) return KVATTN_OK;
   for (int i = 0; i < kStages; ++i) HIP_TRY(c, hipEventCreateWithFlags(&c->ev[i], hipEventDisableTiming));
+  HIP_TRY(c, hipEventCreateWithFlags(&c->time_spare, hipEventDisableSystemFence));
   // the allocation-free entry point's static array, located once per device
   if (int rc = static_scratch_init(c->device))
     return c->fail(rc, "hipGetSymbolAddress of the static scratch array failed");
@@ -390,6 +392,7 @@ void kvattn_destroy(kvattn_ctx* c) {
       if (c->stage[i]) (void)hipHostFree(c->stage[i]);
     }
     if (c->peek) (void)hipHostFree(c->peek);
+    if (c->time_spare) (void)hipEventDestroy(c->time_spare);
 
   }
   delete c;
@@ -585,11 +588,23 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
                                  n_red};
   for (int32_t l0 = 0; l0 < n_il; l0 += chunk) {
     const int n = std::min<int32_t>(chunk, n_il - l0);
-    // the timed kernel's first launch starts the events, its last one stops them
+    // The timed kernel's first launch starts the events and its last one
+    // stops them.  Only one launch per call carries the caller's events (the
+    // runtime holds the host thread at a second event-carrying launch until
+    // the first has run): when the layers are cut into several launches, the
+    // first carries the start event (with a spare event of the context as
+    // its stop) and the stop event is recorded on the stream right after
+    // the last one, so it stamps that kernel's completion.
     KernelEvents ev[3];
+    bool stop_after = false;
     if (tkind >= 0 && kind_items[tkind] > 0) {
-      ev[tkind].start = l0 == 0 ? tev0 : nullptr;
-      ev[tkind].stop = l0 + n >= n_il ? tev1 : nullptr;
+      const bool first = l0 == 0, last = l0 + n >= n_il;
+      if (first) {
+        ev[tkind].start = tev0;
+        ev[tkind].stop = last ? tev1 : c->time_spare;
+      } else if (last) {
+        stop_after = true;
+      }
       timed = true;
     }
     for (int i = 0; i < n; ++i) {
@@ -604,10 +619,13 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
     a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_mfma);
     a.n_items = static_cast<int32_t>(P.items_mfma.size());
     HIP_TRY(c, launch_attn_mfma(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_MFMA]));
+    if (stop_after && tkind == KVATTN_KERNEL_MFMA) HIP_TRY(c, hipEventRecord(tev1, s));
     a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
     a.n_items = static_cast<int32_t>(P.items_valu.size());
     HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_VALU]));
+    if (stop_after && tkind == KVATTN_KERNEL_VALU) HIP_TRY(c, hipEventRecord(tev1, s));
     HIP_TRY(c, launch_reduce(a, n_red, n, g.head_dim, s, ev[KVATTN_KERNEL_MERGE]));
+    if (stop_after && tkind == KVATTN_KERNEL_MERGE) HIP_TRY(c, hipEventRecord(tev1, s));
   }
   return untimed(s);
 }
