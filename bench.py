@@ -925,6 +925,9 @@ def main():
     ap.add_argument("--take", type=int, default=0)
     ap.add_argument("--leg", help="with --trace-stats: record the result under this leg in --trace-out")
     ap.add_argument("--trace-out", metavar="JSON", help="with --trace-stats: merge the result into this file")
+    ap.add_argument("--event-ms", type=float,
+                    help="with --trace-out: the event average (ms) the profiled run itself printed for this leg, "
+                         "recorded beside the trace average")
     ap.add_argument("--profile-command", default=PROFILE_COMMAND,
                     help="with --trace-out: the rocprofv3 command that wrote the trace, recorded beside the leg")
     ap.add_argument("--table", metavar="STEP_START",
@@ -949,12 +952,18 @@ def main():
         return
     if args.trace_stats:
         rec = trace_stats(args.trace_stats, args.kernel, args.skip, args.take)
+        if args.event_ms:
+            rec["event_avg_ms_same_run"] = args.event_ms
+            rec["trace_over_event"] = round(rec["avg_ns"] * 1e-6 / args.event_ms, 4)
         print(json.dumps(rec), flush=True)
         if args.trace_out:
             argv = [a for a in sys.argv[1:]]
-            if "--profile-command" in argv:
-                k = argv.index("--profile-command")
-                del argv[k:k + 2]
+            for opt in ("--profile-command",):
+                if opt in argv:
+                    k = argv.index(opt)
+                    del argv[k:k + 2]
+            # the trace's own location is the profiling run's output folder
+            argv = [f"<out>/{os.path.basename(a)}" if a == args.trace_stats else a for a in argv]
             write_trace_record(args.trace_out, args.kernel, args.leg, rec, " ".join(argv), args.profile_command)
         return
     if args.gpus != 1:
