@@ -1030,10 +1030,17 @@ def main():
                      "event_kind": "k_attn_mfma execution, HIP events bound to every timed launch "
                                    "(hipExtLaunchKernel start/stop)"},
     }
+    # the committed kernel trace of the same command: its average over the
+    # timed dispatches and the event average that profiled run printed
+    # (boxes differ by a few per cent, so the pair, not this run, is the
+    # trace-against-events comparison)
     trace_ms = committed_trace_ms("k_attn_mfma", "attn_mfma.hip", "prefill")
     if trace_ms is not None:
-        tf_trace = per_launch_flop / (trace_ms * 1e-3) / 1e12
-        line["roofline"].update(trace_avg_ms=round(trace_ms, 4), frac_trace=round(tf_trace / MFMA_F16_PEAK_TFLOPS, 4))
+        rec = json.load(open(os.path.join(ROOT, "profiles", "k_attn_mfma_trace.json")))["legs"]["prefill"]
+        line["roofline"]["profile"] = {"file": "profiles/k_attn_mfma_trace.json", "trace_avg_ms": round(trace_ms, 4),
+                                       "event_avg_ms_same_run": rec.get("event_avg_ms_same_run"),
+                                       "frac_trace": round(per_launch_flop / (trace_ms * 1e-3) / 1e12
+                                                           / MFMA_F16_PEAK_TFLOPS, 4)}
     line["hbm_copy_gbs"] = hbm_copy_gbs(dev)
     log(f"[bench] device-to-device copy: {line['hbm_copy_gbs']:.0f} GB/s")
     if not args.no_per_layer:
