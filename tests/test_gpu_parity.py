@@ -371,6 +371,56 @@ def test_kernel_timing_events_change_nothing(name):
     ctx.close()
 
 
+def test_kernel_timing_across_launches():
+    """A call whose layers are cut into several launches (the allocation-free
+    entry point holds 21 layers' partials of this plan per launch, so 28
+    layers take two): the start event belongs to the timed kernel's first
+    launch, the stop event to its last, the outputs stay bit-identical to
+    kvattn_attend's."""
+    wl = W.prefix_decode(n_seq=32, prefix=1024, private=128, n_layer=28, kv_size=8192)
+    print("[gpu] kernel timing across launches", flush=True)
+    layers = list(range(wl.n_layer))
+    ctx = make_ctx(wl, attend_layers=len(layers))
+    dev = torch.device("cuda:0")
+    from tests.helpers import batch_tensors
+    from ubatch_attention_paged_amd.harness import ubatch_rows
+    HD = wl.n_head * wl.head_dim
+    done = False
+    for b, bt in enumerate(wl.batches):
+        t = batch_tensors(wl, b, layers, bt.measured)
+        Kt = [torch.from_numpy(t[(l, W.KIND_K)]).to(dev) for l in layers]
+        Vt = [torch.from_numpy(t[(l, W.KIND_V)]).to(dev) for l in layers]
+        st, ubs, _ = ctx.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        assert st == 0
+        for ub in ubs:
+            ctx.store(ub, 0, [ubatch_rows(ub, x) for x in Kt], [ubatch_rows(ub, x) for x in Vt])
+            if not bt.measured:
+                continue
+            Q = [ubatch_rows(ub, torch.from_numpy(t[(l, W.KIND_Q)]).to(dev)) for l in layers]
+            ref = [torch.full((ub.n_tokens, HD), float("nan"), device=dev) for _ in layers]
+            ctx.attend(ub, 0, Q, ref)
+            stats = ctx.plan_stats()
+            assert stats["n_partial_rows"] * wl.n_layer > 2016 and stats["n_items_mfma"] > 0, stats
+            for kind in (K.KVATTN_KERNEL_MFMA, K.KVATTN_KERNEL_VALU, K.KVATTN_KERNEL_MERGE):
+                k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                k0.record()
+                k1.record()
+                K.kvattn_time_next_attend(ctx.ctx, kind, k0.cuda_event, k1.cuda_event)
+                out = [torch.full_like(r, float("nan")) for r in ref]
+                c0.record()
+                ctx.attend_noalloc(ub, 0, Q, out)
+                c1.record()
+                torch.cuda.synchronize()
+                assert all(torch.equal(a, c) for a, c in zip(ref, out))
+                kt, ct = k0.elapsed_time(k1), c0.elapsed_time(c1)
+                print(f"  kind {kind}: first launch start to last launch end {kt:.4f} ms, call {ct:.4f} ms", flush=True)
+                assert 0 < kt <= ct
+            done = True
+    assert done
+    ctx.close()
+
+
 def test_needles_on_gpu():
     """A dominant key in a visible cell takes over head 0's output; the same
     key planted in a hidden cell (other sequence, future position, stale row
