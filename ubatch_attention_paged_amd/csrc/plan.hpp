@@ -34,9 +34,12 @@ constexpr int kMfmaRowsPerItem = 128;  // query rows (queries x heads of one KV 
 constexpr int kValuTargetWorkgroups = 1024;
 constexpr int kMfmaTargetWorkgroups = 320;
 // Prompt-sized matrix-core classes (more than 64 query rows per KV head) are
-// cut only below this many workgroups per launch -- in practice only when a
-// launch covers one layer -- and never into pieces under 256 cells.
-constexpr int kMfmaHighTargetWorkgroups = 512;
+// cut only below this many workgroups per launch -- in practice when a
+// launch covers one layer, or a few short prompt chunks -- and never into
+// pieces under 256 cells.  Measured: 256 beats 512 and 1024 (one-layer
+// prefill calls 1-2% faster, mixed prompt-chunk ubatches 3-4% faster: fewer
+// partial rows to merge), while 128 leaves one-layer calls 25% slower.
+constexpr int kMfmaHighTargetWorkgroups = 256;
 // Decode chunks never shrink below 256 cells: measured on one-layer decode
 // launches, 64-cell chunks (4x the workgroups) ran slower than 256 (more
 // partial rows to merge, more per-item ramp).
