@@ -139,19 +139,23 @@ def test_mfma_head_shapes(d, g, swa):
     ctx.close()
 
 
-@pytest.mark.parametrize("d,g", [(128, 1), (128, 4), (64, 1), (64, 4)])
-def test_valu_head_shapes(d, g):
-    """The vector-ALU decode kernel's other (head_dim, group) instances (the
-    workloads above run group 2): a cache row is 1024 numbers either way, so
-    lanes map to KV heads differently per head size, and the group sets how
-    many query heads each lane's K/V feeds.  Contexts up to 300 cells are cut
-    into split-K chunks, so the merge runs too."""
+@pytest.mark.parametrize("d,g,hk", [(128, 1, 8), (128, 4, 8), (64, 1, 16), (64, 4, 16),
+                                    (128, 2, 4), (64, 1, 8), (128, 4, 4),
+                                    (128, 2, 16), (64, 4, 32), (128, 1, 32), (64, 2, 64)])
+def test_valu_head_shapes(d, g, hk):
+    """The vector-ALU decode kernel's other (head_dim, group, row width)
+    instances (the workloads above run group 2 over 1024-number rows): lanes
+    map to KV heads differently per head size, the group sets how many query
+    heads each lane's K/V feeds, 512-number rows put two cells in one
+    wavefront load (lane halves, merged at the end), and 2048 / 4096-number
+    rows split each row between wavefront groups.  Contexts up to 300 cells
+    are cut into split-K chunks, so the merge runs too."""
     wl = W.cb_decode(n_seq=16, lengths=(5, 40, 130, 300), n_layer=1, kv_size=4096)
-    wl.n_head_kv = 1024 // d
+    wl.n_head_kv = hk
     wl.n_head = wl.n_head_kv * g
     wl.head_dim = d
     layers = [0]
-    print(f"[gpu] vector-ALU head shape d={d} g={g}", flush=True)
+    print(f"[gpu] vector-ALU head shape d={d} g={g} kv heads {hk} (row {d * hk})", flush=True)
     _, ref, _, _ = oracle_run(wl, layers)
     items = {"valu": 0}
 
@@ -161,10 +165,37 @@ def test_valu_head_shapes(d, g):
     ctx, got = gpu_run(wl, layers, on_ubatch=count)
     worst = 0.0
     for key in ref:
-        ma, _ = assert_parity(got[key], ref[key], tag=f"d={d} g={g} batch {key[0]}")
+        ma, _ = assert_parity(got[key], ref[key], tag=f"d={d} g={g} hk={hk} batch {key[0]}")
         worst = max(worst, ma)
     assert items["valu"] > 0
     assert worst < 2e-5, worst      # fp32 throughout on this path
+    ctx.close()
+
+
+@pytest.mark.parametrize("hk", [4, 16])
+def test_prefix_sharing_other_row_widths(hk):
+    """Shared-prefix decode with 512- and 2048-number rows: the prefix runs
+    on the matrix cores, the private tails on the vector ALUs (two cells per
+    wavefront load, or a row split between wavefront groups), the merge
+    combines them."""
+    wl = W.prefix_decode(n_seq=8, prefix=300, private=50, n_layer=1, kv_size=1024)
+    wl.n_head_kv = hk
+    wl.n_head = 2 * hk
+    layers = [0]
+    print(f"[gpu] prefix sharing, {hk} KV heads x 128", flush=True)
+    _, ref, _, _ = oracle_run(wl, layers)
+    kinds = {"valu": 0, "mfma": 0, "red": 0}
+
+    def count(ctx, b, ub):
+        st = ctx.plan_stats()
+        kinds["valu"] += st["n_items_valu"]
+        kinds["mfma"] += st["n_items_mfma"]
+        kinds["red"] += st["n_reduced"]
+
+    ctx, got = gpu_run(wl, layers, on_ubatch=count)
+    for key in ref:
+        assert_parity(got[key], ref[key], tag=f"hk={hk} batch {key[0]}")
+    assert kinds["valu"] > 0 and kinds["mfma"] > 0 and kinds["red"] > 0, kinds
     ctx.close()
 
 

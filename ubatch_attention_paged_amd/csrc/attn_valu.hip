@@ -2,10 +2,14 @@
 //
 // One workgroup = one (query, chunk of a class's cell list); its 4
 // wavefronts take interleaved groups of U cells.  A cell row of one layer is
-// n_head_kv * head_dim = 1024 F16 (2 KiB): lane l holds 16 consecutive
-// numbers of it (two 16 B loads) -- KV head l / LPH, dims 16 * (l % LPH) ..
-// +16 -- so each K or V row is one fully coalesced 2 KiB wavefront access
-// wherever the cell sits in the cache.  Scores are reduced over the LPH lanes
+// E = n_head_kv * head_dim F16.  A wavefront reads 1024 numbers of a row per
+// load: lane l holds 16 consecutive numbers (two 16 B loads) -- KV head
+// l / LPH of the slice, dims 16 * (l % LPH) .. +16 -- so each access is one
+// fully coalesced 2 KiB wavefront access wherever the cell sits in the
+// cache.  Rows of 2048 or 4096 numbers are cut into 1024-number slices, each
+// owned by 4 / slices wavefronts that split the cells between them; a
+// 512-number row fills half a wavefront, so each wavefront takes two cells
+// per load (one per lane half) and merges the halves' states at the end.  Scores are reduced over the LPH lanes
 // of a head with DPP lane moves; the softmax runs online in base 2 with the
 // scale folded into q (fp32 throughout; the F16 rows are widened inside
 // v_fma_mix).  Each wavefront keeps the K/V rows of its next group of cells
@@ -42,14 +46,19 @@ KVATTN_DEV float group_sum(float s) {
 
 }  // namespace
 
-template <int D, int G>
+template <int D, int G, int E>
 __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   constexpr int LPH = D / 16;          // lanes per KV head
-  constexpr int HK = 64 / LPH;         // KV heads per row (row = 1024 numbers)
-  constexpr int E = HK * D;
+  constexpr int HK = E / D;            // KV heads per row
   constexpr int H = HK * G;
-  constexpr int U = 4;                 // cells in flight per wavefront step
+  constexpr int U = 4;                 // cells in flight per lane per wavefront step
+  constexpr int SL = E >= 1024 ? E / 1024 : 1;    // 1024-number slices of a row
+  constexpr int CPW = E >= 1024 ? 1 : 1024 / E;   // cells per wavefront load (lane halves)
+  constexpr int WPS = 4 / SL;          // wavefronts per slice
+  constexpr int LPR = E / 16 / SL;     // lanes per (slice of a) row
   static_assert(LPH == 4 || LPH == 8, "head_dim 64 or 128");
+  static_assert(E == 512 || E == 1024 || E == 2048 || E == 4096, "row of 512 .. 4096 numbers");
+  static_assert(CPW * LPR == 64 && SL * WPS == 4, "lane and wavefront mapping");
   __shared__ float red[3][64][G * 18];
 
   // item-major, layer-minor: the items are sorted longest first, so the
@@ -58,7 +67,10 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   const WorkItem it = a.items[blockIdx.x / n_il];
   const int il = blockIdx.x % n_il;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int kvh = lane / LPH, part = lane % LPH;
+  const int slice = w / WPS, wi = w % WPS;      // wave-uniform
+  const int half = lane / LPR;                  // lane half (two cells per load), else 0
+  const int rl = lane % LPR;
+  const int kvh = slice * (LPR / LPH) + rl / LPH, part = rl % LPH;
   const SlotInfo si = a.qslots[it.q_off];
   const bool check_mask = !it.pure;
   const _Float16* __restrict__ Kl = a.k[il];
@@ -85,7 +97,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   }
   const int64_t sbase = static_cast<int64_t>(si.stream) * a.kv_size;
   const int last = it.c1 - 1;
-  constexpr int STEP = 4 * U;          // cells the workgroup covers per step
+  constexpr int WSTEP = CPW * U;       // cells one wavefront covers per step
+  constexpr int STEP = WPS * WSTEP;    // cells the wavefronts of a slice cover per step
 
   // Software pipeline over this wavefront's steps (U cells each): while
   // step s computes, the K/V rows of step s+1 and the list entries (cell,
@@ -97,7 +110,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   auto fetch_list = [&](int c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = min(c + u, last);
+      const int idx = min(c + half * U + u, last);
       lc[u] = a.csr_cell[idx];
       lp[u] = a.csr_pos[idx];
       lm[u] = check_mask ? a.csr_mask[idx] : ~0ULL;
@@ -111,7 +124,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
       const half8* vp = reinterpret_cast<const half8*>(Vl + off);
       kr[u][0] = kp[0]; kr[u][1] = kp[1];
       vr[u][0] = vp[0]; vr[u][1] = vp[1];
-      vis[u] = c + u < it.c1 && (!a.causal || lp[u] <= si.pos) && ((lm[u] >> si.seq0) & 1ULL) &&
+      vis[u] = c + half * U + u < it.c1 && (!a.causal || lp[u] <= si.pos) && ((lm[u] >> si.seq0) & 1ULL) &&
                (a.swa == 0 || si.pos - lp[u] < a.swa);
     }
   };
@@ -162,7 +175,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
 
   half8 kA[U][2], vA[U][2], kB[U][2], vB[U][2];
   bool visA[U], visB[U];
-  const int c_first = it.c0 + w * U;   // wave-uniform, as is every step bound below
+  const int c_first = it.c0 + wi * WSTEP;   // wave-uniform, as is every step bound below
   if (c_first < it.c1) {
     fetch_list(c_first);
     issue(c_first, kA, vA, visA);
@@ -185,35 +198,53 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
     }
   }
 
-  // merge the four wavefronts' states
-  if (w > 0) {
+  // two cells per load: merge the lane halves' states (both halves end up
+  // holding the merged state)
+  if constexpr (CPW == 2) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      red[w - 1][lane][g * 18] = m[g];
-      red[w - 1][lane][g * 18 + 1] = l[g];
+      const float mo = __shfl_xor(m[g], 32, 64), lo = __shfl_xor(l[g], 32, 64);
+      const float M = fmaxf(m[g], mo);
+      const float s0 = (M == -INFINITY || m[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[g] - M);
+      const float s1 = (M == -INFINITY || mo == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mo - M);
+      l[g] = l[g] * s0 + lo * s1;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) red[w - 1][lane][g * 18 + 2 + e] = acc[g][e];
+      for (int e = 0; e < 16; ++e) acc[g][e] = acc[g][e] * s0 + __shfl_xor(acc[g][e], 32, 64) * s1;
+      m[g] = M;
     }
   }
-  __syncthreads();
-  if (w != 0) return;
+  // merge the states of each slice's wavefronts into its first one
+  constexpr int NS = WPS - 1;          // stored states per slice
+  if (wi > 0) {
+    const int k0 = slice * NS + wi - 1;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      red[k0][lane][g * 18] = m[g];
+      red[k0][lane][g * 18 + 1] = l[g];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[k0][lane][g * 18 + 2 + e] = acc[g][e];
+    }
+  }
+  if constexpr (NS > 0) __syncthreads();
+  if (wi != 0) return;
+  if (half != 0) return;               // the other lane half holds the same state
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     float M = m[g];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) M = fmaxf(M, red[k][lane][g * 18]);
+    for (int k = 0; k < NS; ++k) M = fmaxf(M, red[slice * NS + k][lane][g * 18]);
     const float s0 = (M == -INFINITY || m[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[g] - M);
     float L = l[g] * s0;
     float o[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[e] = acc[g][e] * s0;
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const float mk = red[k][lane][g * 18];
+    for (int k = 0; k < NS; ++k) {
+      const float mk = red[slice * NS + k][lane][g * 18];
       const float sk = (M == -INFINITY || mk == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk - M);
-      L += red[k][lane][g * 18 + 1] * sk;
+      L += red[slice * NS + k][lane][g * 18 + 1] * sk;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[e] += red[k][lane][g * 18 + 2 + e] * sk;
+      for (int e = 0; e < 16; ++e) o[e] += red[slice * NS + k][lane][g * 18 + 2 + e] * sk;
     }
     const int h = kvh * G + g;
     if (it.prow < 0) {
@@ -235,24 +266,36 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, int E>
 static void valu_launch(const AttnArgs& a, int n_il, hipStream_t s, const KernelEvents& ev) {
   if (ev.any())
-    hipExtLaunchKernelGGL((k_attn_valu<D, G>), dim3(a.n_items * n_il), dim3(256), 0, s, ev.start, ev.stop, 0, a);
+    hipExtLaunchKernelGGL((k_attn_valu<D, G, E>), dim3(a.n_items * n_il), dim3(256), 0, s, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL((k_attn_valu<D, G>), dim3(a.n_items * n_il), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_attn_valu<D, G, E>), dim3(a.n_items * n_il), dim3(256), 0, s, a);
+}
+
+template <int D, int G>
+static hipError_t valu_by_row(const AttnArgs& a, int n_il, int E, hipStream_t s, const KernelEvents& ev) {
+  switch (E) {
+    case 512: valu_launch<D, G, 512>(a, n_il, s, ev); break;
+    case 1024: valu_launch<D, G, 1024>(a, n_il, s, ev); break;
+    case 2048: valu_launch<D, G, 2048>(a, n_il, s, ev); break;
+    case 4096: valu_launch<D, G, 4096>(a, n_il, s, ev); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int D, int G, hipStream_t s, const KernelEvents& ev) {
   if (a.n_items == 0 || n_il == 0) return hipSuccess;
-  if (D == 128 && G == 1) valu_launch<128, 1>(a, n_il, s, ev);
-  else if (D == 128 && G == 2) valu_launch<128, 2>(a, n_il, s, ev);
-  else if (D == 128 && G == 4) valu_launch<128, 4>(a, n_il, s, ev);
-  else if (D == 64 && G == 1) valu_launch<64, 1>(a, n_il, s, ev);
-  else if (D == 64 && G == 2) valu_launch<64, 2>(a, n_il, s, ev);
-  else if (D == 64 && G == 4) valu_launch<64, 4>(a, n_il, s, ev);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
+  const int E = a.n_head_kv * D;
+  if (D == 128 && G == 1) return valu_by_row<128, 1>(a, n_il, E, s, ev);
+  if (D == 128 && G == 2) return valu_by_row<128, 2>(a, n_il, E, s, ev);
+  if (D == 128 && G == 4) return valu_by_row<128, 4>(a, n_il, E, s, ev);
+  if (D == 64 && G == 1) return valu_by_row<64, 1>(a, n_il, E, s, ev);
+  if (D == 64 && G == 2) return valu_by_row<64, 2>(a, n_il, E, s, ev);
+  if (D == 64 && G == 4) return valu_by_row<64, 4>(a, n_il, E, s, ev);
+  return hipErrorInvalidValue;
 }
 
 // split-K merge.  Record k of a query holds (m_k, l_k, acc_k) for each head;

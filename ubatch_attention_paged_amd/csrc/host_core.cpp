@@ -571,7 +571,9 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
 
   // work items
   const int D = g_.head_dim, G = g_.G();
-  const bool valu_ok = g_.E() == 1024 && (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4);
+  const int32_t E = g_.E();
+  const bool valu_ok = (E == 512 || E == 1024 || E == 2048 || E == 4096) && (D == 64 || D == 128) &&
+                       (G == 1 || G == 2 || G == 4);
   const int32_t QT = kMfmaRowsPerItem / G;   // query rows of one matrix-core workgroup
   // Item sizing.  One attend call launches (items x layers per call)
   // workgroups.  Each bandwidth-bound class is cut into chunks of at most
