@@ -887,6 +887,60 @@ def hbm_copy_gbs(dev, nbytes=2 << 30, reps=10):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
+def ceilings(dev, reps=10):
+    """What this GPU delivers to the two instruction forms the attention
+    kernels are built on, measured through the library's probes and timed
+    with fence-free HIP events: whole 2 KiB rows read in a shuffled order
+    (every row of a 2 GiB buffer once per launch: the decode kernel's access,
+    read-only) and back-to-back independent 32x32x16 F16 matrix-core
+    products (the prefill kernel's instruction)."""
+    import torch
+    from ubatch_attention_paged_amd import kvattn_probe_gather, kvattn_probe_mfma
+    stream = torch.cuda.current_stream().cuda_stream
+    n_rows = 1 << 20
+    rows = torch.full((n_rows, 1024), 0.5, dtype=torch.float16, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    index = torch.randperm(n_rows, generator=g, device=dev).to(torch.int32)
+    n_wg = 1024                      # 4 wavefronts per SIMD: the best of 512 .. 16384 measured
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    ev = TimingEvents()
+    ev.reserve(2 * reps)
+
+    def timed(launch):
+        for _ in range(2):
+            launch()
+        ev.recycle()
+        for _ in range(reps):
+            e0, e1 = ev.take()
+            ev.record(e0, stream)
+            launch()
+            ev.record(e1, stream)
+        ms = float(np.mean(ev.elapsed_ms()))
+        ev.recycle()
+        return ms
+
+    g_ms = timed(lambda: kvattn_probe_gather(rows.data_ptr(), n_rows, index.data_ptr(), n_rows, out.data_ptr(),
+                                             n_wg, stream))
+    index.copy_(torch.arange(n_rows, device=dev, dtype=torch.int32))
+    s_ms = timed(lambda: kvattn_probe_gather(rows.data_ptr(), n_rows, index.data_ptr(), n_rows, out.data_ptr(),
+                                             n_wg, stream))
+    gbs, sgbs = (n_rows * 2048 / (t * 1e-3) / 1e9 for t in (g_ms, s_ms))
+    del rows, index
+    ab = torch.ones(16, dtype=torch.float16, device=dev)
+    m_wg, iters = 4096, 4096
+    out = torch.empty(m_wg * 256, dtype=torch.float32, device=dev)
+    m_ms = timed(lambda: kvattn_probe_mfma(ab.data_ptr(), out.data_ptr(), m_wg, iters, stream))
+    tf = m_wg * 4 * iters * 4 * 32768 / (m_ms * 1e-3) / 1e12
+    ev.close()
+    return {"gather_read_gbs": round(gbs, 1), "gather_frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "sequential_read_gbs": round(sgbs, 1),
+            "mfma_f16_tflops": round(tf, 1), "mfma_frac_of_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+            "how": "library probes: every row of a 2 GiB buffer of 2 KiB rows read once per launch, in a "
+                   "shuffled order and in order, 1024 workgroups of 4 wavefronts; 4096 workgroups x 4 "
+                   "wavefronts x 4096 rounds of four independent 32x32x16 F16 products"}
+
+
 def committed_traffic(kernel, source):
     """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE /
     WRITE_SIZE summary, scaled by the copy-kernel calibration recorded there;
@@ -1043,6 +1097,8 @@ def main():
                                                            / MFMA_F16_PEAK_TFLOPS, 4)}
     line["hbm_copy_gbs"] = hbm_copy_gbs(dev)
     log(f"[bench] device-to-device copy: {line['hbm_copy_gbs']:.0f} GB/s")
+    line["ceilings"] = ceilings(dev)
+    log(f"[bench] ceilings: {line['ceilings']}")
     if not args.no_per_layer:
         # a forward pass calls attend once per layer (layer l+1's q depends on
         # layer l): the same prompt with one store and one attend per layer

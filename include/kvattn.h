@@ -350,6 +350,28 @@ int kvattn_get_params(const kvattn_ctx *ctx, kvattn_params *out);
 /* HOST-ONLY.  Text of the last error on this context ("" if none). */
 const char *kvattn_last_error(const kvattn_ctx *ctx);
 
+/* ---- machine ceilings (benchmarks; not part of the method) --------------- */
+
+/* Read rate of the decode kernel's access: every wavefront reads whole 2 KiB
+ * rows (1024 F16) of `rows` ([n_rows][1024], device) in the order of `index`
+ * (n_index device int32; entries outside [0, n_rows) are clamped), each row
+ * one 2 KiB wavefront access, four rows in flight per wavefront.  `out`
+ * (device, n_wg * 256 floats, caller-owned) receives each thread's fp32 sum
+ * of the numbers it read.  Asynchronous on hip_stream; KVATTN_EINVAL for a
+ * NULL pointer or a non-positive size, KVATTN_EHIP if the launch fails. */
+int kvattn_probe_gather(const void *rows, int64_t n_rows, const int32_t *index, int64_t n_index, float *out,
+                        int32_t n_wg, void *hip_stream);
+
+/* Matrix-core issue rate: n_wg workgroups of four wavefronts each run
+ * `iters` rounds of four independent v_mfma_f32_32x32x16_f16 products (the
+ * prefill kernel's instruction) on operands read from `ab` (device, 16 F16:
+ * every lane's A fragment is ab[0..7], its B fragment ab[8..15]).  Each
+ * product adds 2 * sum_j ab[j] * ab[8 + j] to each of its 1024 outputs, so
+ * `out` (device, n_wg * 256 floats) receives 128 * iters * sum_j ab[j] *
+ * ab[8 + j] per thread; one launch performs n_wg * 4 * iters * 4 * 32768
+ * flop.  Asynchronous on hip_stream; errors as kvattn_probe_gather. */
+int kvattn_probe_mfma(const void *ab, float *out, int32_t n_wg, int32_t iters, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

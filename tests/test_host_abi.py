@@ -289,6 +289,19 @@ def test_time_next_attend_arguments():
     assert e.value.code == K.KVATTN_ENODEV
 
 
+def test_probe_arguments_refused_on_the_host():
+    """The ceiling probes check their arguments before any launch."""
+    for args in ((0, 10, 1, 10, 1, 4), (1, 0, 1, 10, 1, 4), (1, 10, 0, 10, 1, 4), (1, 10, 1, 10, 0, 4),
+                 (1, 10, 1, 10, 1, 0), (1, 10, 1, -1, 1, 4)):
+        with pytest.raises(K.KvattnError) as e:
+            K.kvattn_probe_gather(*args)
+        assert e.value.code == K.KVATTN_EINVAL
+    for args in ((0, 1, 4, 10), (1, 0, 4, 10), (1, 1, 0, 10), (1, 1, 4, -1)):
+        with pytest.raises(K.KvattnError) as e:
+            K.kvattn_probe_mfma(*args)
+        assert e.value.code == K.KVATTN_EINVAL
+
+
 def test_empty_batch_and_uncommitted_release():
     ctx = K.Context(1, 2, 1, 16, kv_size=8, n_ubatch=4)
     st, ubs, _ = ctx.split(0)

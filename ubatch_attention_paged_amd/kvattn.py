@@ -108,6 +108,10 @@ SIGNATURES = {
                                              ctypes.c_int32, _vpp, _vpp, ctypes.c_int32, ctypes.c_void_p]),
     "kvattn_time_next_attend": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "kvattn_n_kv": (ctypes.c_int32, [ctypes.c_void_p]),
+    "kvattn_probe_gather": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "kvattn_probe_mfma": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p]),
     "kvattn_get_mask": (ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(kvattn_ubatch), ctypes.c_void_p,
                                        ctypes.c_size_t, _i32p, ctypes.c_void_p]),
     "kvattn_get_classes": (ctypes.c_int, [ctypes.c_void_p, _i32p, _i32p, _u64p, _i32p, ctypes.c_int32,
@@ -323,6 +327,22 @@ def kvattn_time_next_attend(ctx, kind, start_event, stop_event):
     rc = load().kvattn_time_next_attend(ctx, int(kind), ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event))
     if rc != 0:
         raise KvattnError(rc, kvattn_last_error(ctx))
+
+
+def kvattn_probe_gather(rows, n_rows, index, n_index, out, n_wg, stream=0):
+    """Device addresses: rows [n_rows][1024] F16, index int32[n_index],
+    out float[n_wg * 256]."""
+    rc = load().kvattn_probe_gather(ctypes.c_void_p(rows), n_rows, ctypes.c_void_p(index), n_index,
+                                    ctypes.c_void_p(out), n_wg, ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, "kvattn_probe_gather")
+
+
+def kvattn_probe_mfma(ab, out, n_wg, iters, stream=0):
+    """Device addresses: ab 16 F16, out float[n_wg * 256]."""
+    rc = load().kvattn_probe_mfma(ctypes.c_void_p(ab), ctypes.c_void_p(out), n_wg, iters, ctypes.c_void_p(stream))
+    if rc != 0:
+        raise KvattnError(rc, "kvattn_probe_mfma")
 
 
 def kvattn_n_kv(ctx) -> int:
