@@ -100,3 +100,55 @@ def test_noalloc_refuses_partials_beyond_the_array():
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
     ctx.close()
+
+
+def test_noalloc_under_hip_graph_capture():
+    """The caller it is for: a decode step's attention captured into a HIP
+    graph (torch.cuda.graph) and replayed.  Every replay, with eager work and
+    synchronisations between replays, equals the eager call bit for bit (the
+    captured launches read the plan and partials in place; nothing in the
+    call allocates or writes memory outside the kernels)."""
+    import torch
+    import ubatch_attention_paged_amd as K
+    from ubatch_attention_paged_amd.harness import ubatch_rows
+    dev = torch.device("cuda:0")
+    wl = W.prefix_decode(n_seq=8, prefix=256, private=64, n_layer=3, kv_size=2048)
+    layers = list(range(wl.n_layer))
+    ctx = make_ctx(wl, attend_layers=len(layers))
+    HD = wl.n_head * wl.head_dim
+    checked = 0
+    for b, bt in enumerate(wl.batches):
+        t = batch_tensors(wl, b, layers, bt.measured)
+        Kt = [torch.from_numpy(t[(l, W.KIND_K)]).to(dev) for l in layers]
+        Vt = [torch.from_numpy(t[(l, W.KIND_V)]).to(dev) for l in layers]
+        st, ubs, _ = ctx.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        assert st == 0
+        for ub in ubs:
+            ctx.store(ub, 0, [ubatch_rows(ub, x) for x in Kt], [ubatch_rows(ub, x) for x in Vt])
+            if not bt.measured:
+                continue
+            Q = [ubatch_rows(ub, torch.from_numpy(t[(l, W.KIND_Q)]).to(dev)) for l in layers]
+            ref = [torch.full((ub.n_tokens, HD), float("nan"), device=dev) for _ in layers]
+            ctx.attend_noalloc(ub, 0, Q, ref)
+            torch.cuda.synchronize()
+            assert ctx.plan_stats()["n_reduced"] > 0       # split-K partials in the static array
+            out = [torch.full_like(r, float("nan")) for r in ref]
+            print("[gpu] capturing kvattn_attend_noalloc into a HIP graph", flush=True)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                ctx.attend_noalloc(ub, 0, Q, out)
+            scratch = [torch.full_like(r, float("nan")) for r in ref]
+            for rep in range(3):
+                for o in out:
+                    o.fill_(float("nan"))
+                graph.replay()
+                torch.cuda.synchronize()
+                assert all(torch.equal(a, c) for a, c in zip(ref, out)), f"replay {rep}"
+                # eager work between replays: the workspace entry point into other buffers
+                ctx.attend(ub, 0, Q, scratch)
+                torch.cuda.synchronize()
+                assert_parity(scratch[0].double().cpu().numpy(), ref[0].double().cpu().numpy(), tag="eager")
+            checked += 1
+            del graph
+    assert checked == 1
+    ctx.close()
