@@ -366,3 +366,57 @@ def test_seq_state_size_matches_oracle():
     with pytest.raises(K.KvattnError) as e:
         K.kvattn_seq_state_load(ctx.ctx, 0, 4096, 1 << 20)
     assert e.value.code == K.KVATTN_ENODEV
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_random_batches_match_oracle(seed):
+    """Differential check on random inputs: batches of random sequence-id sets
+    (shared prefixes, ids spanning streams), random positions and output
+    flags or auto-fill, every split strategy, one to four streams, shuffled
+    free lists, partially stored splits (the unstored ubatches' cells are
+    released by the next split), retirements and full caches.  Every
+    ubatch's slots, positions, cells and copies, the status, output_ids and
+    the committed cell table must equal the oracle's after every step."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 77]))
+    n_stream = int(rng.choice([1, 2, 4]))
+    n_seq_max = int(rng.integers(2, 13))
+    kv_size = int(rng.choice([24, 48, 96]))
+    n_batch = int(rng.choice([8, 16, 32]))
+    n_ubatch = int(rng.choice([3, 4, 8, 16]))
+    mode = str(rng.choice(["auto", "simple", "equal", "seq"]))
+    order = (np.stack([rng.permutation(kv_size) for _ in range(n_stream)]).astype(np.int32)
+             if rng.random() < 0.5 else None)
+    ctx = K.Context(1, 2, 1, 16, kv_size, n_stream, n_seq_max, n_batch, n_ubatch, cell_order=order,
+                    split_mode=mode)
+    eng = OracleEngine(1, 2, 1, 16, kv_size, n_stream, n_seq_max, n_batch, n_ubatch, cell_order=order,
+                       layers=[], split_mode=mode)
+    nb = ctx.n_batch()
+    next_pos = [0] * n_seq_max
+    for step in range(12):
+        if step and rng.random() < 0.25:
+            args = (int(rng.integers(-1, n_seq_max)), int(rng.integers(-1, 8)), int(rng.integers(-1, 40)))
+            ctx.seq_rm(*args)
+            eng.seq_rm(*args)
+            compare_tables(ctx, eng)
+            continue
+        n = int(rng.integers(0, nb + 1))
+        seqs, pos = [], []
+        for _ in range(n):
+            first = int(rng.integers(0, n_seq_max))
+            ids = [first]
+            if rng.random() < 0.2:          # a shared slot: extra ids (possibly in other streams)
+                extra = rng.choice(n_seq_max, size=int(rng.integers(1, min(3, n_seq_max) + 1)), replace=False)
+                ids += [int(x) for x in extra if int(x) != first]
+            seqs.append(ids)
+            pos.append(next_pos[first] if rng.random() < 0.8 else int(rng.integers(0, 64)))
+            next_pos[first] = pos[-1] + 1
+        out = (rng.random(n) < 0.3).astype(np.int8).tolist()
+        if rng.random() < 0.15:
+            pos_arg, out_arg = None, None       # auto-fill positions and output flags
+        else:
+            pos_arg, out_arg = pos, out
+        ubs, rubs = compare_split(ctx, eng, n, pos_arg, seqs, out_arg)
+        if ubs:
+            keep = len(ubs) if rng.random() < 0.8 else int(rng.integers(0, len(ubs) + 1))
+            commit_all(ctx, eng, ubs[:keep], rubs[:keep])
+        compare_tables(ctx, eng)
