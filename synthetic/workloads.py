@@ -213,6 +213,68 @@ def prefix_decode(n_seq=32, prefix=2048, private=256, n_layer=28, kv_size=16384,
                     note=f"{n_seq} sequences share {prefix} cells, {private} private each")
 
 
+def random_mix(seed, n_batches=6):
+    """A randomized small workload for differential tests: random head shape
+    (head_dim 64 or 128, group 1, 2 or 4, 2 to 8 KV heads), one to four
+    streams, shuffled or ordered free lists, any split strategy, causal or
+    not, sometimes a sliding window; batches mix prompt runs of one sequence
+    (consecutive positions), decode tokens, slots shared by several
+    sequences (which may span streams) and positions drawn at random, with
+    random output flags.  Every batch is measured and the cache never fills."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, PURPOSE_STRUCTURE, 9]))
+    head_dim = int(rng.choice([64, 128]))
+    g = int(rng.choice([1, 2, 4]))
+    hk = int(rng.choice([2, 4, 8]))
+    n_stream = int(rng.choice([1, 1, 2, 4]))
+    n_seq = int(rng.integers(2, 9))
+    n_batch = int(rng.choice([16, 48, 96]))
+    n_ubatch = int(rng.choice([7, 16, 32, 96]))
+    causal = bool(rng.random() < 0.8)
+    swa = int(rng.choice([0, 0, 0, 5, 40]))
+    split = str(rng.choice(["auto", "simple", "equal", "seq"]))
+    next_pos = [0] * n_seq
+    batches, total = [], 0
+    for _ in range(n_batches):
+        n = int(rng.integers(1, n_batch + 1))
+        pos, seqs = [], []
+        while len(pos) < n:
+            kind = rng.random()
+            s = int(rng.integers(0, n_seq))
+            if kind < 0.4:                       # a prompt run of one sequence
+                run = int(min(n - len(pos), rng.integers(1, 24)))
+                pos += list(range(next_pos[s], next_pos[s] + run))
+                seqs += [(s,)] * run
+                next_pos[s] += run
+            elif kind < 0.75:                    # one decode token
+                pos.append(next_pos[s])
+                seqs.append((s,))
+                next_pos[s] += 1
+            elif kind < 0.9:                     # a slot shared by several sequences
+                ids = [s] + [int(x) for x in rng.choice(n_seq, size=int(rng.integers(1, n_seq)), replace=False)
+                             if int(x) != s]
+                p = max(next_pos[i] for i in ids)
+                pos.append(p)
+                seqs.append(tuple(ids))
+                for i in ids:
+                    next_pos[i] = p + 1
+            else:                                # a position drawn at random
+                pos.append(int(rng.integers(0, 64)))
+                seqs.append((s,))
+        out = (rng.random(n) < 0.4).astype(np.int8)
+        batches.append(_batch(pos, seqs, out, True))
+        total += n
+    kv_size = int(2 * total + 64)            # every slot and its copies fit, in any stream
+    wl = Workload(f"random_mix_{seed}", 1, hk * g, hk, head_dim, kv_size=kv_size, n_stream=n_stream,
+                  n_seq_max=n_seq, seed=seed, batches=batches, n_batch=n_batch, n_ubatch=n_ubatch,
+                  causal=causal, split_mode=split, swa=swa,
+                  note=f"random mix {seed}: d={head_dim} g={g} kv heads {hk}, {n_stream} streams, {split}, "
+                       f"causal={causal}, window {swa}")
+    if rng.random() < 0.5:
+        orng = np.random.default_rng(np.random.SeedSequence([seed, PURPOSE_CELL_ORDER]))
+        wl.cell_order = np.stack([orng.permutation(kv_size) for _ in range(n_stream)]).astype(np.int32)
+    return wl
+
+
 WORKLOADS = {"tiny": tiny, "qwen_prefill": qwen_prefill, "cb_decode": cb_decode,
              "mixed": mixed, "prefix_decode": prefix_decode}
 
