@@ -44,7 +44,8 @@
 extern "C" {
 #endif
 
-#define KVATTN_MAX_SEQ 64           /* sequence ids live in [0, 64): one bit each */
+#define KVATTN_MAX_SEQ 256          /* sequence ids live in [0, 256): one bit each */
+#define KVATTN_SEQ_WORDS 4          /* a sequence set is 4 uint64 words; id q is bit q % 64 of word q / 64 */
 #define KVATTN_MAX_LAYERS_PER_LAUNCH 32
 
 enum {
@@ -269,9 +270,10 @@ int kvattn_get_mask(kvattn_ctx *ctx, const kvattn_ubatch *ub, void *d_mask, size
 /* Visibility lists of the most recently committed ubatch, copied to host
  * (synchronises hip_stream): the mask of "llama.cpp and the ubatch", "The
  * mask is doing the work", kept in sparse form.  Cells are grouped in classes of equal
- * sequence sets; per class: stream, sequence-set bitmask, number of cells,
- * then the cells in ascending index.  Fills up to cap_classes classes and
- * cap_cells cells; *n_classes / *n_cells receive the totals. */
+ * sequence sets; per class: stream, sequence set (KVATTN_SEQ_WORDS words at
+ * cls_mask + KVATTN_SEQ_WORDS * class), number of cells, then the cells in
+ * ascending index.  Fills up to cap_classes classes and cap_cells cells;
+ * *n_classes / *n_cells receive the totals. */
 int kvattn_get_classes(kvattn_ctx *ctx, int32_t *n_classes, int32_t *cls_stream,
                        uint64_t *cls_mask, int32_t *cls_count, int32_t cap_classes,
                        int32_t *n_cells, int32_t *cells, int32_t cap_cells, void *hip_stream);
@@ -279,7 +281,8 @@ int kvattn_get_classes(kvattn_ctx *ctx, int32_t *n_classes, int32_t *cls_stream,
 /* HOST-ONLY.  Copy of the committed cell table of one stream: pos (-1 =
  * empty) and the sequence-set bitmask of each of the kv_size cells (the
  * per-cell metadata the mask reads, "llama.cpp and the ubatch", "The mask is
- * doing the work").  pos and seqmask are host arrays of kv_size entries. */
+ * doing the work").  pos is a host array of kv_size entries, seqmask one of
+ * KVATTN_SEQ_WORDS * kv_size words (cell c's set at seqmask + KVATTN_SEQ_WORDS * c). */
 int kvattn_get_cells(const kvattn_ctx *ctx, int32_t stream, int32_t *pos, uint64_t *seqmask);
 
 /* HOST-ONLY.  Remove sequence seq_id (every sequence when < 0) from cells

@@ -220,8 +220,13 @@ def random_mix(seed, n_batches=6):
     not, sometimes a sliding window; batches mix prompt runs of one sequence
     (consecutive positions), decode tokens, slots shared by several
     sequences (which may span streams) and positions drawn at random, with
-    random output flags.  Every batch is measured and the cache never fills."""
+    random output flags.  Every batch is measured and the cache never fills.
+    Half of the seeds spread the sequences over a wide id space (n_seq_max
+    drawn in [65, 256], ids placed at random in it), so that sets span
+    several 64-bit words; that draw comes from a stream of its own, so the
+    rest of a seed's workload does not depend on it."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, PURPOSE_STRUCTURE, 9]))
+    irng = np.random.default_rng(np.random.SeedSequence([seed, PURPOSE_STRUCTURE, 10]))
     head_dim = int(rng.choice([64, 128]))
     g = int(rng.choice([1, 2, 4]))
     hk = int(rng.choice([2, 4, 8]))
@@ -261,14 +266,20 @@ def random_mix(seed, n_batches=6):
                 pos.append(int(rng.integers(0, 64)))
                 seqs.append((s,))
         out = (rng.random(n) < 0.4).astype(np.int8)
-        batches.append(_batch(pos, seqs, out, True))
+        batches.append((pos, seqs, out))
         total += n
+    n_seq_max = n_seq
+    ids = list(range(n_seq))
+    if irng.random() < 0.5:                  # a wide id space
+        n_seq_max = int(irng.integers(65, 257))
+        ids = [int(x) for x in irng.choice(n_seq_max, size=n_seq, replace=False)]
+    batches = [_batch(pos, [tuple(ids[i] for i in t) for t in seqs], out, True) for pos, seqs, out in batches]
     kv_size = int(2 * total + 64)            # every slot and its copies fit, in any stream
     wl = Workload(f"random_mix_{seed}", 1, hk * g, hk, head_dim, kv_size=kv_size, n_stream=n_stream,
-                  n_seq_max=n_seq, seed=seed, batches=batches, n_batch=n_batch, n_ubatch=n_ubatch,
+                  n_seq_max=n_seq_max, seed=seed, batches=batches, n_batch=n_batch, n_ubatch=n_ubatch,
                   causal=causal, split_mode=split, swa=swa,
                   note=f"random mix {seed}: d={head_dim} g={g} kv heads {hk}, {n_stream} streams, {split}, "
-                       f"causal={causal}, window {swa}")
+                       f"causal={causal}, window {swa}, ids {ids} of {n_seq_max}")
     if rng.random() < 0.5:
         orng = np.random.default_rng(np.random.SeedSequence([seed, PURPOSE_CELL_ORDER]))
         wl.cell_order = np.stack([orng.permutation(kv_size) for _ in range(n_stream)]).astype(np.int32)

@@ -55,11 +55,11 @@ def expected_classes(eng, ub):
         if not qseqs:
             continue
         pos = eng.cells.pos[s]
-        bits = (eng.cells.member[s].astype(np.uint64) << np.arange(eng.n_seq_max, dtype=np.uint64)).sum(axis=1)
+        bits = np.array([sum(1 << int(q) for q in np.nonzero(row)[0]) for row in eng.cells.member[s]], dtype=object)
         occupied = np.nonzero(pos >= 0)[0]
-        masks = sorted({int(bits[j]) for j in occupied if any(int(bits[j]) >> q & 1 for q in qseqs)})
+        masks = sorted({bits[j] for j in occupied if any(bits[j] >> q & 1 for q in qseqs)})
         for m in masks:
-            out.append((s, m, occupied[bits[occupied] == np.uint64(m)]))
+            out.append((s, m, occupied[bits[occupied] == m]))
     return out
 
 

@@ -1,8 +1,9 @@
 """GPU parity on randomized small workloads (synthetic.workloads.random_mix):
 random head shapes, stream counts, free-list orders, split strategies,
 causal or not, sliding windows, and batches mixing prompt runs, decode
-tokens, slots shared by several sequences and positions drawn at random.
-Cells and dense masks bit for bit, cache bytes bit for bit, every output of
+tokens, slots shared by several sequences and positions drawn at random;
+half of the seeds place their sequence ids across [0, 256), so that cell
+sets span several 64-bit words.  Cells and dense masks bit for bit, cache bytes bit for bit, every output of
 every slot within tolerance of the fp64 oracle."""
 
 import numpy as np

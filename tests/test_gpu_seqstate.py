@@ -74,8 +74,8 @@ def test_restore_then_attend_matches_oracle():
         S.load(eng, seq, blobs[src])
     pos, mask = dst.cells(0)
     assert np.array_equal(pos, eng.cells.pos[0])
-    ref_mask = sum(eng.cells.member[0][:, q].astype(np.uint64) << np.uint64(q) for q in range(wl.n_seq_max))
-    assert np.array_equal(mask, ref_mask)
+    assert np.array_equal(K.seqset_members(mask, K.MAX_SEQ)[:, :wl.n_seq_max], eng.cells.member[0])
+    assert not K.seqset_members(mask, K.MAX_SEQ)[:, wl.n_seq_max:].any()
     assert blob_bytes(dst.state_save(2)) == blobs[0] and blob_bytes(dst.state_save(3)) == blobs[1]
     # one decode token for each restored sequence, attention over the copies
     n, p = 2, 40 + 9 + 1

@@ -87,8 +87,9 @@ def compare_tables(ctx, eng):
     for s in range(eng.n_stream):
         pos, mask = ctx.cells(s)
         assert np.array_equal(pos, eng.cells.pos[s])
-        bits = (eng.cells.member[s].astype(np.uint64) << np.arange(eng.n_seq_max, dtype=np.uint64)).sum(axis=1)
-        assert np.array_equal(mask, bits.astype(np.uint64))
+        member = K.seqset_members(mask, K.MAX_SEQ)
+        assert np.array_equal(member[:, :eng.n_seq_max], eng.cells.member[s])
+        assert not member[:, eng.n_seq_max:].any()
 
 
 def shrink(wl, layers=1):
@@ -265,7 +266,7 @@ def test_error_codes():
     with pytest.raises(K.KvattnError):
         K.Context(1, 2, 1, 24, kv_size=8)                 # unsupported head_dim
     with pytest.raises(K.KvattnError):
-        K.Context(1, 2, 1, 16, kv_size=8, n_seq_max=65)   # more than 64 sequences
+        K.Context(1, 2, 1, 16, kv_size=8, n_seq_max=257)   # more than 256 sequences
     with pytest.raises(K.KvattnError):
         K.Context(1, 2, 1, 16, kv_size=4, cell_order=[0, 1, 1, 2])
 
@@ -326,7 +327,7 @@ def test_workspace_and_cache_bytes():
 
 
 @pytest.mark.parametrize("kw", [dict(head_dim=48), dict(n_head=3, n_head_kv=2), dict(n_head=32, n_head_kv=2),
-                                dict(n_seq_max=65), dict(kv_size=0), dict(split_mode=4), dict(split_mode=-1), dict(swa_window=-1),
+                                dict(n_seq_max=257), dict(kv_size=0), dict(split_mode=4), dict(split_mode=-1), dict(swa_window=-1),
                                 # one layer's K tensor at 2 GiB: 2^20 cells x 8 heads x 128 x 2 B
                                 dict(kv_size=1 << 20, n_head=8, n_head_kv=8, head_dim=128)])
 def test_create_rejects_bad_geometry(kw):
@@ -374,12 +375,18 @@ def test_random_batches_match_oracle(seed):
     (shared prefixes, ids spanning streams), random positions and output
     flags or auto-fill, every split strategy, one to four streams, shuffled
     free lists, partially stored splits (the unstored ubatches' cells are
-    released by the next split), retirements and full caches.  Every
-    ubatch's slots, positions, cells and copies, the status, output_ids and
-    the committed cell table must equal the oracle's after every step."""
+    released by the next split), retirements and full caches; half of the
+    seeds map the sequences to ids spread over [0, 256).  Every ubatch's
+    slots, positions, cells and copies, the status, output_ids and the
+    committed cell table must equal the oracle's after every step."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 77]))
+    irng = np.random.default_rng(np.random.SeedSequence([seed, 78]))
     n_stream = int(rng.choice([1, 2, 4]))
-    n_seq_max = int(rng.integers(2, 13))
+    n_seqs = int(rng.integers(2, 13))
+    n_seq_max, idmap = n_seqs, list(range(n_seqs))
+    if irng.random() < 0.5:                 # a wide id space
+        n_seq_max = int(irng.integers(65, K.MAX_SEQ + 1))
+        idmap = [int(x) for x in irng.choice(n_seq_max, size=n_seqs, replace=False)]
     kv_size = int(rng.choice([24, 48, 96]))
     n_batch = int(rng.choice([8, 16, 32]))
     n_ubatch = int(rng.choice([3, 4, 8, 16]))
@@ -391,10 +398,11 @@ def test_random_batches_match_oracle(seed):
     eng = OracleEngine(1, 2, 1, 16, kv_size, n_stream, n_seq_max, n_batch, n_ubatch, cell_order=order,
                        layers=[], split_mode=mode)
     nb = ctx.n_batch()
-    next_pos = [0] * n_seq_max
+    next_pos = [0] * n_seqs
     for step in range(12):
         if step and rng.random() < 0.25:
-            args = (int(rng.integers(-1, n_seq_max)), int(rng.integers(-1, 8)), int(rng.integers(-1, 40)))
+            who = int(rng.integers(-1, n_seqs))
+            args = (idmap[who] if who >= 0 else -1, int(rng.integers(-1, 8)), int(rng.integers(-1, 40)))
             ctx.seq_rm(*args)
             eng.seq_rm(*args)
             compare_tables(ctx, eng)
@@ -402,12 +410,12 @@ def test_random_batches_match_oracle(seed):
         n = int(rng.integers(0, nb + 1))
         seqs, pos = [], []
         for _ in range(n):
-            first = int(rng.integers(0, n_seq_max))
+            first = int(rng.integers(0, n_seqs))
             ids = [first]
             if rng.random() < 0.2:          # a shared slot: extra ids (possibly in other streams)
-                extra = rng.choice(n_seq_max, size=int(rng.integers(1, min(3, n_seq_max) + 1)), replace=False)
+                extra = rng.choice(n_seqs, size=int(rng.integers(1, min(3, n_seqs) + 1)), replace=False)
                 ids += [int(x) for x in extra if int(x) != first]
-            seqs.append(ids)
+            seqs.append([idmap[i] for i in ids])
             pos.append(next_pos[first] if rng.random() < 0.8 else int(rng.integers(0, 64)))
             next_pos[first] = pos[-1] + 1
         out = (rng.random(n) < 0.3).astype(np.int8).tolist()

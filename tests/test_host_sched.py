@@ -71,11 +71,11 @@ def compare_tables(ctx, eng, n_stream):
     for s in range(n_stream):
         pos, mask = ctx.cells(s)
         rpos = eng.cells.pos[s]
-        rmask = np.zeros(len(rpos), np.uint64)
-        for q in range(eng.cells.member.shape[2]):
-            rmask |= eng.cells.member[s][:, q].astype(np.uint64) << np.uint64(q)
+        nq = eng.cells.member.shape[2]
+        member = K.seqset_members(mask, K.MAX_SEQ)
         assert np.array_equal(pos, rpos)
-        assert np.array_equal(mask, rmask)
+        assert np.array_equal(member[:, :nq], eng.cells.member[s])
+        assert not member[:, nq:].any()
 
 
 def drive_both(stream, max_iters=5000):

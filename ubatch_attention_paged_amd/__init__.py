@@ -18,7 +18,7 @@ from .kvattn import (  # noqa: F401
     KVATTN_REQ_WAITING, KVATTN_REQ_RUNNING, KVATTN_REQ_DONE,
     kvattn_seq_state_size, kvattn_seq_state_save, kvattn_seq_state_load,
     kvattn_time_next_attend, KVATTN_KERNEL_MFMA, KVATTN_KERNEL_VALU, KVATTN_KERNEL_MERGE,
-    kvattn_probe_gather, kvattn_probe_mfma,
+    kvattn_probe_gather, kvattn_probe_mfma, MAX_SEQ, SEQ_WORDS, seqset_int, seqset_members,
 )
 
 load()

@@ -36,16 +36,16 @@ WsLayout ws_layout(const Geometry& g) {
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + bytes); return at; };
   L.cpos = take(sc * 4);
-  L.cmask = take(sc * 8);
+  L.cmask = take(sc * sizeof(SeqSet));
   L.cellcls = take(sc * 4);
   L.counts = take(static_cast<size_t>(kMaxClasses) * nseg * 4);
   L.csr_cell = take(sc * 4);
   L.csr_pos = take(sc * 4);
-  L.csr_mask = take(sc * 8);
+  L.csr_mask = take(sc * sizeof(SeqSet));
   const size_t ntile = sc / kTileCells + kMaxClasses + 1;   // each class adds at most one partial tile
   L.tile_min = take(ntile * 4);
   L.tile_max = take(ntile * 4);
-  L.arena_bytes = (16u << 20) + 48 * sc + 64 * static_cast<size_t>(g.n_ubatch);
+  L.arena_bytes = (16u << 20) + (32 + sizeof(CellUpdate)) * sc + 64 * static_cast<size_t>(g.n_ubatch);
   L.arena = take(L.arena_bytes);
   const size_t hd = static_cast<size_t>(g.n_head) * g.head_dim;
   L.part_acc = take(kPartialRowsCap * hd * 4);
@@ -140,7 +140,7 @@ int ensure_device(kvattn_ctx* c) {
   // empty device mirror: every cell free
   const size_t sc = static_cast<size_t>(c->core.geo().n_stream) * c->core.geo().kv_size;
   HIP_TRY(c, hipMemset(c->ws + c->wl.cpos, 0xFF, sc * 4));
-  HIP_TRY(c, hipMemset(c->ws + c->wl.cmask, 0, sc * 8));
+  HIP_TRY(c, hipMemset(c->ws + c->wl.cmask, 0, sc * sizeof(SeqSet)));
   HIP_TRY(c, hipDeviceSynchronize());
   c->dev_ready = true;
   return KVATTN_OK;
@@ -266,12 +266,12 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
   char* arena = c->arena();
   CsrArgs ca{};
   ca.cpos = c->dptr<int32_t>(c->wl.cpos);
-  ca.cmask = c->dptr<uint64_t>(c->wl.cmask);
+  ca.cmask = c->dptr<SeqSet>(c->wl.cmask);
   ca.cellcls = c->dptr<int32_t>(c->wl.cellcls);
   ca.counts = c->dptr<int32_t>(c->wl.counts);
   ca.csr_cell = c->dptr<int32_t>(c->wl.csr_cell);
   ca.csr_pos = c->dptr<int32_t>(c->wl.csr_pos);
-  ca.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);
+  ca.csr_mask = c->dptr<SeqSet>(c->wl.csr_mask);
   ca.n_updates = static_cast<int32_t>(c->upd.size());
   ca.n_classes = c->plan_ok ? static_cast<int32_t>(P0.classes.size()) : 0;
   ca.n_seg = P0.n_seg;
@@ -555,7 +555,7 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
   a.qslots = reinterpret_cast<const SlotInfo*>(arena + VL.qslots);
   a.csr_cell = c->dptr<int32_t>(c->wl.csr_cell);
   a.csr_pos = c->dptr<int32_t>(c->wl.csr_pos);
-  a.csr_mask = c->dptr<uint64_t>(c->wl.csr_mask);
+  a.csr_mask = c->dptr<SeqSet>(c->wl.csr_mask);
   a.tile_min = c->dptr<int32_t>(c->wl.tile_min);
   a.tile_max = c->dptr<int32_t>(c->wl.tile_max);
   // split-K partials: the workspace's region, or the caller's (the
@@ -662,7 +662,7 @@ int kvattn_get_mask(kvattn_ctx* c, const kvattn_ubatch* ub, void* d_mask, size_t
   if (static_cast<size_t>(T) * P.n_kv > cap_elems || !d_mask) return c->fail(KVATTN_EINVAL, "mask buffer too small");
   MaskArgs a{};
   a.cpos = c->dptr<int32_t>(c->wl.cpos);
-  a.cmask = c->dptr<uint64_t>(c->wl.cmask);
+  a.cmask = c->dptr<SeqSet>(c->wl.cmask);
   a.slots = reinterpret_cast<const SlotInfo*>(c->arena() + c->al.v[0].slots);
   a.mask = static_cast<uint16_t*>(d_mask);
   a.n_rows = T;
@@ -686,7 +686,8 @@ int kvattn_get_classes(kvattn_ctx* c, int32_t* n_classes, int32_t* cls_stream, u
   if (n_cells) *n_cells = P.total_cells;
   for (int32_t i = 0; i < std::min<int32_t>(cap_classes, static_cast<int32_t>(P.classes.size())); ++i) {
     if (cls_stream) cls_stream[i] = P.classes[i].stream;
-    if (cls_mask) cls_mask[i] = P.classes[i].mask;
+    if (cls_mask)
+      for (int w = 0; w < kSeqWords; ++w) cls_mask[static_cast<size_t>(i) * kSeqWords + w] = P.classes[i].mask.w[w];
     if (cls_count) cls_count[i] = P.classes[i].n_cells;
   }
   const int32_t n = std::min(cap_cells, P.total_cells);

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 Ks[2][KT * D];
   __shared__ __attribute__((aligned(16))) _Float16 Vs[2][KT * DP];
   __shared__ int32_t kpos_s[2][KT];
-  __shared__ uint64_t kmask_s[2][KT];
+  __shared__ uint64_t kmask_s[2][kSeqWords][KT];   // word-major: a row reads one word
 
   const int HK = a.n_head_kv;
   const int H = a.n_head;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
 
   // this lane's query rows: row block b of wavefront w is rows
   // 32 * (w * RB + b) .. +31, the lane owning row lane % 32 of it
-  int t_r[RB], h_r[RB], pos_lim[RB], pos_lo[RB], qseq[RB];
+  int t_r[RB], h_r[RB], pos_lim[RB], pos_lo[RB], qword[RB], qbit[RB];
   bool qvalid[RB];
   SlotInfo si[RB];
   bool any_row = false;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   // that tile, so no wait inside a tile's compute covers the loads in flight
   // (vmcnt retires in order: any wait would also wait for the next tile).
   int pk = INT32_MAX, nmin = 0, nmax = 0;
-  uint64_t mk = 0;
+  SeqSet mk = SeqSet::none();
   auto issue = [&](int tile, int bsel, const int* cells) {
     const int lim = it.c1 - (it.c0 + tile * KT);     // rows of this tile inside the list
     // a whole tile inside the list (wave-uniform) needs no per-row test;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
       const int idx = it.c0 + tile * KT + tid;
       const bool in = idx < it.c1;
       pk = in ? a.csr_pos[idx] : INT32_MAX;
-      mk = in ? a.csr_mask[idx] : 0ULL;
+      mk = in ? a.csr_mask[idx] : SeqSet::none();
     }
     nmin = a.tile_min[tb + tile];
     nmax = a.tile_max[tb + tile];
@@ -253,7 +253,8 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
   for (int b = 0; b < RB; ++b) {
     pos_lim[b] = a.causal ? si[b].pos : INT32_MAX - 1;     // largest visible cell position
     pos_lo[b] = SWA ? si[b].pos - a.swa + 1 : INT32_MIN;   // smallest, with a sliding window
-    qseq[b] = si[b].seq0;
+    qword[b] = si[b].seq0 >> 6;
+    qbit[b] = si[b].seq0 & 63;
     any_row |= qvalid[b];
   }
   const bool wave_rows = ballot(any_row) != 0ULL;   // wave-uniform: padding-only waves skip the math
@@ -360,7 +361,10 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
     // issued (vmcnt), positions and masks go through registers
     if (tid < KT) {
       kpos_s[buf][tid] = pk;
-      if constexpr (!PURE) kmask_s[buf][tid] = mk;
+      if constexpr (!PURE) {
+#pragma unroll
+        for (int wd = 0; wd < kSeqWords; ++wd) kmask_s[buf][wd][tid] = mk.w[wd];
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(256 / RB, 2 / RB) void k_attn_mfma(AttnArgs a) {
           const int key = kb * 32 + acc_row(e, lane);
           const int kp = kpos_s[buf][key];
           bool vis = kp <= pos_lim[b];
-          if constexpr (!PURE) vis &= static_cast<bool>((kmask_s[buf][key] >> qseq[b]) & 1ULL);
+          if constexpr (!PURE) vis &= static_cast<bool>((kmask_s[buf][qword[b]][key] >> qbit[b]) & 1ULL);
           if constexpr (SWA) vis &= kp >= pos_lo[b];
           sb[e] = vis ? sb[e] : -INFINITY;
         }

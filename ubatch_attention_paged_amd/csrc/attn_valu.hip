@@ -102,7 +102,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
 
   // Software pipeline over this wavefront's steps (U cells each): while
   // step s computes, the K/V rows of step s+1 and the list entries (cell,
-  // position, sequence set) of step s+2 are in flight.  Two register sets
+  // position, and the word of its sequence set that holds the row's
+  // sequence) of step s+2 are in flight.  Two register sets
   // A/B alternate; visibility is decided when a step's rows are issued, so
   // its list entries are dead by then.
   int lc[U], lp[U];
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
       const int idx = min(c + half * U + u, last);
       lc[u] = a.csr_cell[idx];
       lp[u] = a.csr_pos[idx];
-      lm[u] = check_mask ? a.csr_mask[idx] : ~0ULL;
+      lm[u] = check_mask ? a.csr_mask[idx].w[si.seq0 >> 6] : ~0ULL;
     }
   };
   auto issue = [&](int c, half8 (&kr)[U][2], half8 (&vr)[U][2], bool (&vis)[U]) {
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a) {
       const half8* vp = reinterpret_cast<const half8*>(Vl + off);
       kr[u][0] = kp[0]; kr[u][1] = kp[1];
       vr[u][0] = vp[0]; vr[u][1] = vp[1];
-      vis[u] = c + half * U + u < it.c1 && (!a.causal || lp[u] <= si.pos) && ((lm[u] >> si.seq0) & 1ULL) &&
+      vis[u] = c + half * U + u < it.c1 && (!a.causal || lp[u] <= si.pos) && ((lm[u] >> (si.seq0 & 63)) & 1ULL) &&
                (a.swa == 0 || si.pos - lp[u] < a.swa);
     }
   };

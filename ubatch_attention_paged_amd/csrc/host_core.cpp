@@ -9,7 +9,6 @@ namespace kvattn {
 
 namespace {
 
-inline int lowest_bit(uint64_t m) { return __builtin_ctzll(m); }
 inline int32_t ceil_div(int64_t a, int64_t b) { return static_cast<int32_t>((a + b - 1) / b); }
 inline int32_t round_up(int64_t a, int64_t b) { return static_cast<int32_t>(ceil_div(a, b) * b); }
 constexpr int32_t kNkvQuantum = 256;   // n_pad floor of get_n_kv
@@ -35,7 +34,7 @@ int make_geometry(const kvattn_params& p, Geometry& g, std::string& err) {
     return KVATTN_EINVAL;
   }
   if (p.kv_size <= 0 || p.n_stream <= 0 || p.n_seq_max <= 0 || p.n_seq_max > kMaxSeq) {
-    err = "kv_size and n_stream must be positive and 0 < n_seq_max <= 64";
+    err = "kv_size and n_stream must be positive and 0 < n_seq_max <= " + std::to_string(kMaxSeq);
     return KVATTN_EINVAL;
   }
   if (static_cast<int64_t>(p.kv_size) * p.n_stream > (1LL << 30)) {
@@ -85,10 +84,12 @@ int HostCore::init(const kvattn_params& p, std::string& err) {
   for (int s = 0; s < g_.n_stream; ++s) {
     Stream& S = st_[s];
     S.pos.assign(g_.kv_size, -1);
-    S.mask.assign(g_.kv_size, 0);
+    S.mask.assign(g_.kv_size, SeqSet::none());
     S.rank_of.assign(g_.kv_size, -1);
     S.cell_at.assign(g_.kv_size, 0);
     S.avail.assign(g_.kv_size, 1);
+    S.seq_bits.assign(g_.n_seq_max, {});
+    S.seq_n.assign(g_.n_seq_max, 0);
     for (int32_t r = 0; r < g_.kv_size; ++r) {
       const int32_t c = p.cell_order ? p.cell_order[static_cast<int64_t>(s) * g_.kv_size + r] : r;
       if (c < 0 || c >= g_.kv_size || S.rank_of[c] != -1) {
@@ -151,31 +152,32 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
   }
   // -- sequence ids: first listed id first, the rest ascending, duplicates dropped
   std::vector<int32_t> beg(n + 1, 0);
-  std::vector<uint64_t> setmask(n, 0);
+  std::vector<SeqSet> setmask(n, SeqSet::none());
   seq_flat_.clear();
   for (int32_t i = 0; i < n; ++i) {
     beg[i] = static_cast<int32_t>(seq_flat_.size());
     if (!b.seq_id) {
       seq_flat_.push_back(0);
-      setmask[i] = 1;
+      setmask[i] = SeqSet::one(0);
     } else {
       const int32_t k = b.n_seq_id ? b.n_seq_id[i] : 1;
       if (k < 1 || !b.seq_id[i]) {
         err = "slot " + std::to_string(i) + ": needs at least one sequence id";
         return KVATTN_EINVAL;
       }
-      uint64_t m = 0;
+      SeqSet m = SeqSet::none();
       for (int32_t t = 0; t < k; ++t) {
         const int32_t s = b.seq_id[i][t];
         if (s < 0 || s >= g_.n_seq_max) {
           err = "slot " + std::to_string(i) + ": sequence id " + std::to_string(s) + " outside [0, n_seq_max)";
           return KVATTN_EINVAL;
         }
-        m |= 1ULL << s;
+        m.set(s);
       }
       const int32_t first = b.seq_id[i][0];
       seq_flat_.push_back(first);
-      for (uint64_t r = m & ~(1ULL << first); r; r &= r - 1) seq_flat_.push_back(lowest_bit(r));
+      for (int q = m.lowest(); q >= 0; q = m.next(q))
+        if (q != first) seq_flat_.push_back(q);
       setmask[i] = m;
     }
   }
@@ -193,15 +195,12 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
       pos[i] = b.pos[i];
     }
   } else if (n > 0) {
-    std::vector<int32_t> next(g_.n_seq_max, 0);
-    for (auto& S : st_)
-      for (int32_t j = 0; j < g_.kv_size; ++j)
-        if (S.pos[j] >= 0)
-          for (uint64_t m = S.mask[j]; m; m &= m - 1) {
-            const int q = lowest_bit(m);
-            next[q] = std::max(next[q], S.pos[j] + 1);
-          }
-    for (int32_t i = 0; i < n; ++i) pos[i] = next[seq0(i)]++;
+    std::vector<int32_t> next(g_.n_seq_max, -1);   // -1: not looked up yet
+    for (int32_t i = 0; i < n; ++i) {
+      int32_t& nx = next[seq0(i)];
+      if (nx < 0) nx = seq_pos_max(seq0(i)) + 1;
+      pos[i] = nx++;
+    }
   }
   std::vector<int8_t> out(n, 0);
   if (b.output) {
@@ -224,7 +223,7 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
     while (true) {
       while (first < n && used[first]) ++first;
       if (first == n) break;
-      const uint64_t set = setmask[first];
+      const SeqSet set = setmask[first];
       Part p;
       for (int32_t i = first; i < n && static_cast<int32_t>(p.slots.size()) < U; ++i)
         if (!used[i] && setmask[i] == set) {
@@ -252,10 +251,10 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
     std::vector<uint8_t> used(n, 0);
     int32_t left = n;
     while (left > 0) {
-      std::vector<uint64_t> sets;
-      uint64_t uni = 0;
+      std::vector<SeqSet> sets;
+      SeqSet uni = SeqSet::none();
       for (int32_t i = 0; i < n && static_cast<int32_t>(sets.size()) < U; ++i) {
-        if (used[i] || (setmask[i] & uni)) continue;
+        if (used[i] || (setmask[i] & uni).any()) continue;
         sets.push_back(setmask[i]);
         uni |= setmask[i];
       }
@@ -270,7 +269,7 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
       std::vector<size_t> order(sets.size());
       std::iota(order.begin(), order.end(), 0);
       std::sort(order.begin(), order.end(),
-                [&](size_t a, size_t c) { return lowest_bit(sets[a]) < lowest_bit(sets[c]); });
+                [&](size_t a, size_t c) { return sets[a].lowest() < sets[c].lowest(); });
       Part p;
       for (size_t k : order)
         for (int32_t t = 0; t < nst; ++t) {
@@ -292,12 +291,12 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
   // ("What does llama.cpp's KV cache ...", "Unified versus non-unified":
   // common prefixes need separate copies) a slot whose ids span streams also
   // gets one cell in each other stream, holding the ids that live there.
-  std::vector<uint64_t> smask(g_.n_stream, 0);       // ids of each stream
-  for (int32_t q = 0; q < g_.n_seq_max; ++q) smask[q % g_.n_stream] |= 1ULL << q;
+  std::vector<SeqSet> smask(g_.n_stream, SeqSet::none());   // ids of each stream
+  for (int32_t q = 0; q < g_.n_seq_max; ++q) smask[q % g_.n_stream].set(q);
   std::vector<int32_t> need(g_.n_stream, 0);
   for (int32_t i = 0; i < n; ++i)
     for (int s = 0; s < g_.n_stream; ++s)
-      if (setmask[i] & smask[s]) ++need[s];
+      if ((setmask[i] & smask[s]).any()) ++need[s];
   for (int s = 0; s < g_.n_stream; ++s)
     if (need[s] > st_[s].n_avail) {
       err = "no free cells: stream " + std::to_string(s) + " needs " + std::to_string(need[s]) +
@@ -309,7 +308,7 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
     u.id = next_id_++;
     u.n_seq_tokens = p.nst;
     u.n_seqs = p.ns;
-    uint64_t unq = 0;
+    SeqSet unq = SeqSet::none();
     for (int32_t i : p.slots) {
       const int s = seq0(i) % g_.n_stream;
       u.src.push_back(i);
@@ -322,7 +321,7 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
       u.stream.push_back(s);
       u.cells.push_back(pop_cell(s));
       for (int s2 = 0; s2 < g_.n_stream; ++s2) {
-        if (s2 == s || !(setmask[i] & smask[s2])) continue;
+        if (s2 == s || !(setmask[i] & smask[s2]).any()) continue;
         u.copy_src.push_back(static_cast<int32_t>(u.src.size()) - 1);
         u.copy_stream.push_back(s2);
         u.copy_cell.push_back(pop_cell(s2));
@@ -330,7 +329,7 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
       }
       unq |= setmask[i];
     }
-    for (uint64_t m = unq; m; m &= m - 1) u.seq_unq.push_back(lowest_bit(m));
+    for (int q = unq.lowest(); q >= 0; q = unq.next(q)) u.seq_unq.push_back(q);
     ubs_.push_back(std::move(u));
   }
   if (output_ids) {
@@ -342,15 +341,42 @@ int HostCore::split(const kvattn_batch& b, int32_t* output_ids, std::string& err
 
 // ---- cell table ------------------------------------------------------------
 
-void HostCore::set_cell(int s, int32_t cell, int32_t pos, uint64_t mask) {
+template <class F>
+void HostCore::for_seq_cells(int s, int32_t seq, F&& f) const {
+  const Stream& S = st_[s];
+  if (S.seq_n[seq] == 0) return;
+  const std::vector<uint64_t>& bits = S.seq_bits[seq];
+  const int32_t nw = (S.umax + 63) / 64;   // no cell at or past umax is occupied
+  for (int32_t wi = 0; wi < nw; ++wi)
+    for (uint64_t m = bits[wi]; m; m &= m - 1) f(64 * wi + __builtin_ctzll(m));
+}
+
+void HostCore::set_cell(int s, int32_t cell, int32_t pos, const SeqSet& mask) {
   Stream& S = st_[s];
+  // an empty cell holds the empty set, so the old set is always S.mask[cell]
+  const SeqSet& old = S.mask[cell];
+  const uint64_t bit = 1ULL << (cell & 63);
+  for (int wd = 0; wd < kSeqWords; ++wd) {
+    for (uint64_t gone = old.w[wd] & ~mask.w[wd]; gone; gone &= gone - 1) {
+      const int q = 64 * wd + __builtin_ctzll(gone);
+      S.seq_bits[q][cell >> 6] &= ~bit;
+      --S.seq_n[q];
+    }
+    for (uint64_t came = mask.w[wd] & ~old.w[wd]; came; came &= came - 1) {
+      const int q = 64 * wd + __builtin_ctzll(came);
+      if (S.seq_bits[q].empty()) S.seq_bits[q].assign((g_.kv_size + 63) / 64, 0);
+      S.seq_bits[q][cell >> 6] |= bit;
+      ++S.seq_n[q];
+    }
+  }
   if (S.pos[cell] >= 0) {
     auto it = S.count.find(S.mask[cell]);
     if (it != S.count.end() && --it->second == 0) S.count.erase(it);
   }
-  S.pos[cell] = mask ? pos : -1;
-  S.mask[cell] = mask ? mask : 0;
-  if (mask) {
+  const bool occupied = mask.any();
+  S.pos[cell] = occupied ? pos : -1;
+  S.mask[cell] = mask;
+  if (occupied) {
     ++S.count[mask];
     S.umax = std::max(S.umax, cell + 1);
   } else {
@@ -380,7 +406,7 @@ int HostCore::commit(int k, std::vector<CellUpdate>* upd, std::string& err) {
     for (int32_t idx : pending_) {
       const Stream& S = st_[idx / g_.kv_size];
       const int32_t j = idx % g_.kv_size;
-      upd->push_back(CellUpdate{idx, S.pos[j], S.mask[j]});
+      upd->push_back(CellUpdate{S.mask[j], idx, S.pos[j], {0, 0}});
     }
   }
   pending_.clear();
@@ -390,19 +416,27 @@ int HostCore::commit(int k, std::vector<CellUpdate>* upd, std::string& err) {
 int HostCore::seq_rm(int32_t seq, int32_t p0, int32_t p1) {
   if (seq >= g_.n_seq_max) return KVATTN_EINVAL;
   const int32_t lo = p0 < 0 ? 0 : p0;
+  auto in_range = [&](int32_t p) { return p >= lo && (p1 < 0 || p < p1); };
   for (int s = 0; s < g_.n_stream; ++s) {
     Stream& S = st_[s];
-    const int32_t end = S.umax;           // every cell at or past umax is empty
-    for (int32_t j = 0; j < end; ++j) {
-      const int32_t p = S.pos[j];
-      if (p < 0 || p < lo || (p1 >= 0 && p >= p1)) continue;
-      uint64_t m = S.mask[j];
-      if (seq < 0) m = 0;
-      else if (m >> seq & 1) m &= ~(1ULL << seq);
-      else continue;
-      set_cell(s, j, p, m);
-      if (!m) push_cell(s, j);
+    if (seq < 0) {
+      const int32_t end = S.umax;         // every cell at or past umax is empty
+      for (int32_t j = 0; j < end; ++j) {
+        const int32_t p = S.pos[j];
+        if (p < 0 || !in_range(p)) continue;
+        set_cell(s, j, p, SeqSet::none());
+        push_cell(s, j);
+      }
+      continue;
     }
+    for_seq_cells(s, seq, [&](int32_t j) {
+      const int32_t p = S.pos[j];
+      if (!in_range(p)) return;
+      SeqSet m = S.mask[j];
+      m.reset(seq);
+      set_cell(s, j, p, m);
+      if (!m.any()) push_cell(s, j);
+    });
   }
   latest_ = -1;                       // the device mirror is stale until the next commit
   return KVATTN_OK;
@@ -415,8 +449,7 @@ int HostCore::seq_cells(int32_t seq, std::vector<int32_t>& cells, std::vector<in
   const int s = seq % g_.n_stream;
   const Stream& S = st_[s];
   std::vector<std::pair<int32_t, int32_t>> v;
-  for (int32_t j = 0; j < S.umax; ++j)
-    if (S.pos[j] >= 0 && (S.mask[j] >> seq & 1)) v.push_back({S.pos[j], j});
+  for_seq_cells(s, seq, [&](int32_t j) { v.push_back({S.pos[j], j}); });
   std::sort(v.begin(), v.end());
   for (const auto& pc : v) {
     pos.push_back(pc.first);
@@ -438,10 +471,9 @@ int HostCore::seq_restore(int32_t seq, const int32_t* pos, int32_t n, std::vecto
     }
   const int s = seq % g_.n_stream;
   Stream& S = st_[s];
-  const uint64_t bit = 1ULL << seq;
+  const SeqSet bit = SeqSet::one(seq);
   int32_t own = 0;
-  for (int32_t j = 0; j < S.umax; ++j)
-    if (S.pos[j] >= 0 && S.mask[j] == bit) ++own;
+  for_seq_cells(s, seq, [&](int32_t j) { own += S.mask[j] == bit; });
   if (S.n_avail + own < n) {
     err = "no room in the stream for the saved cells";
     return KVATTN_NO_SLOT;
@@ -459,9 +491,8 @@ int HostCore::seq_restore(int32_t seq, const int32_t* pos, int32_t n, std::vecto
 int32_t HostCore::seq_pos_max(int32_t seq) const {
   if (seq < 0 || seq >= g_.n_seq_max) return -1;
   int32_t best = -1;
-  for (const auto& S : st_)
-    for (int32_t j = 0; j < S.umax; ++j)
-      if (S.pos[j] >= 0 && (S.mask[j] >> seq & 1)) best = std::max(best, S.pos[j]);
+  for (int s = 0; s < g_.n_stream; ++s)
+    for_seq_cells(s, seq, [&](int32_t j) { best = std::max(best, st_[s].pos[j]); });
   return best;
 }
 
@@ -478,7 +509,9 @@ int32_t HostCore::n_kv() const {
 void HostCore::get_cells(int32_t s, int32_t* pos, uint64_t* mask) const {
   const Stream& S = st_[s];
   if (pos) std::copy(S.pos.begin(), S.pos.end(), pos);
-  if (mask) std::copy(S.mask.begin(), S.mask.end(), mask);
+  if (mask)
+    for (size_t j = 0; j < S.mask.size(); ++j)
+      for (int i = 0; i < kSeqWords; ++i) mask[j * kSeqWords + i] = S.mask[j].w[i];
 }
 
 // ---- work plan -------------------------------------------------------------
@@ -503,15 +536,15 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   const int32_t NQ = static_cast<int32_t>(P.slots.size());
   // classes come from every slot of the ubatch, so both plan variants (all
   // rows / output rows only) share one class table and one set of lists
-  std::vector<uint64_t> qseqs(S, 0);
-  for (int32_t i = 0; i < T; ++i) qseqs[u.stream[i]] |= 1ULL << u.seq_ptr[i][0];
+  std::vector<SeqSet> qseqs(S, SeqSet::none());
+  for (int32_t i = 0; i < T; ++i) qseqs[u.stream[i]].set(u.seq_ptr[i][0]);
 
   // classes: the committed sequence sets of each stream that some query can see
-  std::vector<std::vector<std::pair<uint64_t, int32_t>>> rel(S);
+  std::vector<std::vector<std::pair<SeqSet, int32_t>>> rel(S);
   size_t n_rel = 0;
   for (int s = 0; s < S; ++s) {
     for (const auto& kv : st_[s].count)
-      if (kv.second > 0 && (kv.first & qseqs[s])) rel[s].push_back(kv);
+      if (kv.second > 0 && (kv.first & qseqs[s]).any()) rel[s].push_back(kv);
     std::sort(rel[s].begin(), rel[s].end());
     n_rel += rel[s].size();
   }
@@ -532,13 +565,13 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
       } else {
         if (merged < 0) {
           merged = static_cast<int32_t>(P.classes.size());
-          P.classes.push_back(ClassInfo{0, s, 0, 0, 0, 0, 0, 0, 0});
+          P.classes.push_back(ClassInfo{SeqSet::none(), s, 0, 0, 0, 0, 0, 0, 0});
         }
         c = merged;
         P.classes[c].mask |= kv.first;
         P.classes[c].n_cells += kv.second;
       }
-      P.lookup.push_back(LookupEntry{kv.first, c, 0});
+      P.lookup.push_back(LookupEntry{kv.first, c, {0, 0, 0}});
     }
   }
   P.lookup_off[S] = static_cast<int32_t>(P.lookup.size());
@@ -565,7 +598,7 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   for (auto& c : P.classes) {
     c.q_off = static_cast<int32_t>(P.qlist.size());
     for (int32_t q : qorder)
-      if (P.slots[q].stream == c.stream && (c.mask >> P.slots[q].seq0 & 1)) P.qlist.push_back(q);
+      if (P.slots[q].stream == c.stream && c.mask.test(P.slots[q].seq0)) P.qlist.push_back(q);
     c.n_q = static_cast<int32_t>(P.qlist.size()) - c.q_off;
   }
 

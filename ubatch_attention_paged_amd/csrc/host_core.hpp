@@ -34,11 +34,11 @@ struct UbatchRec {
   int32_t id = 0;
   int32_t n_seq_tokens = 0, n_seqs = 0;
   std::vector<int32_t> src, pos, n_seq_id, stream, cells, seq_unq;
-  std::vector<uint64_t> setmask;      // ids of the slot that live in its own stream (its cell's set)
+  std::vector<SeqSet> setmask;        // ids of the slot that live in its own stream (its cell's set)
   // separate copies: a slot whose ids span several streams also gets a cell
   // in each other stream, holding the ids that live there
   std::vector<int32_t> copy_src, copy_stream, copy_cell;   // copy_src = slot index in this ubatch
-  std::vector<uint64_t> copy_mask;
+  std::vector<SeqSet> copy_mask;
   std::vector<const int32_t*> seq_ptr;
   std::vector<int8_t> output;
   int32_t n_outputs = 0;
@@ -92,6 +92,7 @@ class HostCore {
   int seq_restore(int32_t seq, const int32_t* pos, int32_t n, std::vector<int32_t>& cells, std::string& err);
   int32_t seq_pos_max(int32_t seq) const;
   int32_t n_kv() const;
+  // mask: kSeqWords words per cell (the set's bits, id q in word q / 64, bit q % 64)
   void get_cells(int32_t s, int32_t* pos, uint64_t* mask) const;
 
   // limits used by the planner (bounded by the workspace)
@@ -100,16 +101,25 @@ class HostCore {
  private:
   struct Stream {
     std::vector<int32_t> pos;         // -1 empty
-    std::vector<uint64_t> mask;
+    std::vector<SeqSet> mask;
     std::vector<int32_t> rank_of, cell_at;
     std::vector<uint8_t> avail;       // by rank: free and not reserved
     int32_t hint = 0, n_avail = 0, umax = 0;   // umax = used_max_p1
-    std::unordered_map<uint64_t, int32_t> count;   // committed cells per set
+    std::unordered_map<SeqSet, int32_t, SeqSetHash> count;   // committed cells per set
+    // per sequence: which cells hold it (bit j of the bitmap = cell j; the
+    // bitmap is allocated on the sequence's first cell in this stream) and
+    // how many, so that per-sequence queries visit that sequence's cells only
+    std::vector<std::vector<uint64_t>> seq_bits;
+    std::vector<int32_t> seq_n;
   };
+  // calls f(cell) for each cell of stream s that holds seq, ascending; f may
+  // change the cell table
+  template <class F>
+  void for_seq_cells(int s, int32_t seq, F&& f) const;
   int32_t pop_cell(int s);
   void push_cell(int s, int32_t cell);
   void release_uncommitted();
-  void set_cell(int s, int32_t cell, int32_t pos, uint64_t mask);
+  void set_cell(int s, int32_t cell, int32_t pos, const SeqSet& mask);
 
   Geometry g_;
   std::vector<Stream> st_;

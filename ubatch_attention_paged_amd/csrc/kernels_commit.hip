@@ -73,11 +73,11 @@ __global__ __launch_bounds__(256) void k_csr_classify(CsrArgs a) {
   if (j < a.n_kv) {
     const int64_t idx = static_cast<int64_t>(s) * a.kv_size + j;
     if (a.cpos[idx] >= 0) {
-      const uint64_t m = a.cmask[idx];
+      const SeqSet m = a.cmask[idx];
       int lo = a.lookup_off[s], hi = a.lookup_off[s + 1] - 1;
       while (lo <= hi) {
         const int mid = (lo + hi) >> 1;
-        const uint64_t mm = a.lookup[mid].mask;
+        const SeqSet mm = a.lookup[mid].mask;
         if (mm == m) { cls = a.lookup[mid].cls; break; }
         if (mm < m) lo = mid + 1; else hi = mid - 1;
       }
@@ -204,19 +204,17 @@ KVATTN_DEV void commit_small(const CsrArgs& a) {
   __syncthreads();
   if (nc == 0) return;
   const int total = a.n_stream * a.n_kv;
-  // every cell this thread will place (cell tid + 256 k), read once: its
-  // position, sequence set and class stay in registers
+  // every cell this thread will place (cell tid + 256 k): its position and
+  // class stay in registers; its sequence set is read for the class lookup
+  // and again when the cell is written to its list
   int pos_r[KMAX], cls_r[KMAX];
-  uint64_t msk_r[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     const int i = tid + 256 * k;
     pos_r[k] = -1;
-    msk_r[k] = 0;
     if (i < total) {
       const int64_t idx = static_cast<int64_t>(i / a.n_kv) * a.kv_size + i % a.n_kv;
       pos_r[k] = a.cpos[idx];
-      msk_r[k] = a.cmask[idx];
     }
   }
 #pragma unroll
@@ -225,12 +223,13 @@ KVATTN_DEV void commit_small(const CsrArgs& a) {
     const int i = tid + 256 * k;
     if (i < total && pos_r[k] >= 0) {
       const int s = i / a.n_kv;
+      const SeqSet m = a.cmask[static_cast<int64_t>(s) * a.kv_size + i % a.n_kv];
       int lo = lko[s], hi = lko[s + 1] - 1;
       while (lo <= hi) {
         const int mid = (lo + hi) >> 1;
-        const uint64_t mm = lk[mid].mask;
-        if (mm == msk_r[k]) { cls = lk[mid].cls; break; }
-        if (mm < msk_r[k]) lo = mid + 1; else hi = mid - 1;
+        const SeqSet mm = lk[mid].mask;
+        if (mm == m) { cls = lk[mid].cls; break; }
+        if (mm < m) lo = mid + 1; else hi = mid - 1;
       }
     }
     cls_r[k] = cls;
@@ -257,9 +256,10 @@ KVATTN_DEV void commit_small(const CsrArgs& a) {
       int dst = base[cls] + rank;
       for (int w2 = 0; w2 < w; ++w2) dst += wc[w2][cls];
       if (dst < a.csr_cap) {
-        a.csr_cell[dst] = (tid + 256 * k) % a.n_kv;
+        const int i = tid + 256 * k;
+        a.csr_cell[dst] = i % a.n_kv;
         a.csr_pos[dst] = pos_r[k];
-        a.csr_mask[dst] = msk_r[k];
+        a.csr_mask[dst] = a.cmask[static_cast<int64_t>(i / a.n_kv) * a.kv_size + i % a.n_kv];
       }
     }
     __syncthreads();
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(256) void k_mask_dense(MaskArgs a) {
   const SlotInfo q = a.slots[i];
   const int64_t idx = static_cast<int64_t>(q.stream) * a.kv_size + j;
   const int32_t p = a.cpos[idx];
-  const bool vis = p >= 0 && ((a.cmask[idx] >> q.seq0) & 1ULL) && (!a.causal || p <= q.pos) &&
+  const bool vis = p >= 0 && a.cmask[idx].test(q.seq0) && (!a.causal || p <= q.pos) &&
                    (a.swa == 0 || q.pos - p < a.swa);
   a.mask[static_cast<int64_t>(i) * a.n_kv + j] = vis ? 0x0000 : 0xFC00;
 }

@@ -24,12 +24,12 @@ struct StoreArgs {
 
 struct CsrArgs {
   int32_t* cpos;              // [S * C] device mirror: position, -1 empty
-  uint64_t* cmask;            // [S * C] sequence-set bitmask
+  SeqSet* cmask;              // [S * C] sequence set of each cell
   int32_t* cellcls;           // [S * C] class of each cell (-1 none), scratch
   int32_t* counts;            // [n_classes * n_seg] per segment counts, then offsets
   int32_t* csr_cell;          // [total] cells, class-major, ascending within a class
   int32_t* csr_pos;
-  uint64_t* csr_mask;
+  SeqSet* csr_mask;
   const ClassInfo* classes;
   const LookupEntry* lookup;
   const int32_t* lookup_off;  // [S + 1]
@@ -59,7 +59,7 @@ struct AttnArgs {
   const WorkItem* items;
   const int32_t* csr_cell;
   const int32_t* csr_pos;
-  const uint64_t* csr_mask;
+  const SeqSet* csr_mask;
   const int32_t* tile_min;
   const int32_t* tile_max;
   float* part_acc;            // [n_il][rows][n_head * head_dim]
@@ -80,7 +80,7 @@ struct AttnArgs {
 
 struct MaskArgs {
   const int32_t* cpos;
-  const uint64_t* cmask;
+  const SeqSet* cmask;
   const SlotInfo* slots;      // ubatch order
   uint16_t* mask;             // [n_rows][n_kv]
   int32_t n_rows, n_kv, kv_size, causal, swa;

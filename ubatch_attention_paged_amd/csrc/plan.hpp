@@ -12,9 +12,10 @@
 
 #include <cstdint>
 
+#include "seqset.hpp"
+
 namespace kvattn {
 
-constexpr int kMaxSeq = 64;            // sequence ids are bits of a uint64_t
 constexpr int kMaxLayersPerLaunch = 32;
 constexpr int kMaxClasses = 1024;      // per ubatch; extra sequence sets are merged
 constexpr int kSegCells = 64;          // cells per counting segment (one wavefront)
@@ -55,19 +56,20 @@ struct SlotInfo {        // one query slot
 };
 
 struct CellUpdate {      // one cell of the device mirror to overwrite
+  SeqSet mask;           // sequence set
   int32_t idx;           // stream * kv_size + cell
   int32_t pos;           // -1 = empty
-  uint64_t mask;         // sequence-set bitmask
+  int32_t pad[2];
 };
 
 struct LookupEntry {     // sorted by (stream, mask); maps a cell's set to its class
-  uint64_t mask;
+  SeqSet mask;
   int32_t cls;
-  int32_t pad;
+  int32_t pad[3];
 };
 
 struct ClassInfo {
-  uint64_t mask;         // OR of the member sets
+  SeqSet mask;           // OR of the member sets
   int32_t stream;
   int32_t n_cells;
   int32_t cell_off;      // first entry in the csr arrays

@@ -6,9 +6,9 @@
 // The pages ask the per-iteration host work to stay well inside one forward
 // pass and to keep memory allocation off that path ("What the loop costs
 // elsewhere"): every table of the scheduler is sized at create, and one
-// step touches only the running sequences (at most n_seq_max <= 64) and the
+// step touches only the running sequences (at most n_seq_max <= 256) and the
 // waiting requests it admits, plus one kvattn_seq_rm per retired or
-// preempted sequence.
+// preempted sequence, which visits only that sequence's cells.
 #include <algorithm>
 #include <cstring>
 #include <new>

@@ -30,7 +30,8 @@ KVATTN_REQ_WAITING, KVATTN_REQ_RUNNING, KVATTN_REQ_DONE = 0, 1, 2
 KVATTN_PREEMPT_RECOMPUTE, KVATTN_PREEMPT_SWAP = 0, 1
 KVATTN_KERNEL_MFMA, KVATTN_KERNEL_VALU, KVATTN_KERNEL_MERGE = 0, 1, 2
 PREEMPT_MODES = {"recompute": KVATTN_PREEMPT_RECOMPUTE, "swap": KVATTN_PREEMPT_SWAP}
-MAX_SEQ = 64
+MAX_SEQ = 256
+SEQ_WORDS = 4          # a sequence set is 4 uint64 words: id q is bit q % 64 of word q // 64
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u64p = ctypes.POINTER(ctypes.c_uint64)
@@ -368,7 +369,7 @@ def kvattn_get_classes(ctx, stream=0):
         raise KvattnError(rc, kvattn_last_error(ctx))
     k, n = ncls.value, ncells.value
     st = np.zeros(max(1, k), np.int32)
-    mk = np.zeros(max(1, k), np.uint64)
+    mk = np.zeros((max(1, k), SEQ_WORDS), np.uint64)
     ct = np.zeros(max(1, k), np.int32)
     cells = np.zeros(max(1, n), np.int32)
     rc = lib.kvattn_get_classes(ctx, ctypes.byref(ncls), st.ctypes.data_as(_i32p), mk.ctypes.data_as(_u64p),
@@ -378,14 +379,28 @@ def kvattn_get_classes(ctx, stream=0):
         raise KvattnError(rc, kvattn_last_error(ctx))
     out, off = [], 0
     for i in range(k):
-        out.append((int(st[i]), int(mk[i]), cells[off:off + ct[i]].copy()))
+        out.append((int(st[i]), seqset_int(mk[i]), cells[off:off + ct[i]].copy()))
         off += ct[i]
     return out
 
 
+def seqset_int(words):
+    """A sequence set (SEQ_WORDS uint64 words) as one Python integer: bit q
+    set when sequence q is a member."""
+    return sum(int(w) << (64 * j) for j, w in enumerate(words))
+
+
+def seqset_members(mask, n_seq):
+    """Membership table [n, n_seq] (bool) of n sequence sets given as an
+    [n, SEQ_WORDS] uint64 array."""
+    q = np.arange(n_seq)
+    return ((mask[:, q // 64] >> (q % 64).astype(np.uint64)) & np.uint64(1)).astype(bool)
+
+
 def kvattn_get_cells(ctx, stream: int, kv_size: int):
+    """(pos [kv_size] int32, mask [kv_size, SEQ_WORDS] uint64) of one stream."""
     pos = np.zeros(kv_size, np.int32)
-    mask = np.zeros(kv_size, np.uint64)
+    mask = np.zeros((kv_size, SEQ_WORDS), np.uint64)
     rc = load().kvattn_get_cells(ctx, stream, pos.ctypes.data_as(_i32p), mask.ctypes.data_as(_u64p))
     if rc != 0:
         raise KvattnError(rc, "kvattn_get_cells")
