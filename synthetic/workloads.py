@@ -213,6 +213,47 @@ def prefix_decode(n_seq=32, prefix=2048, private=256, n_layer=28, kv_size=16384,
                     note=f"{n_seq} sequences share {prefix} cells, {private} private each")
 
 
+def many_sequences(n_seq=256, group=8, prefix=24, private=(3, 40), n_shared=0, shared_size=8, n_layer=1,
+                   kv_size=16384, seed=1007):
+    """Many live sequences at once: groups of ``group`` sequences share a
+    prefix stored once (cells holding ``group`` ids), every sequence then
+    gets a private prompt of random length, and ``n_shared`` further slots
+    each hold ``shared_size`` random sequences (so one decode ubatch sees up
+    to n_shared more distinct sequence sets, each read by several queries).
+    Then two measured steps of one decode token per sequence."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, PURPOSE_STRUCTURE]))
+    next_pos = [0] * n_seq
+    batches = []
+    pos, seqs = [], []
+    for g0 in range(0, n_seq, group):
+        ids = tuple(range(g0, min(n_seq, g0 + group)))
+        pos += list(range(prefix))
+        seqs += [ids] * prefix
+        for i in ids:
+            next_pos[i] = prefix
+    lens = rng.integers(private[0], private[1], size=n_seq, endpoint=True)
+    for i in range(n_seq):
+        pos += list(range(next_pos[i], next_pos[i] + int(lens[i])))
+        seqs += [(i,)] * int(lens[i])
+        next_pos[i] += int(lens[i])
+    for _ in range(n_shared):
+        ids = tuple(int(x) for x in rng.choice(n_seq, size=shared_size, replace=False))
+        p = max(next_pos[i] for i in ids)
+        pos.append(p)
+        seqs.append(ids)
+        for i in ids:
+            next_pos[i] = p + 1
+    for a, b in _chunks(len(pos), 2048):
+        batches.append(_batch(pos[a:b], seqs[a:b], [0] * (b - a), False))
+    for _ in range(2):
+        batches.append(_batch([next_pos[i] for i in range(n_seq)], [(i,) for i in range(n_seq)], [1] * n_seq, True))
+        next_pos = [p + 1 for p in next_pos]
+    return Workload("many_sequences", n_layer, 16, 8, 128, kv_size=kv_size, n_stream=1, n_seq_max=n_seq,
+                    seed=seed, batches=batches, n_batch=2048, n_ubatch=512,
+                    note=f"{n_seq} sequences in groups of {group} sharing {prefix} cells, {private[0]}..{private[1]} "
+                         f"private each, {n_shared} slots of {shared_size} random sequences, two decode steps")
+
+
 def random_mix(seed, n_batches=6):
     """A randomized small workload for differential tests: random head shape
     (head_dim 64 or 128, group 1, 2 or 4, 2 to 8 KV heads), one to four

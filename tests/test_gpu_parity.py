@@ -674,3 +674,55 @@ def test_sliding_window_parity(name, w):
     _, got = gpu_run(wl, layers, on_ubatch=check)
     for key in ref:
         assert_parity(got[key], ref[key], tag=f"window {w} {name} {key}")
+
+
+@pytest.mark.parametrize("n_shared", [0, 1200])
+def test_many_sequences(n_shared):
+    """256 live sequences, the widest sequence set: two decode ubatches of 256
+    queries over group prefixes (cells holding 8 ids), private prompts and,
+    with n_shared, 1200 cells holding 8 random ids each, so one ubatch sees
+    288 or ~1500 distinct sets, read by ~40 queries each in the second case.
+    Past 1024 classes the tail of the class list is merged
+    into one class of the union set, walked with the per-cell membership
+    test; when the queries then still need more split-K partial rows than
+    the workspace holds (each query gets one per class it reads), the
+    planner halves the class cap until they fit.  Cells and dense masks bit
+    for bit, the class lists too while nothing is merged, every output
+    within tolerance."""
+    wl = W.many_sequences(n_shared=n_shared)
+    print(f"[gpu] many_sequences: {wl.note}", flush=True)
+    eng, ref, masks, meta = oracle_run(wl, [0], keep_masks=True)
+    ub_index = {b: 0 for b in range(len(wl.batches))}
+    plan_classes = []
+
+    def check(ctx, b, ub):
+        u = ub_index[b]
+        assert ub.cells.tolist() == meta[(b, u)].cells
+        if wl.batches[b].measured:
+            m = ctx.mask(ub).cpu().numpy().view(np.uint16)
+            assert np.array_equal(m, masks[(b, u)].view(np.uint16)), f"mask differs (batch {b}, ubatch {u})"
+            st = ctx.plan_stats()
+            plan_classes.append((st["n_classes"], st["n_partial_rows"]))
+        ub_index[b] += 1
+
+    ctx, got = gpu_run(wl, [0], on_ubatch=check)
+    last = max(meta)
+    exp = expected_classes(eng, meta[last])
+    n_classes = ctx.plan_stats()["n_classes"]
+    if len(exp) <= 1024:
+        got_cls = ctx.classes()
+        assert n_classes == len(exp) == len(got_cls)
+        assert [(s, m) for s, m, _ in got_cls] == [(s, m) for s, m, _ in exp]
+        for (_, _, cg), (_, _, ce) in zip(got_cls, exp):
+            assert np.array_equal(cg, ce)
+    else:
+        # 1023 sets of ~8 queries each would need ~8000 partial rows: the cap shrinks
+        assert max(c for c, _ in plan_classes) < 1024, plan_classes
+    worst = 0.0
+    for key in ref:
+        ma, _ = assert_parity(got[key], ref[key], tag=f"many_sequences n_shared={n_shared} batch {key[0]}")
+        worst = max(worst, ma)
+    print(f"[gpu] many_sequences n_shared={n_shared}: {len(exp)} sets, (classes, partial rows) per decode ubatch "
+          f"{plan_classes}, max abs error {worst:.3e}", flush=True)
+    assert worst < MFMA_BOUND, worst
+    ctx.close()

@@ -180,8 +180,10 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
   const Geometry& g = c->core.geo();
   UbatchRec& u = c->core.ubatches()[k];
   std::string e0, e1;
-  int rc0 = c->core.build_plan(k, false, c->plan[0], e0);
-  int rc1 = rc0 ? rc0 : c->core.build_plan(k, true, c->plan[1], e1);
+  // both variants share one class table: the output-only plan takes the
+  // class cap the full plan settled on
+  int rc0 = c->core.build_plan(k, false, kMaxClasses, true, c->plan[0], e0);
+  int rc1 = rc0 ? rc0 : c->core.build_plan(k, true, c->plan[0].class_cap, false, c->plan[1], e1);
   c->plan_ok = rc0 == KVATTN_OK && rc1 == KVATTN_OK;
   if (!c->plan_ok) {
     c->plan[0] = Plan();

@@ -516,7 +516,8 @@ void HostCore::get_cells(int32_t s, int32_t* pos, uint64_t* mask) const {
 
 // ---- work plan -------------------------------------------------------------
 
-int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) const {
+int HostCore::build_plan(int k, bool only_outputs, int32_t max_classes, bool shrink, Plan& P,
+                         std::string& err) const {
   const UbatchRec& u = ubs_[k];
   P = Plan();
   P.n_kv = n_kv();
@@ -550,42 +551,6 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
   }
   int32_t n_streams_rel = 0;
   for (int s = 0; s < S; ++s) n_streams_rel += rel[s].empty() ? 0 : 1;
-  // past kMaxClasses, the tail of each stream's list is merged into one class
-  int32_t budget = n_rel <= static_cast<size_t>(kMaxClasses) ? kMaxClasses : kMaxClasses - n_streams_rel;
-  P.lookup_off.assign(S + 1, 0);
-  for (int s = 0; s < S; ++s) {
-    P.lookup_off[s] = static_cast<int32_t>(P.lookup.size());
-    int32_t merged = -1;
-    for (const auto& kv : rel[s]) {
-      int32_t c;
-      if (budget > 0) {
-        c = static_cast<int32_t>(P.classes.size());
-        P.classes.push_back(ClassInfo{kv.first, s, kv.second, 0, 0, 0, 1, 0, 0});
-        --budget;
-      } else {
-        if (merged < 0) {
-          merged = static_cast<int32_t>(P.classes.size());
-          P.classes.push_back(ClassInfo{SeqSet::none(), s, 0, 0, 0, 0, 0, 0, 0});
-        }
-        c = merged;
-        P.classes[c].mask |= kv.first;
-        P.classes[c].n_cells += kv.second;
-      }
-      P.lookup.push_back(LookupEntry{kv.first, c, {0, 0, 0}});
-    }
-  }
-  P.lookup_off[S] = static_cast<int32_t>(P.lookup.size());
-  int32_t off = 0, tiles = 0;
-  for (auto& c : P.classes) {
-    c.cell_off = off;
-    c.tile_base = tiles;
-    off += c.n_cells;
-    tiles += ceil_div(c.n_cells, kTileCells);
-    P.max_class_tiles = std::max(P.max_class_tiles, ceil_div(c.n_cells, kTileCells));
-  }
-  P.total_cells = off;
-  P.total_tiles = tiles;
-
   // queries of each class, grouped by sequence then position
   std::vector<int32_t> qorder(NQ);
   std::iota(qorder.begin(), qorder.end(), 0);
@@ -595,131 +560,193 @@ int HostCore::build_plan(int k, bool only_outputs, Plan& P, std::string& err) co
     if (x.pos != y.pos) return x.pos < y.pos;
     return a < b;
   });
-  for (auto& c : P.classes) {
-    c.q_off = static_cast<int32_t>(P.qlist.size());
-    for (int32_t q : qorder)
-      if (P.slots[q].stream == c.stream && c.mask.test(P.slots[q].seq0)) P.qlist.push_back(q);
-    c.n_q = static_cast<int32_t>(P.qlist.size()) - c.q_off;
-  }
-
-  // work items
-  const int D = g_.head_dim, G = g_.G();
-  const int32_t E = g_.E();
-  const bool valu_ok = (E == 512 || E == 1024 || E == 2048 || E == 4096) && (D == 64 || D == 128) &&
-                       (G == 1 || G == 2 || G == 4);
-  const int32_t QT = kMfmaRowsPerItem / G;   // query rows of one matrix-core workgroup
-  // Item sizing.  One attend call launches (items x layers per call)
-  // workgroups.  Each bandwidth-bound class is cut into chunks of at most
-  // `ch` cells; ch is the largest power of two (256 .. 8192 cells) for which
-  // the launch still reaches its workgroup target, so a long context is
-  // split only when there are too few queries to fill the GPU.
-  const int64_t L = std::max(1, g_.attend_layers);
-  std::vector<std::pair<int32_t, int32_t>> valu_lists, low_lists, high_lists;   // (cells, copies)
-  for (const auto& c : P.classes) {
-    if (c.n_q == 0 || c.n_cells == 0) continue;
-    if (valu_ok && c.n_q <= kValuMaxQueries) valu_lists.push_back({c.n_cells, c.n_q});
-    else if (c.n_q * G <= 64) low_lists.push_back({c.n_cells, ceil_div(c.n_q, QT) * g_.n_head_kv});
-    else high_lists.push_back({c.n_cells, ceil_div(c.n_q, QT) * g_.n_head_kv});
-  }
-  auto pick_chunk = [&](const std::vector<std::pair<int32_t, int32_t>>& lists, int64_t target, int32_t lo,
-                        int32_t hi) {
-    int32_t ch = hi;
-    while (ch > lo) {
-      int64_t wg = 0;
-      for (const auto& x : lists) wg += static_cast<int64_t>(ceil_div(x.first, ch)) * x.second;
-      if (wg * L >= target) break;
-      ch /= 2;
-    }
-    return ch;
-  };
-  int32_t chv = pick_chunk(valu_lists, kValuTargetWorkgroups, kValuMinChunk, 8192);
-  // matrix-core items with few query rows are bandwidth-bound too: their
-  // cells (multiples of the 64-cell tile) are cut the same way
-  int32_t chm_lowreuse = pick_chunk(low_lists, kMfmaTargetWorkgroups, 256, 4096);
-  // prompt-sized classes are cut only when the launch would not fill the
-  // GPU otherwise (one layer per call): every cut costs a partial row per
-  // query and merge work, so a layer range keeps whole cell lists
-  int32_t chm_high = pick_chunk(high_lists, kMfmaHighTargetWorkgroups, 256, 1 << 30);
-
-  for (int attempt = 0; attempt < 16; ++attempt) {
+  // Past the class cap, the tail of each stream's list is merged into one
+  // class (its set: the union; its cells walked with the per-cell membership
+  // test).  The cap starts at max_classes.  A query gets one partial row per
+  // class it reads, so when even whole classes need more split-K partial
+  // rows than the workspace holds (queries that each see many sets), the
+  // cap is halved and the plan built again, when the caller allows it.
+  auto plan_with_cap = [&](int32_t cap) -> int {
+    P.classes.clear();
+    P.lookup.clear();
+    P.qlist.clear();
     P.items_valu.clear();
     P.items_mfma.clear();
-    std::vector<int32_t> coverage(NQ, 0);
-    // VALU items: (query, chunk)
-    struct Pending { WorkItem it; bool valu; };
-    std::vector<Pending> pend;
-    for (int32_t ci = 0; ci < static_cast<int32_t>(P.classes.size()); ++ci) {
-      const ClassInfo& c = P.classes[ci];
+    P.red_slot.clear();
+    P.red_off.clear();
+    P.red_rows.clear();
+    P.max_class_tiles = 0;
+    P.n_partial_rows = 0;
+    int32_t budget = n_rel <= static_cast<size_t>(cap) ? cap : std::max(0, cap - n_streams_rel);
+    P.lookup_off.assign(S + 1, 0);
+    for (int s = 0; s < S; ++s) {
+      P.lookup_off[s] = static_cast<int32_t>(P.lookup.size());
+      int32_t merged = -1;
+      for (const auto& kv : rel[s]) {
+        int32_t c;
+        if (budget > 0) {
+          c = static_cast<int32_t>(P.classes.size());
+          P.classes.push_back(ClassInfo{kv.first, s, kv.second, 0, 0, 0, 1, 0, 0});
+          --budget;
+        } else {
+          if (merged < 0) {
+            merged = static_cast<int32_t>(P.classes.size());
+            P.classes.push_back(ClassInfo{SeqSet::none(), s, 0, 0, 0, 0, 0, 0, 0});
+          }
+          c = merged;
+          P.classes[c].mask |= kv.first;
+          P.classes[c].n_cells += kv.second;
+        }
+        P.lookup.push_back(LookupEntry{kv.first, c, {0, 0, 0}});
+      }
+    }
+    P.lookup_off[S] = static_cast<int32_t>(P.lookup.size());
+    int32_t off = 0, tiles = 0;
+    for (auto& c : P.classes) {
+      c.cell_off = off;
+      c.tile_base = tiles;
+      off += c.n_cells;
+      tiles += ceil_div(c.n_cells, kTileCells);
+      P.max_class_tiles = std::max(P.max_class_tiles, ceil_div(c.n_cells, kTileCells));
+    }
+    P.total_cells = off;
+    P.total_tiles = tiles;
+
+    for (auto& c : P.classes) {
+      c.q_off = static_cast<int32_t>(P.qlist.size());
+      for (int32_t q : qorder)
+        if (P.slots[q].stream == c.stream && c.mask.test(P.slots[q].seq0)) P.qlist.push_back(q);
+      c.n_q = static_cast<int32_t>(P.qlist.size()) - c.q_off;
+    }
+
+    // work items
+    const int D = g_.head_dim, G = g_.G();
+    const int32_t E = g_.E();
+    const bool valu_ok = (E == 512 || E == 1024 || E == 2048 || E == 4096) && (D == 64 || D == 128) &&
+                         (G == 1 || G == 2 || G == 4);
+    const int32_t QT = kMfmaRowsPerItem / G;   // query rows of one matrix-core workgroup
+    // Item sizing.  One attend call launches (items x layers per call)
+    // workgroups.  Each bandwidth-bound class is cut into chunks of at most
+    // `ch` cells; ch is the largest power of two (256 .. 8192 cells) for which
+    // the launch still reaches its workgroup target, so a long context is
+    // split only when there are too few queries to fill the GPU.
+    const int64_t L = std::max(1, g_.attend_layers);
+    std::vector<std::pair<int32_t, int32_t>> valu_lists, low_lists, high_lists;   // (cells, copies)
+    for (const auto& c : P.classes) {
       if (c.n_q == 0 || c.n_cells == 0) continue;
-      const bool valu = valu_ok && c.n_q <= kValuMaxQueries;
-      if (valu) {
-        const int32_t parts = ceil_div(c.n_cells, chv);
-        const int32_t len = ceil_div(c.n_cells, parts);
-        for (int32_t t = 0; t < c.n_q; ++t) {
-          const int32_t q = P.qlist[c.q_off + t];
-          for (int32_t a = 0; a < c.n_cells; a += len) {
-            WorkItem it{ci, c.q_off + t, 1, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + len), -1,
-                        P.slots[q].pos, P.slots[q].pos, c.tile_base + a / kTileCells, c.stream, c.pure, 0};
-            pend.push_back({it, true});
-            ++coverage[q];
+      if (valu_ok && c.n_q <= kValuMaxQueries) valu_lists.push_back({c.n_cells, c.n_q});
+      else if (c.n_q * G <= 64) low_lists.push_back({c.n_cells, ceil_div(c.n_q, QT) * g_.n_head_kv});
+      else high_lists.push_back({c.n_cells, ceil_div(c.n_q, QT) * g_.n_head_kv});
+    }
+    auto pick_chunk = [&](const std::vector<std::pair<int32_t, int32_t>>& lists, int64_t target, int32_t lo,
+                          int32_t hi) {
+      int32_t ch = hi;
+      while (ch > lo) {
+        int64_t wg = 0;
+        for (const auto& x : lists) wg += static_cast<int64_t>(ceil_div(x.first, ch)) * x.second;
+        if (wg * L >= target) break;
+        ch /= 2;
+      }
+      return ch;
+    };
+    int32_t chv = pick_chunk(valu_lists, kValuTargetWorkgroups, kValuMinChunk, 8192);
+    // matrix-core items with few query rows are bandwidth-bound too: their
+    // cells (multiples of the 64-cell tile) are cut the same way
+    int32_t chm_lowreuse = pick_chunk(low_lists, kMfmaTargetWorkgroups, 256, 4096);
+    // prompt-sized classes are cut only when the launch would not fill the
+    // GPU otherwise (one layer per call): every cut costs a partial row per
+    // query and merge work, so a layer range keeps whole cell lists
+    int32_t chm_high = pick_chunk(high_lists, kMfmaHighTargetWorkgroups, 256, 1 << 30);
+
+    for (int attempt = 0; attempt < 16; ++attempt) {
+      P.items_valu.clear();
+      P.items_mfma.clear();
+      std::vector<int32_t> coverage(NQ, 0);
+      // VALU items: (query, chunk)
+      struct Pending { WorkItem it; bool valu; };
+      std::vector<Pending> pend;
+      for (int32_t ci = 0; ci < static_cast<int32_t>(P.classes.size()); ++ci) {
+        const ClassInfo& c = P.classes[ci];
+        if (c.n_q == 0 || c.n_cells == 0) continue;
+        const bool valu = valu_ok && c.n_q <= kValuMaxQueries;
+        if (valu) {
+          const int32_t parts = ceil_div(c.n_cells, chv);
+          const int32_t len = ceil_div(c.n_cells, parts);
+          for (int32_t t = 0; t < c.n_q; ++t) {
+            const int32_t q = P.qlist[c.q_off + t];
+            for (int32_t a = 0; a < c.n_cells; a += len) {
+              WorkItem it{ci, c.q_off + t, 1, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + len), -1,
+                          P.slots[q].pos, P.slots[q].pos, c.tile_base + a / kTileCells, c.stream, c.pure, 0};
+              pend.push_back({it, true});
+              ++coverage[q];
+            }
           }
-        }
-      } else {
-        // few query rows per KV head -> bandwidth-bound -> split the cells
-        const int32_t ch = (c.n_q * G <= 64) ? chm_lowreuse : chm_high;
-        for (int32_t t0 = 0; t0 < c.n_q; t0 += QT) {
-          const int32_t nq = std::min(QT, c.n_q - t0);
-          int32_t pmin = INT32_MAX, pmax = INT32_MIN;
-          for (int32_t t = 0; t < nq; ++t) {
-            const int32_t p = P.slots[P.qlist[c.q_off + t0 + t]].pos;
-            pmin = std::min(pmin, p);
-            pmax = std::max(pmax, p);
-          }
-          for (int32_t a = 0; a < c.n_cells; a += ch) {
-            WorkItem it{ci, c.q_off + t0, nq, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + ch), -1,
-                        pmin, pmax, c.tile_base + a / kTileCells, c.stream, c.pure, 0};
-            pend.push_back({it, false});
-            for (int32_t t = 0; t < nq; ++t) ++coverage[P.qlist[c.q_off + t0 + t]];
+        } else {
+          // few query rows per KV head -> bandwidth-bound -> split the cells
+          const int32_t ch = (c.n_q * G <= 64) ? chm_lowreuse : chm_high;
+          for (int32_t t0 = 0; t0 < c.n_q; t0 += QT) {
+            const int32_t nq = std::min(QT, c.n_q - t0);
+            int32_t pmin = INT32_MAX, pmax = INT32_MIN;
+            for (int32_t t = 0; t < nq; ++t) {
+              const int32_t p = P.slots[P.qlist[c.q_off + t0 + t]].pos;
+              pmin = std::min(pmin, p);
+              pmax = std::max(pmax, p);
+            }
+            for (int32_t a = 0; a < c.n_cells; a += ch) {
+              WorkItem it{ci, c.q_off + t0, nq, c.cell_off + a, c.cell_off + std::min(c.n_cells, a + ch), -1,
+                          pmin, pmax, c.tile_base + a / kTileCells, c.stream, c.pure, 0};
+              pend.push_back({it, false});
+              for (int32_t t = 0; t < nq; ++t) ++coverage[P.qlist[c.q_off + t0 + t]];
+            }
           }
         }
       }
-    }
-    // direct output when every query of the item is covered once
-    int32_t rows = 0;
-    std::vector<std::vector<int32_t>> qrows(NQ);
-    for (auto& pd : pend) {
-      bool direct = true;
-      for (int32_t t = 0; t < pd.it.n_q; ++t) direct &= coverage[P.qlist[pd.it.q_off + t]] == 1;
-      if (!direct) {
-        pd.it.prow = rows;
-        for (int32_t t = 0; t < pd.it.n_q; ++t) qrows[P.qlist[pd.it.q_off + t]].push_back(rows + t);
-        rows += pd.it.n_q;
+      // direct output when every query of the item is covered once
+      int32_t rows = 0;
+      std::vector<std::vector<int32_t>> qrows(NQ);
+      for (auto& pd : pend) {
+        bool direct = true;
+        for (int32_t t = 0; t < pd.it.n_q; ++t) direct &= coverage[P.qlist[pd.it.q_off + t]] == 1;
+        if (!direct) {
+          pd.it.prow = rows;
+          for (int32_t t = 0; t < pd.it.n_q; ++t) qrows[P.qlist[pd.it.q_off + t]].push_back(rows + t);
+          rows += pd.it.n_q;
+        }
+        (pd.valu ? P.items_valu : P.items_mfma).push_back(pd.it);
       }
-      (pd.valu ? P.items_valu : P.items_mfma).push_back(pd.it);
+      if (rows > prow_max) {
+        chv *= 2;
+        chm_lowreuse *= 2;
+        chm_high = std::min(chm_high, 1 << 29) * 2;
+        continue;
+      }
+      P.n_partial_rows = rows;
+      P.red_off.push_back(0);
+      for (int32_t q = 0; q < NQ; ++q) {
+        if (qrows[q].empty()) continue;
+        P.red_slot.push_back(q);
+        P.red_rows.insert(P.red_rows.end(), qrows[q].begin(), qrows[q].end());
+        P.red_off.push_back(static_cast<int32_t>(P.red_rows.size()));
+      }
+      // longest first in both sets (the kernels dispatch items in this order):
+      // the last workgroups of a launch are then the shortest ones
+      std::stable_sort(P.items_valu.begin(), P.items_valu.end(),
+                       [](const WorkItem& a, const WorkItem& b) { return a.c1 - a.c0 > b.c1 - b.c0; });
+      // MFMA items: causal tiles late in a prompt see the most cells
+      std::stable_sort(P.items_mfma.begin(), P.items_mfma.end(), [](const WorkItem& a, const WorkItem& b) {
+        return std::min(a.c1 - a.c0, a.qpos_max) > std::min(b.c1 - b.c0, b.qpos_max);
+      });
+      return KVATTN_OK;
     }
-    if (rows > prow_max) {
-      chv *= 2;
-      chm_lowreuse *= 2;
-      chm_high = std::min(chm_high, 1 << 29) * 2;
-      continue;
+
+    return KVATTN_ENOMEM;
+  };
+  for (int32_t cap = max_classes;; cap /= 2) {
+    if (plan_with_cap(cap) == KVATTN_OK) {
+      P.class_cap = cap;
+      return KVATTN_OK;
     }
-    P.n_partial_rows = rows;
-    P.red_off.push_back(0);
-    for (int32_t q = 0; q < NQ; ++q) {
-      if (qrows[q].empty()) continue;
-      P.red_slot.push_back(q);
-      P.red_rows.insert(P.red_rows.end(), qrows[q].begin(), qrows[q].end());
-      P.red_off.push_back(static_cast<int32_t>(P.red_rows.size()));
-    }
-    // longest first in both sets (the kernels dispatch items in this order):
-    // the last workgroups of a launch are then the shortest ones
-    std::stable_sort(P.items_valu.begin(), P.items_valu.end(),
-                     [](const WorkItem& a, const WorkItem& b) { return a.c1 - a.c0 > b.c1 - b.c0; });
-    // MFMA items: causal tiles late in a prompt see the most cells
-    std::stable_sort(P.items_mfma.begin(), P.items_mfma.end(), [](const WorkItem& a, const WorkItem& b) {
-      return std::min(a.c1 - a.c0, a.qpos_max) > std::min(b.c1 - b.c0, b.qpos_max);
-    });
-    return KVATTN_OK;
+    if (!shrink || cap <= n_streams_rel) break;   // one class per stream already
   }
   err = "split-K partial rows exceed the workspace";
   return KVATTN_ENOMEM;

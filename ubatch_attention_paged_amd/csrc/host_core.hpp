@@ -52,6 +52,7 @@ struct Plan {
   int32_t total_tiles = 0;            // 64-cell tiles over all classes
   int32_t max_class_tiles = 0;
   int32_t n_partial_rows = 0;
+  int32_t class_cap = 0;              // the class cap the plan was built with
   std::vector<SlotInfo> slots;
   std::vector<ClassInfo> classes;
   std::vector<LookupEntry> lookup;
@@ -79,8 +80,10 @@ class HostCore {
   int commit(int k, std::vector<CellUpdate>* upd, std::string& err);
   int latest_committed() const { return latest_; }
 
-  // Work plan of ubatch k over the current table.
-  int build_plan(int k, bool only_outputs, Plan& plan, std::string& err) const;
+  // Work plan of ubatch k over the current table, with at most max_classes
+  // classes; with shrink, fewer when the split-K partial rows would not fit
+  // otherwise (plan.class_cap records the cap used).
+  int build_plan(int k, bool only_outputs, int32_t max_classes, bool shrink, Plan& plan, std::string& err) const;
 
   int seq_rm(int32_t seq, int32_t p0, int32_t p1);
   // Committed cells holding seq (all in stream seq % n_stream), ordered by
