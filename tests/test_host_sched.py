@@ -78,7 +78,7 @@ def compare_tables(ctx, eng, n_stream):
         assert not member[:, nq:].any()
 
 
-def drive_both(stream, max_iters=5000):
+def drive_both(stream, max_iters=5000, stats=None):
     n_batch = stream.token_budget
     ctx = host_ctx(stream.kv_size, stream.n_stream, stream.n_seq_max, n_batch, stream.n_ubatch, stream.split_mode)
     eng = OracleEngine(1, 2, 1, 16, stream.kv_size, stream.n_stream, stream.n_seq_max, n_batch, stream.n_ubatch,
@@ -105,6 +105,8 @@ def drive_both(stream, max_iters=5000):
         for key in KEYS:
             assert got[key] == exp[key], (it, key, got[key], exp[key])
         n_pre += len(exp["preempted"])
+        if stats is not None:
+            stats["max_running"] = max(stats.get("max_running", 0), exp["n_running"])
         ubs = run_batch(ctx, sch)
         if exp["pos"]:
             st, rubs, _ = eng.split(len(exp["pos"]), exp["pos"], [(q,) for q in exp["seq"]], exp["output"])
@@ -143,6 +145,17 @@ def test_native_loop_matches_oracle(name):
     assert iters > 10
     if name.startswith("paged_tight"):
         assert n_pre > 0
+
+
+def test_native_loop_many_running():
+    """More than 64 sequences running at once (sequence ids up to 255): the
+    native loop against the oracle loop, every iteration's records, every
+    ubatch's cells and the whole cell table bit for bit."""
+    st = request_stream(n_req=300, rate=8.0, burst=200, prompt_range=(1, 16), gen_range=(1, 40), kv_size=4096,
+                        n_seq_max=256, token_budget=512, n_ubatch=128, seed=2400)
+    stats = {}
+    iters, _ = drive_both(st, stats=stats)
+    assert iters > 10 and stats["max_running"] > 200, stats
 
 
 def test_native_errors():
