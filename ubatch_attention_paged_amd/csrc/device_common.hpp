@@ -5,6 +5,8 @@
 
 #include <cstdint>
 
+#include "seqset.hpp"
+
 namespace kvattn {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -79,6 +81,37 @@ KVATTN_DEV void buffer_load16_lds(u32x4 rsrc, uint32_t lds, uint32_t off) {
       : "=&s"(saved)
       : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(rsrc)
       : "memory");
+}
+
+// 32-byte sequence sets moved as two 16-byte vector accesses.  Copying the
+// struct as a whole makes the compiler stage it through a private slot,
+// which it then promotes to LDS (32 B per thread of every workgroup).
+KVATTN_DEV SeqSet load_set(const SeqSet* p) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(p);
+  const u32x4 lo = s[0], hi = s[1];
+  SeqSet r;
+  r.w[0] = lo[0] | (static_cast<uint64_t>(lo[1]) << 32);
+  r.w[1] = lo[2] | (static_cast<uint64_t>(lo[3]) << 32);
+  r.w[2] = hi[0] | (static_cast<uint64_t>(hi[1]) << 32);
+  r.w[3] = hi[2] | (static_cast<uint64_t>(hi[3]) << 32);
+  return r;
+}
+KVATTN_DEV void store_set(SeqSet* p, const SeqSet& v) {
+  u32x4* d = reinterpret_cast<u32x4*>(p);
+  u32x4 lo, hi;
+  lo[0] = static_cast<uint32_t>(v.w[0]); lo[1] = static_cast<uint32_t>(v.w[0] >> 32);
+  lo[2] = static_cast<uint32_t>(v.w[1]); lo[3] = static_cast<uint32_t>(v.w[1] >> 32);
+  hi[0] = static_cast<uint32_t>(v.w[2]); hi[1] = static_cast<uint32_t>(v.w[2] >> 32);
+  hi[2] = static_cast<uint32_t>(v.w[3]); hi[3] = static_cast<uint32_t>(v.w[3] >> 32);
+  d[0] = lo;
+  d[1] = hi;
+}
+KVATTN_DEV void copy_set(SeqSet* dst, const SeqSet* src) {
+  const u32x4* s = reinterpret_cast<const u32x4*>(src);
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+  const u32x4 lo = s[0], hi = s[1];
+  d[0] = lo;
+  d[1] = hi;
 }
 
 // Accumulator register r of lane l in a 32x32 MFMA block holds row

@@ -57,9 +57,9 @@ hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s) {
 __global__ __launch_bounds__(256) void k_apply_updates(CsrArgs a, int64_t n_counts) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < a.n_updates) {
-    const CellUpdate u = a.updates[i];
-    a.cpos[u.idx] = u.pos;
-    a.cmask[u.idx] = u.mask;
+    const int32_t idx = a.updates[i].idx;
+    a.cpos[idx] = a.updates[i].pos;
+    copy_set(&a.cmask[idx], &a.updates[i].mask);
   }
   if (i < n_counts) a.counts[i] = 0;
 }
@@ -174,19 +174,23 @@ __global__ __launch_bounds__(256) void k_tile_minmax(CsrArgs a) {
   }
 }
 
-// The whole commit in one 256-thread workgroup, for caches of at most
-// kSmallCommitCells (stream, cell) pairs below n_kv, kSmallCommitClasses
-// classes and lookup entries and kSmallCommitStreams streams: mirror
-// updates, classification (kept in LDS), the ordered per-class lists (256
-// cells at a time in (stream, cell) order: a cell's slot is its class's
-// running offset + the same-class cells of earlier wavefronts of the chunk +
-// its rank in its wavefront), then the per-tile position ranges.  Produces
-// exactly what the multi-kernel path produces.  The class and lookup tables
-// are read once into LDS (they may sit in host memory); each thread reads
-// its cells' mirror entries once, up front, and keeps them in registers.
+// The whole commit in one workgroup of kCommitThreads threads, for caches of
+// at most kSmallCommitCells (stream, cell) pairs below n_kv,
+// kSmallCommitClasses classes and lookup entries and kSmallCommitStreams
+// streams: mirror updates, classification (kept in LDS), the ordered
+// per-class lists (kCommitThreads cells at a time in (stream, cell) order: a
+// cell's slot is its class's running offset + the same-class cells of
+// earlier wavefronts of the chunk + its rank in its wavefront), then the
+// per-tile position ranges.  Produces exactly what the multi-kernel path
+// produces.  The class and lookup tables are read once into LDS (they may
+// sit in host memory); each thread reads its (at most four) cells' mirror
+// entries -- position and 32-byte sequence set -- once, up front, and keeps
+// them in registers, so the whole commit waits on global memory about once.
+constexpr int kCommitThreads = 1024;
 KVATTN_DEV void commit_small(const CsrArgs& a) {
-  constexpr int KMAX = kSmallCommitCells / 256;     // cells per thread at most
-  __shared__ int32_t wc[4][kSmallCommitClasses];
+  constexpr int NT = kCommitThreads, NWV = NT / 64;
+  constexpr int KMAX = kSmallCommitCells / NT;      // cells per thread at most
+  __shared__ int32_t wc[NWV][kSmallCommitClasses];
   __shared__ int32_t base[kSmallCommitClasses];
   __shared__ LookupEntry lk[kSmallCommitClasses];
   __shared__ ClassInfo cl[kSmallCommitClasses];
@@ -196,50 +200,51 @@ KVATTN_DEV void commit_small(const CsrArgs& a) {
   if (tid < a.n_lookup) lk[tid] = a.lookup[tid];
   if (tid < nc) cl[tid] = a.classes[tid];
   if (tid <= a.n_stream && nc > 0) lko[tid] = a.lookup_off[tid];
-  for (int i = tid; i < a.n_updates; i += 256) {
-    const CellUpdate u = a.updates[i];
-    a.cpos[u.idx] = u.pos;
-    a.cmask[u.idx] = u.mask;
+  for (int i = tid; i < a.n_updates; i += NT) {
+    const int32_t idx = a.updates[i].idx;
+    a.cpos[idx] = a.updates[i].pos;
+    copy_set(&a.cmask[idx], &a.updates[i].mask);
   }
   __syncthreads();
   if (nc == 0) return;
   const int total = a.n_stream * a.n_kv;
-  // every cell this thread will place (cell tid + 256 k): its position and
-  // class stay in registers; its sequence set is read for the class lookup
-  // and again when the cell is written to its list
+  // every cell this thread will place (cell tid + NT k), read once: its
+  // position, sequence set and class stay in registers
   int pos_r[KMAX], cls_r[KMAX];
+  SeqSet msk_r[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
-    const int i = tid + 256 * k;
+    const int i = tid + NT * k;
     pos_r[k] = -1;
+    msk_r[k] = SeqSet::none();
     if (i < total) {
       const int64_t idx = static_cast<int64_t>(i / a.n_kv) * a.kv_size + i % a.n_kv;
       pos_r[k] = a.cpos[idx];
+      msk_r[k] = load_set(&a.cmask[idx]);
     }
   }
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     int cls = -1;
-    const int i = tid + 256 * k;
+    const int i = tid + NT * k;
     if (i < total && pos_r[k] >= 0) {
       const int s = i / a.n_kv;
-      const SeqSet m = a.cmask[static_cast<int64_t>(s) * a.kv_size + i % a.n_kv];
       int lo = lko[s], hi = lko[s + 1] - 1;
       while (lo <= hi) {
         const int mid = (lo + hi) >> 1;
         const SeqSet mm = lk[mid].mask;
-        if (mm == m) { cls = lk[mid].cls; break; }
-        if (mm < m) lo = mid + 1; else hi = mid - 1;
+        if (mm == msk_r[k]) { cls = lk[mid].cls; break; }
+        if (mm < msk_r[k]) lo = mid + 1; else hi = mid - 1;
       }
     }
     cls_r[k] = cls;
   }
   if (tid < nc) base[tid] = cl[tid].cell_off;
-  for (int z = tid; z < 4 * kSmallCommitClasses; z += 256) wc[z / kSmallCommitClasses][z % kSmallCommitClasses] = 0;
+  for (int z = tid; z < NWV * kSmallCommitClasses; z += NT) wc[z / kSmallCommitClasses][z % kSmallCommitClasses] = 0;
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
-    if (256 * k >= total) break;
+    if (NT * k >= total) break;
     const int cls = cls_r[k];
     int rank = 0;
     uint64_t active = ballot(cls >= 0);
@@ -256,25 +261,29 @@ KVATTN_DEV void commit_small(const CsrArgs& a) {
       int dst = base[cls] + rank;
       for (int w2 = 0; w2 < w; ++w2) dst += wc[w2][cls];
       if (dst < a.csr_cap) {
-        const int i = tid + 256 * k;
-        a.csr_cell[dst] = i % a.n_kv;
+        a.csr_cell[dst] = (tid + NT * k) % a.n_kv;
         a.csr_pos[dst] = pos_r[k];
-        a.csr_mask[dst] = a.cmask[static_cast<int64_t>(i / a.n_kv) * a.kv_size + i % a.n_kv];
+        store_set(&a.csr_mask[dst], msk_r[k]);
       }
     }
     __syncthreads();
     // the thread that folds class tid's counts into its offset also clears
     // them (only classes < nc are ever counted)
     if (tid < nc) {
-      base[tid] += wc[0][tid] + wc[1][tid] + wc[2][tid] + wc[3][tid];
-      wc[0][tid] = wc[1][tid] = wc[2][tid] = wc[3][tid] = 0;
+      int add = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < NWV; ++w2) {
+        add += wc[w2][tid];
+        wc[w2][tid] = 0;
+      }
+      base[tid] += add;
     }
     __syncthreads();
   }
   for (int c = 0; c < nc; ++c) {
     const ClassInfo ci = cl[c];
     const int nt = (ci.n_cells + kTileCells - 1) / kTileCells;
-    for (int k = w; k < nt; k += 4) {
+    for (int k = w; k < nt; k += NWV) {
       const int j = k * kTileCells + lane;
       const bool in = j < ci.n_cells;
       const int p = in ? a.csr_pos[ci.cell_off + j] : INT32_MAX;
@@ -297,7 +306,7 @@ bool commit_is_small(const CsrArgs& a) {
 // instance runs the small commit.  The other (y, z) = (0, 0) blocks also copy
 // the plan from pinned host memory into the device plan arena, which the
 // attention launches read after this kernel.
-__global__ __launch_bounds__(256) void k_store_commit(StoreArgs a, CsrArgs c) {
+__global__ __launch_bounds__(kCommitThreads) void k_store_commit(StoreArgs a, CsrArgs c) {
   if (blockIdx.x == gridDim.x - 1) {
     if (blockIdx.y == 0 && blockIdx.z == 0) commit_small(c);
     return;
@@ -313,8 +322,8 @@ __global__ __launch_bounds__(256) void k_store_commit(StoreArgs a, CsrArgs c) {
 
 hipError_t launch_store_commit(const StoreArgs& a, int n_il, const CsrArgs& c, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(a.n_rows) * (a.E / 8);
-  dim3 grid(static_cast<unsigned>((n + 255) / 256) + 1, n_il, 2);
-  hipLaunchKernelGGL(k_store_commit, grid, dim3(256), 0, s, a, c);
+  dim3 grid(static_cast<unsigned>((n + kCommitThreads - 1) / kCommitThreads) + 1, n_il, 2);
+  hipLaunchKernelGGL(k_store_commit, grid, dim3(kCommitThreads), 0, s, a, c);
   return hipGetLastError();
 }
 
