@@ -17,7 +17,8 @@ using namespace kvattn;
 
 namespace {
 
-constexpr int kStages = 4;                 // pinned staging buffers in flight
+constexpr int kStages = 16;                // pinned staging buffers in flight
+constexpr int kStagesPerEvent = 8;         // uses of the ring covered by one recorded event
 constexpr int64_t kPartialRowsCap = 16384; // split-K partial rows x layers per launch
 constexpr size_t kAlign = 256;
 
@@ -82,6 +83,15 @@ struct kvattn_ctx {
   char* stage_dev[kStages] = {};     // device view of each pinned staging buffer
   hipEvent_t ev[kStages] = {};
   bool ev_used[kStages] = {};
+  // Staging reuse: an event recorded after the GPU work of a use shows that
+  // use done.  Recording one per use put a marker in the stream every
+  // ubatch, and each marker held the next kernel back ~6 us; so one event
+  // covers up to kStagesPerEvent consecutive uses on one stream.
+  int cover[kStages];                // stage whose event covers this stage's last use, -1 = none
+  kvattn_ctx() { std::fill(cover, cover + kStages, -1); }
+  int uncovered[kStagesPerEvent];    // uses since the last recorded event, in order
+  int n_uncovered = 0;
+  hipStream_t uncovered_stream = nullptr;
   int stage_next = 0;
   Plan plan[2];
   ArenaLayout al{};
@@ -149,10 +159,37 @@ int ensure_device(kvattn_ctx* c) {
 // The next pinned staging buffer of the ring, at least `bytes` large, once
 // the GPU work that last read it has finished.  Its event must be recorded
 // after the work that reads it now.
+// Record one event after the uses not yet covered by one (on the stream
+// they ran on); it covers all of them.
+int cover_stages(kvattn_ctx* c) {
+  if (c->n_uncovered == 0) return KVATTN_OK;
+  const int last = c->uncovered[c->n_uncovered - 1];
+  HIP_TRY(c, hipEventRecord(c->ev[last], c->uncovered_stream));
+  c->ev_used[last] = true;
+  for (int i = 0; i < c->n_uncovered; ++i) c->cover[c->uncovered[i]] = last;
+  c->n_uncovered = 0;
+  return KVATTN_OK;
+}
+
+// Stage st is read by GPU work just enqueued on stream s.
+int release_stage(kvattn_ctx* c, int st, hipStream_t s) {
+  if (c->n_uncovered > 0 && s != c->uncovered_stream)
+    if (int rc = cover_stages(c)) return rc;
+  c->cover[st] = -1;
+  c->uncovered[c->n_uncovered++] = st;
+  c->uncovered_stream = s;
+  return c->n_uncovered == kStagesPerEvent ? cover_stages(c) : KVATTN_OK;
+}
+
 int acquire_stage(kvattn_ctx* c, size_t bytes, int* out) {
   const int st = c->stage_next;
   c->stage_next = (st + 1) % kStages;
-  if (c->ev_used[st]) HIP_TRY(c, hipEventSynchronize(c->ev[st]));
+  // (a ring of kStages >= 2 kStagesPerEvent is always covered by now)
+  for (int i = 0; i < c->n_uncovered; ++i)
+    if (c->uncovered[i] == st)
+      if (int rc = cover_stages(c)) return rc;
+  if (c->cover[st] >= 0) HIP_TRY(c, hipEventSynchronize(c->ev[c->cover[st]]));
+  c->cover[st] = -1;
   if (c->stage_cap[st] < bytes) {
     if (c->stage[st]) HIP_TRY(c, hipHostFree(c->stage[st]));
     c->stage[st] = nullptr;
@@ -302,8 +339,7 @@ int upload_commit(kvattn_ctx* c, int k, hipStream_t s, bool may_fuse) {
     c->fused_dst_rows = reinterpret_cast<const int32_t*>(c->stage_dev[st] + A.dst_rows);
   } else {
     if (A.total) HIP_TRY(c, hipMemcpyAsync(arena, b, A.total, hipMemcpyHostToDevice, s));
-    HIP_TRY(c, hipEventRecord(c->ev[st], s));
-    c->ev_used[st] = true;
+    if (int rc = release_stage(c, st, s)) return rc;
   }
   // launched by the caller: alone, or inside the first store launch
   c->pending_fused = fused;
@@ -388,6 +424,7 @@ void kvattn_destroy(kvattn_ctx* c) {
   if (!c) return;
   if (c->dev_ready) {
     (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();      // covers the staging uses no event covers yet
     for (int i = 0; i < kStages; ++i) {
       if (c->ev_used[i]) (void)hipEventSynchronize(c->ev[i]);
       if (c->ev[i]) (void)hipEventDestroy(c->ev[i]);
@@ -502,8 +539,7 @@ int kvattn_store(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t il0, int32_t n_
       StoreArgs af = a;
       af.dst_rows = c->fused_dst_rows;     // the arena copy lands during this launch
       HIP_TRY(c, launch_store_commit(af, n, c->pending, s));
-      HIP_TRY(c, hipEventRecord(c->ev[c->fused_stage], s));
-      c->ev_used[c->fused_stage] = true;
+      if (int rc2 = release_stage(c, c->fused_stage, s)) return rc2;
     } else {
       HIP_TRY(c, launch_store(a, n, s));
     }
@@ -798,8 +834,7 @@ int restore_rows(kvattn_ctx* c, int32_t seq, const void* src, const int32_t* pos
     a.blob_r = static_cast<const uint32_t*>(src);
     HIP_TRY(c, launch_state_copy(a, false, s));
   }
-  HIP_TRY(c, hipEventRecord(c->ev[st], s));
-  c->ev_used[st] = true;
+  if ((rc = release_stage(c, st, s))) return rc;
   return KVATTN_OK;
 }
 
@@ -863,8 +898,7 @@ int kvattn_seq_state_save(kvattn_ctx* c, int32_t seq_id, void* dst, size_t cap, 
     a.prefix_words = static_cast<int32_t>(sg.rec0 / 4);
     HIP_TRY(c, launch_state_copy(a, true, s));
   }
-  HIP_TRY(c, hipEventRecord(c->ev[st], s));
-  c->ev_used[st] = true;
+  if ((rc = release_stage(c, st, s))) return rc;
   if (written) *written = sg.total;
   return KVATTN_OK;
 }
