@@ -53,9 +53,13 @@ hipError_t launch_store(const StoreArgs& a, int n_il, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Mirror updates, and the per-(class, segment) counts cleared, in one launch.
+// Mirror updates (read from the pinned staging buffer), the per-(class,
+// segment) counts cleared and the plan copied from the staging buffer into
+// the device arena, in one launch; the later commit kernels and the
+// attention read the arena.
 __global__ __launch_bounds__(256) void k_apply_updates(CsrArgs a, int64_t n_counts) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < a.plan_n16) static_cast<u32x4*>(a.plan_dst)[i] = static_cast<const u32x4*>(a.plan_src)[i];
   if (i < a.n_updates) {
     const int32_t idx = a.updates[i].idx;
     a.cpos[idx] = a.updates[i].pos;
@@ -329,7 +333,7 @@ hipError_t launch_store_commit(const StoreArgs& a, int n_il, const CsrArgs& c, h
 
 hipError_t launch_commit(const CsrArgs& a, hipStream_t s) {
   const int64_t nc = static_cast<int64_t>(a.n_classes) * a.n_seg;
-  const int64_t n_apply = std::max<int64_t>(a.n_updates, nc);
+  const int64_t n_apply = std::max<int64_t>(std::max<int64_t>(a.n_updates, nc), a.plan_n16);
   if (n_apply > 0)
     hipLaunchKernelGGL(k_apply_updates, dim3(static_cast<unsigned>((n_apply + 255) / 256)), dim3(256), 0, s, a, nc);
   if (a.n_classes == 0) return hipGetLastError();
