@@ -334,16 +334,23 @@ def bench_decode(wl, dev, steps, warmup, layer_chunk):
         runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, True)
         t += 1
     runner.reserve(steps * runner.calls // max(1, warmup))
+    # a pass with events around every attend call (the attend times), then
+    # the timed steps without them (the throughput): each event in the
+    # stream holds the next kernel back a few microseconds
     torch.cuda.synchronize()
     t_first = t
-    t0 = time.perf_counter()
     for _ in range(steps):
         runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, True)
         t += 1
     torch.cuda.synchronize()
+    cells = np.mean([decode_step_cells(wl, s) for s in range(t_first, t)])
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        runner.run_batch(bt.n_tokens, bt.pos + t, sid, bt.output, K, V, Q, outs, False)
+        t += 1
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     avg_ms, n_launch = runner.attend_avg_ms()
-    cells = np.mean([decode_step_cells(wl, s) for s in range(t_first, t)])
     row = 2 * wl.n_head_kv * wl.head_dim * 2                       # K + V bytes per cell per layer
     kv_bytes = cells * row * wl.n_layer
     qo_bytes = 2 * bt.n_tokens * HD * 4 * wl.n_layer
