@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kStages = 16;                // pinned staging buffers in flight
 constexpr int kStagesPerEvent = 8;         // uses of the ring covered by one recorded event
+static_assert(kStages >= 2 * kStagesPerEvent, "a cover event outlives the stages it covers");
 constexpr int64_t kPartialRowsCap = 16384; // split-K partial rows x layers per launch
 constexpr size_t kAlign = 256;
 
@@ -157,9 +158,6 @@ int ensure_device(kvattn_ctx* c) {
   return KVATTN_OK;
 }
 
-// The next pinned staging buffer of the ring, at least `bytes` large, once
-// the GPU work that last read it has finished.  Its event must be recorded
-// after the work that reads it now.
 // Record one event after the uses not yet covered by one (on the stream
 // they ran on); it covers all of them.
 int cover_stages(kvattn_ctx* c) {
@@ -182,10 +180,16 @@ int release_stage(kvattn_ctx* c, int st, hipStream_t s) {
   return c->n_uncovered == kStagesPerEvent ? cover_stages(c) : KVATTN_OK;
 }
 
+// The next pinned staging buffer of the ring, at least `bytes` large, once
+// the GPU work that last read it has finished; release_stage must follow
+// the enqueuing of the work that reads it now.  A cover event is never
+// recorded again before the stages it covers come round (a stage comes
+// round after kStages uses, the event's own stage no sooner), so waiting on
+// it is waiting on the right point of the stream.
 int acquire_stage(kvattn_ctx* c, size_t bytes, int* out) {
   const int st = c->stage_next;
   c->stage_next = (st + 1) % kStages;
-  // (a ring of kStages >= 2 kStagesPerEvent is always covered by now)
+  // (with kStages >= 2 kStagesPerEvent the last use is always covered by now)
   for (int i = 0; i < c->n_uncovered; ++i)
     if (c->uncovered[i] == st)
       if (int rc = cover_stages(c)) return rc;
