@@ -57,7 +57,10 @@ def test_full_size_sampled_layers(name):
     layers = list(range(wl.n_layer))
     keep = KEEP[name]
     print(f"[gpu] full size {name}: {wl.note}; oracle layers {keep}", flush=True)
-    eng, ref, _, meta = oracle_run(wl, keep, measured_only=True)
+    # the rounding model costs ~3x the oracle; the mixed workload keeps the
+    # flat bound instead (its oracle alone takes ~30 s for one layer)
+    model = name != "mixed"
+    eng, ref, _, meta = oracle_run(wl, keep, measured_only=True, sigma=model)
     print(f"[gpu] full size {name}: oracle done ({len(ref)} outputs)", flush=True)
     ub_index = {b: 0 for b in range(len(wl.batches))}
     seen = {"cells": 0, "mask": 0}
@@ -79,10 +82,12 @@ def test_full_size_sampled_layers(name):
     assert set(got) == set(ref)
     worst = 0.0
     for key in sorted(ref):
-        ma, _ = assert_parity(got[key], ref[key], tag=f"{name} batch {key[0]} layer {key[1]}")
+        ma, _ = assert_parity(got[key], ref[key], tag=f"{name} batch {key[0]} layer {key[1]}", **ref.model(key))
         worst = max(worst, ma)
-    bound = VALU_BOUND if name == "cb_decode" else MFMA_BOUND
-    assert worst < bound, worst
+    if name == "cb_decode":
+        assert worst < VALU_BOUND, worst
+    elif not model:
+        assert worst < MFMA_BOUND, worst
     occ = eng.cells.pos >= 0
     for l in keep:
         assert np.array_equal(ctx.K[l].cpu().numpy().view(np.uint16)[occ], eng.K[l][occ].view(np.uint16))

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from synthetic import workloads as W
-from tests.helpers import MFMA_BOUND, assert_parity, gpu_run, oracle_run
+from tests.helpers import assert_parity, gpu_run, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -41,9 +41,8 @@ def test_random_mix_parity(seed):
     assert checked["mask"] == len(meta)
     worst = 0.0
     for key in ref:
-        ma, _ = assert_parity(got[key], ref[key], tag=f"seed {seed} batch {key[0]}")
+        ma, _ = assert_parity(got[key], ref[key], tag=f"seed {seed} batch {key[0]}", **ref.model(key))
         worst = max(worst, ma)
-    assert worst < MFMA_BOUND, worst
     gk = ctx.K[0].cpu().numpy().view(np.uint16)
     gv = ctx.V[0].cpu().numpy().view(np.uint16)
     occ = eng.cells.pos >= 0
