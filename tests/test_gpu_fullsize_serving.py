@@ -13,6 +13,8 @@ ubatch of layer 27 are compared with the fp64 oracle, row by row.  Layers
 0..26 read a seeded pool (their values do not enter layer 27).
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -22,7 +24,7 @@ from oracle.attention import masked_attention
 from oracle.scheduler import OracleScheduler
 from synthetic.serving import qwen_serving
 
-from helpers import assert_parity
+from helpers import assert_parity, mfma_query, weight_sigma
 
 pytestmark = pytest.mark.gpu
 
@@ -89,9 +91,12 @@ def test_serving_loop_full_size_sampled_layer():
                 got27 = outs[CHECK, :u.n_tokens].double().cpu().numpy()
                 pick = np.unique(np.random.default_rng(it + u.id).integers(0, u.n_tokens, 24))
                 streams = np.asarray(ru.streams)
-                want = masked_attention(q27[np.asarray(ru.src)[pick]], eng.K[CHECK], eng.V[CHECK], streams[pick],
-                                        ru.mask[pick], st.n_head, st.n_head_kv)
-                assert_parity(got27[pick], want, tag=f"iteration {it} ubatch {u.id}")
+                qp = q27[np.asarray(ru.src)[pick]]
+                args = (eng.K[CHECK], eng.V[CHECK], streams[pick], ru.mask[pick], st.n_head, st.n_head_kv)
+                want = masked_attention(qp, *args)
+                qt = mfma_query(qp, st.head_dim)
+                alt, sig = masked_attention(qt, *args, math.log(2.0)), weight_sigma(qt, *args, math.log(2.0))
+                assert_parity(got27[pick], want, tag=f"iteration {it} ubatch {u.id}", alt=alt, sigma=sig)
                 checked += len(pick)
         sch.advance()
         ref.advance()

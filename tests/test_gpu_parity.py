@@ -230,7 +230,7 @@ def test_mfma_long_context_items(swa):
 def test_class_lists_bit_exact(name):
     wl = small(name)
     print(f"[gpu] class lists {name}", flush=True)
-    eng, _, _, meta = oracle_run(wl, [0], keep_masks=False)
+    eng, _, _, meta = oracle_run(wl, [0], keep_masks=False, sigma=False)
     # replay the placement on the GPU, checking the lists after every commit
     eng2, _, _, _ = None, None, None, None
     from oracle import OracleEngine

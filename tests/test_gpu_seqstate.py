@@ -22,7 +22,7 @@ from oracle import OracleEngine
 from oracle import seqstate as S
 from synthetic import workloads as W
 
-from helpers import ATOL, RTOL, assert_parity, gpu_run, oracle_run, make_ctx
+from helpers import ATOL, RTOL, assert_parity, gpu_run, make_ctx, model_for, oracle_run
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +35,7 @@ def saved_pair(wl, seqs):
     layers = list(range(wl.n_layer))
     print(f"seqstate: {wl.name} {wl.note}", flush=True)
     ctx, _ = gpu_run(wl, layers)
-    eng, _, _, _ = oracle_run(wl, layers, measured_only=False)
+    eng, _, _, _ = oracle_run(wl, layers, measured_only=False, sigma=False)
     out = {}
     for q in seqs:
         g = blob_bytes(ctx.state_save(q))
@@ -95,7 +95,9 @@ def test_restore_then_attend_matches_oracle():
     eng.commit(ru, build_mask=True)
     for l in range(2):
         eng.store(ru, l, kv[l][0][ru.src], kv[l][1][ru.src])
-        assert_parity(outs[l].double().cpu().numpy(), eng.attend(ru, l, q[l][ru.src]), tag=f"layer {l}")
+        alt, sig = model_for(eng, ru, l, q[l][ru.src])
+        assert_parity(outs[l].double().cpu().numpy(), eng.attend(ru, l, q[l][ru.src]), tag=f"layer {l}",
+                      alt=alt, sigma=sig)
 
 
 def test_restore_refusals_change_nothing():

@@ -21,7 +21,7 @@ from oracle.scheduler import OracleScheduler
 from synthetic.serving import request_stream, QWEN3_06B
 from synthetic.workloads import KIND_K, KIND_V, KIND_Q
 
-from helpers import assert_parity
+from helpers import assert_parity, model_for
 
 pytestmark = pytest.mark.gpu
 
@@ -83,9 +83,11 @@ def serve_parity(stream, max_iters=400):
                 eng.commit(ru, build_mask=True)
                 for i, l in enumerate(layers):
                     eng.store(ru, l, rows[(l, KIND_K)][ru.src], rows[(l, KIND_V)][ru.src])
-                    want = eng.attend(ru, l, rows[(l, KIND_Q)][ru.src])
+                    qr = rows[(l, KIND_Q)][ru.src]
+                    want = eng.attend(ru, l, qr)
+                    alt, sig = model_for(eng, ru, l, qr)
                     have = outs[i].double().cpu().numpy()
-                    e, _ = assert_parity(have, want, tag=f"it {it} ubatch {u.id} layer {l}")
+                    e, _ = assert_parity(have, want, tag=f"it {it} ubatch {u.id} layer {l}", alt=alt, sigma=sig)
                     stats["max_abs"] = max(stats["max_abs"], e)
                 stats["rows"] += u.n_tokens
         sch.advance()
