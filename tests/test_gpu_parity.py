@@ -345,7 +345,9 @@ def test_repeat_store_attend_is_idempotent():
 @pytest.mark.parametrize("name", ["prefix", "cb_decode"])
 def test_kernel_timing_events_change_nothing(name):
     """Arming kernel timing (hipExtLaunchKernel start/stop events) leaves the
-    results bit-identical; a timed kernel's elapsed time is positive and
+    results bit-identical (for the shared-prefix plan, timing the matrix-core
+    or the vector-ALU kernel turns the combined launch into two); a timed
+    kernel's elapsed time is positive and
     within the events around the whole call; a kind the call does not launch
     gets both events back to back (about zero)."""
     wl = small(name)
@@ -397,6 +399,53 @@ def test_kernel_timing_events_change_nothing(name):
         torch.cuda.synchronize()
         assert all(torch.equal(a, c) for a, c in zip(ref, out))
     assert checked == 3
+    ctx.close()
+
+
+@pytest.mark.parametrize("hk,g,d", [(8, 2, 128), (4, 2, 128), (8, 1, 128), (8, 4, 64), (16, 2, 64), (16, 2, 128)])
+def test_combined_launch_matches_separate_launches(hk, g, d):
+    """A plan with matrix-core and vector-ALU items (a shared prefix beside
+    each sequence's own cells) runs both in one launch where the shape allows
+    (one launch of both bodies, the vector-ALU merge in rounds through one
+    LDS slot per row slice); timing one kind of kernel runs them as two
+    launches.  Both give bit-identical outputs -- the rounds repeat the
+    one-round merge's arithmetic in its order -- over rows of 512, 1024 and
+    2048 numbers, one to four query heads per KV head, head sizes 64 and
+    128 (2048-number rows of 128-number heads take the two launches
+    either way)."""
+    wl = W.prefix_decode(n_seq=8, prefix=300, private=50, n_layer=2, kv_size=1024)
+    wl.n_head_kv, wl.n_head, wl.head_dim = hk, hk * g, d
+    print(f"[gpu] combined launch: {hk} KV heads x {d}, group {g}", flush=True)
+    ctx = make_ctx(wl)
+    dev = torch.device("cuda:0")
+    from tests.helpers import batch_tensors
+    layers = list(range(wl.n_layer))
+    compared = 0
+    for b, bt in enumerate(wl.batches):
+        t = batch_tensors(wl, b, layers, bt.measured)
+        st, ubs, _ = ctx.split(bt.n_tokens, bt.pos, bt.seq_ids, bt.output)
+        assert st == 0 and len(ubs) == 1
+        ub = ubs[0]
+        ctx.store(ub, 0, [torch.from_numpy(t[(l, W.KIND_K)]).to(dev) for l in layers],
+                  [torch.from_numpy(t[(l, W.KIND_V)]).to(dev) for l in layers])
+        if not bt.measured:
+            continue
+        stats = ctx.plan_stats()
+        assert stats["n_items_mfma"] > 0 and stats["n_items_valu"] > 0, stats
+        Q = [torch.from_numpy(t[(l, W.KIND_Q)]).to(dev) for l in layers]
+        combined = [torch.full_like(q, float("nan")) for q in Q]
+        ctx.attend(ub, 0, Q, combined)
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record()
+        k1.record()
+        K.kvattn_time_next_attend(ctx.ctx, K.KVATTN_KERNEL_VALU, k0.cuda_event, k1.cuda_event)
+        separate = [torch.full_like(q, float("nan")) for q in Q]
+        ctx.attend(ub, 0, Q, separate)
+        torch.cuda.synchronize()
+        for a, c in zip(combined, separate):
+            assert torch.isfinite(a).all() and torch.equal(a, c)
+        compared += 1
+    assert compared == 1
     ctx.close()
 
 

@@ -23,7 +23,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvattn.so")
 SOURCES = ["host_core.cpp", "api.cpp", "sched.cpp", "kernels_commit.hip", "kernels_state.hip", "attn_valu.hip", "attn_mfma.hip",
-           "attend_static.hip", "probes.hip"]
+           "attn_both.hip", "attend_static.hip", "probes.hip"]
 ARCH = os.environ.get("KVATTN_OFFLOAD_ARCH", "gfx950")
 
 

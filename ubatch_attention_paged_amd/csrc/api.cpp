@@ -631,6 +631,11 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
   const int32_t n_red = static_cast<int32_t>(P.red_slot.size());
   const int32_t kind_items[3] = {static_cast<int32_t>(P.items_mfma.size()), static_cast<int32_t>(P.items_valu.size()),
                                  n_red};
+  // A plan with both matrix-core and vector-ALU items (a shared prefix beside
+  // each sequence's own cells, or prompt chunks beside decode tokens) runs
+  // them in one launch, where the shape allows it
+  const bool both = kind_items[0] > 0 && kind_items[1] > 0 && g.swa == 0 && tkind != KVATTN_KERNEL_MFMA &&
+                    tkind != KVATTN_KERNEL_VALU && attn_both_supported(g.head_dim, g.G(), g.E());
   for (int32_t l0 = 0; l0 < n_il; l0 += chunk) {
     const int n = std::min<int32_t>(chunk, n_il - l0);
     // The timed kernel's first launch starts the events and its last one
@@ -663,12 +668,19 @@ int kvattn::attend_with_partials(kvattn_ctx* c, const kvattn_ubatch* ub, int32_t
     // would otherwise wait for vector-ALU workgroups to drain
     a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_mfma);
     a.n_items = static_cast<int32_t>(P.items_mfma.size());
-    HIP_TRY(c, launch_attn_mfma(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_MFMA]));
-    if (stop_after && tkind == KVATTN_KERNEL_MFMA) HIP_TRY(c, hipEventRecord(tev1, s));
-    a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
-    a.n_items = static_cast<int32_t>(P.items_valu.size());
-    HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_VALU]));
-    if (stop_after && tkind == KVATTN_KERNEL_VALU) HIP_TRY(c, hipEventRecord(tev1, s));
+    if (both) {
+      // both kinds in one launch (unless one kind's kernel is being timed)
+      a.items2 = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
+      a.n_items2 = static_cast<int32_t>(P.items_valu.size());
+      HIP_TRY(c, launch_attn_both(a, n, g.head_dim, g.G(), s));
+    } else {
+      HIP_TRY(c, launch_attn_mfma(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_MFMA]));
+      if (stop_after && tkind == KVATTN_KERNEL_MFMA) HIP_TRY(c, hipEventRecord(tev1, s));
+      a.items = reinterpret_cast<const WorkItem*>(arena + VL.items_valu);
+      a.n_items = static_cast<int32_t>(P.items_valu.size());
+      HIP_TRY(c, launch_attn_valu(a, n, g.head_dim, g.G(), s, ev[KVATTN_KERNEL_VALU]));
+      if (stop_after && tkind == KVATTN_KERNEL_VALU) HIP_TRY(c, hipEventRecord(tev1, s));
+    }
     HIP_TRY(c, launch_reduce(a, n_red, n, g.head_dim, s, ev[KVATTN_KERNEL_MERGE]));
     if (stop_after && tkind == KVATTN_KERNEL_MERGE) HIP_TRY(c, hipEventRecord(tev1, s));
   }

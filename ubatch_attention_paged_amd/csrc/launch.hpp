@@ -76,6 +76,11 @@ struct AttnArgs {
   int32_t swa;                // sliding window in positions, 0 = none
   float scale_log2e;          // kq_scale * log2(e)
   uint32_t layer_bytes;       // bytes of one layer's K (= V) tensor, < 2 GiB
+  // combined launch (attn_both.hip): the vector-ALU items beside the
+  // matrix-core ones in `items`, and the layers of the launch
+  const WorkItem* items2;
+  int32_t n_items2;
+  int32_t n_il;
 };
 
 struct MaskArgs {
@@ -128,6 +133,12 @@ struct KernelEvents {
 hipError_t launch_attn_valu(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s,
                             const KernelEvents& ev = {});
 hipError_t launch_attn_mfma(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s,
+                            const KernelEvents& ev = {});
+// matrix-core items (items, n_items) and vector-ALU items (items2,
+// n_items2) in one launch, for the shapes attn_both_supported accepts (no
+// sliding window)
+bool attn_both_supported(int head_dim, int group, int row);
+hipError_t launch_attn_both(const AttnArgs& a, int n_il, int head_dim, int group, hipStream_t s,
                             const KernelEvents& ev = {});
 hipError_t launch_reduce(const AttnArgs& a, int n_reduced, int n_il, int head_dim, hipStream_t s,
                          const KernelEvents& ev = {});
