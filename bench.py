@@ -887,6 +887,7 @@ PROFILE_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --
                    "-o run -- python -u <repo>/bench.py --gpus 1 --steps 20 --warmup 5 --no-cpu-baseline")
 
 KERNEL_SOURCES = {"k_attn_mfma": "attn_mfma.hip", "k_attn_valu": "attn_valu.hip", "k_attn_reduce": "attn_valu.hip",
+                  "k_attn_both": "attn_both.hip",
                   "k_store_commit": "kernels_commit.hip", "k_store": "kernels_commit.hip"}
 
 
